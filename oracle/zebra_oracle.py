@@ -1,0 +1,289 @@
+"""CPU oracle for Zebra3D's layerwise hybrid global attention.
+
+TEST INFRASTRUCTURE ONLY. This module is the plain, slow, obviously correct
+reference that the HIP path is checked against. Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import it; the library and its Python binding never do, and they share no
+code with it (the seeded input generators are the only common module).
+
+Everything is NumPy float64, one step per definition, in the order the pages
+state it, with no blocking, fusion or reordering of any sum. Query rows are
+independent, so functions that loop over rows or tiles do so only to keep
+memory bounded; that changes no arithmetic.
+
+Sources. Citations name the page by its title and host, then the part of it:
+  [paper page] "Zebra3D: Efficient Hybrid Foundation Models For Scalable 3D
+               Reconstruction", thelatestinai.com paper page
+  [news page]  "Zebra3D speeds up 3D reconstruction by up to 7.1x on 1024
+               frames without training from scratch", news.hamidun.com
+  [synopsis]   "3D reconstruction drops dense attention layer by layer: up to
+               5.6x end-to-end speedup at 1,024 views", ai4snews.wisdomeyes.cn
+
+Readings taken where the pages are silent (each is listed again where used):
+  R1 tiles are contiguous runs of the token order; the last tile may be short
+     and its mean is over its valid tokens only.
+  R2 tile selection: score s_ij = mean(Q_tile_i) . mean(K_tile_j) (unscaled),
+     keep the top_k key tiles per query tile under the order (score
+     descending, tile index ascending); the kept list is returned ascending.
+  R3 a landmark is one ordinary softmax column with key mean(K_tile_j) and
+     value mean(V_tile_j), logit scale * q . kbar_j, with no multiplicity term;
+     only omitted tiles (j not kept) contribute a landmark.
+  R4 the linear feature map is phi(x) = elu(x) + 1, with no scale and no
+     epsilon in the normaliser; "linear-centered" is read as the centred least
+     squares fit (with intercept) of a per-head, per-channel affine map.
+  R5 the fit target is dense softmax attention of the same stage at sampled
+     queries; a channel whose inputs do not vary gets scale 0 and bias mean(y).
+
+Parity status: every function on the attention path is pinned by
+``tests/oracle_pins.py`` against closed forms, library routines or brute
+force. ``mean_attention_sparsity`` is bookkeeping, not part of the path; the
+pages' "about 79%" and "about 94%" figures pin it only weakly (leaving out
+the landmark columns also lands within one point of both).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "tile_bounds", "pool_tiles", "block_scores", "select_top_tiles",
+    "select_tiles", "attention_columns", "tile_sparse_attention_tile",
+    "tile_sparse_attention", "dense_attention", "elu_plus_one",
+    "linear_attention", "fit_affine", "affine_apply", "mean_attention_sparsity",
+]
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------
+# tiles and landmarks
+# ----------------------------------------------------------------------------
+
+def tile_bounds(n_tokens: int, tile: int):
+    """Token ranges [start, end) of the contiguous tiles of a sequence (reading R1).
+
+    The paper page (Figure 8 caption) measures attention on 64x64 token
+    blocks; tiles here are runs of ``tile`` consecutive tokens, the last one
+    possibly short.
+    """
+    if tile <= 0:
+        raise ValueError("tile must be positive")
+    return [(s, min(s + tile, n_tokens)) for s in range(0, n_tokens, tile)]
+
+
+def pool_tiles(x, tile: int) -> np.ndarray:
+    """Mean over the valid tokens of every tile: [N][d] -> [T][d].
+
+    Omitted tiles are summarised by the mean key and mean value of their
+    tokens ([paper page] Figure 1 caption; [news page] "How Zebra3D works",
+    landmark summaries of unselected regions). The same means of the query
+    tiles feed the tile scores (reading R2).
+    """
+    x = _f64(x)
+    bounds = tile_bounds(x.shape[0], tile)
+    out = np.zeros((len(bounds), x.shape[1]), dtype=np.float64)
+    for t, (s, e) in enumerate(bounds):
+        out[t] = x[s:e].sum(axis=0) / (e - s)
+    return out
+
+
+def block_scores(qbar, kbar) -> np.ndarray:
+    """s_ij = qbar_i . kbar_j, unscaled (reading R2): [Tq][d] x [Tk][d] -> [Tq][Tk]."""
+    return _f64(qbar) @ _f64(kbar).T
+
+
+def select_top_tiles(scores_row, top_k: int) -> np.ndarray:
+    """Kept key tiles of one query tile, ascending (reading R2).
+
+    The tile-sparse stage computes only selected blocks ([news page] "How
+    Zebra3D works"). Ranking is by score, highest first; equal scores go to
+    the lower tile index. The kept set is returned in ascending index order.
+    """
+    s = _f64(scores_row)
+    if not 0 <= top_k <= s.shape[0]:
+        raise ValueError("top_k out of range")
+    idx = np.arange(s.shape[0])
+    order = np.lexsort((idx, -s))  # primary: -score ascending; secondary: index
+    return np.sort(order[:top_k]).astype(np.int64)
+
+
+def select_tiles(qbar, kbar, top_k: int) -> np.ndarray:
+    """Kept tiles of every query tile: [Tq][top_k] int64, each row ascending."""
+    s = block_scores(qbar, kbar)
+    if s.shape[0] == 0:
+        return np.zeros((0, top_k), dtype=np.int64)
+    return np.stack([select_top_tiles(s[i], top_k) for i in range(s.shape[0])])
+
+
+# ----------------------------------------------------------------------------
+# tile-sparse softmax attention with mean-key/value landmarks
+# ----------------------------------------------------------------------------
+
+def attention_columns(k, v, k_tile: int, kept):
+    """Keys and values one query tile attends to (readings R1, R3).
+
+    Every token of every kept tile, then one landmark (kbar_j, vbar_j) for
+    every omitted tile j. Kept tiles keep full softmax interactions and
+    omitted tiles become mean-key/value landmarks ([paper page] Figure 1
+    caption); the [synopsis] ("Interpretation") calls the kept part exact
+    softmax over selected tiles.
+    """
+    k = _f64(k)
+    v = _f64(v)
+    bounds = tile_bounds(k.shape[0], k_tile)
+    kept = [int(j) for j in kept]
+    kept_set = set(kept)
+    if len(kept_set) != len(kept):
+        raise ValueError("kept tiles must be distinct")
+    kbar = pool_tiles(k, k_tile)
+    vbar = pool_tiles(v, k_tile)
+    keys, vals = [], []
+    for j in sorted(kept):
+        s, e = bounds[j]
+        keys.append(k[s:e])
+        vals.append(v[s:e])
+    for j in range(len(bounds)):
+        if j not in kept_set:
+            keys.append(kbar[j:j + 1])
+            vals.append(vbar[j:j + 1])
+    if not keys:
+        return np.zeros((0, k.shape[1])), np.zeros((0, v.shape[1]))
+    return np.concatenate(keys, axis=0), np.concatenate(vals, axis=0)
+
+
+def _softmax_rows(logits: np.ndarray) -> np.ndarray:
+    m = logits.max(axis=1, keepdims=True)
+    w = np.exp(logits - m)
+    return w / w.sum(axis=1, keepdims=True)
+
+
+def tile_sparse_attention_tile(q_rows, k, v, k_tile: int, kept, scale: float) -> np.ndarray:
+    """Output of the queries of one query tile: softmax(scale q C_k^T) C_v."""
+    q_rows = _f64(q_rows)
+    ck, cv = attention_columns(k, v, k_tile, kept)
+    return _softmax_rows(scale * (q_rows @ ck.T)) @ cv
+
+
+def tile_sparse_attention(q, k, v, q_tile: int, k_tile: int, top_k: int, scale: float,
+                          sel=None):
+    """Tile-sparse stage over all heads: [H][Nq][d], [H][Nk][d] x2 -> ([H][Nq][d], sel).
+
+    ``sel`` ([H][Tq][top_k]) replaces the oracle's own selection when given,
+    which lets the attention step be checked on another implementation's
+    choice of tiles.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    heads, n_q, _ = q.shape
+    out = np.zeros((heads, n_q, v.shape[2]), dtype=np.float64)
+    sels = []
+    for h in range(heads):
+        if sel is None:
+            sel_h = select_tiles(pool_tiles(q[h], q_tile), pool_tiles(k[h], k_tile), top_k)
+        else:
+            sel_h = np.asarray(sel[h])
+        sels.append(sel_h)
+        for i, (s, e) in enumerate(tile_bounds(n_q, q_tile)):
+            out[h, s:e] = tile_sparse_attention_tile(q[h, s:e], k[h], v[h], k_tile,
+                                                     sel_h[i], scale)
+    return out, np.stack(sels) if sels else np.zeros((0, 0, top_k), dtype=np.int64)
+
+
+def dense_attention(q, k, v, scale: float, row_block: int = 1024) -> np.ndarray:
+    """Exact softmax attention of every query over every key, one head: [Nq][d] -> [Nq][d].
+
+    This is the dense global attention that the hybrid replaces ([news page]
+    "Where scaling breaks down": the tokens of all frames attend to each other)
+    and the target of the affine fit (reading R5). Rows are independent; they
+    are taken ``row_block`` at a time to bound memory.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    out = np.zeros((q.shape[0], v.shape[1]), dtype=np.float64)
+    for s in range(0, q.shape[0], row_block):
+        e = min(q.shape[0], s + row_block)
+        out[s:e] = _softmax_rows(scale * (q[s:e] @ k.T)) @ v
+    return out
+
+
+# ----------------------------------------------------------------------------
+# linear attention and the closed-form affine fit
+# ----------------------------------------------------------------------------
+
+def elu_plus_one(x) -> np.ndarray:
+    """phi(x) = x + 1 for x > 0, exp(x) otherwise (reading R4)."""
+    x = _f64(x)
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def linear_attention(q, k, v, aff_scale=None, aff_bias=None):
+    """Linear attention of one head, then the per-channel affine map (reading R4).
+
+    Tolerant stages run linear(-centered) attention ([paper page] Abstract;
+    [news page] "How Zebra3D works"). With phi = elu + 1:
+        S = sum_n phi(k_n) v_n^T,  z = sum_n phi(k_n),
+        o_n = (phi(q_n)^T S) / (phi(q_n)^T z),
+    then out = a * o + b per channel ([paper page] Table 3(a), "Linear-centered
+    + fit"). Returns (out, S, z).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    fq = elu_plus_one(q)
+    fk = elu_plus_one(k)
+    state = fk.T @ v
+    z = fk.sum(axis=0)
+    o = (fq @ state) / (fq @ z)[:, None]
+    if aff_scale is not None or aff_bias is not None:
+        o = affine_apply(o, aff_scale, aff_bias)
+    return o, state, z
+
+
+def affine_apply(o, aff_scale=None, aff_bias=None) -> np.ndarray:
+    """out = a * o + b, per channel; a defaults to 1 and b to 0."""
+    o = _f64(o)
+    a = np.ones(o.shape[-1]) if aff_scale is None else _f64(aff_scale)
+    b = np.zeros(o.shape[-1]) if aff_bias is None else _f64(aff_bias)
+    return o * a + b
+
+
+def fit_affine(x, y, degenerate_rel: float = 1e-30):
+    """Closed-form least squares a, b per channel: min sum_i (a x_ic + b - y_ic)^2.
+
+    The linear components are fitted by a closed-form affine map with no
+    gradient descent ([news page] "How Zebra3D works"; [paper page] Table 3(a)
+    contrasts an uncentered fit with the centred fit used here, reading R4).
+    x is the linear output before the map and y the dense output at the same
+    M queries, both [M][d]. Centred form of the 2x2 normal equations:
+        a = sum (x - xbar)(y - ybar) / sum (x - xbar)^2,  b = ybar - a xbar.
+    A channel with sum (x - xbar)^2 <= degenerate_rel * M gets a = 0, b = ybar
+    (reading R5). Returns (a, b, n_degenerate).
+    """
+    x, y = _f64(x), _f64(y)
+    m = x.shape[0]
+    if m == 0:
+        raise ValueError("fit needs at least one sample")
+    xbar = x.sum(axis=0) / m
+    ybar = y.sum(axis=0) / m
+    dx = x - xbar
+    sxx = (dx * dx).sum(axis=0)
+    sxy = (dx * (y - ybar)).sum(axis=0)
+    ok = sxx > degenerate_rel * m
+    a = np.where(ok, sxy / np.where(ok, sxx, 1.0), 0.0)
+    b = ybar - a * xbar
+    return a, b, int((~ok).sum())
+
+
+# ----------------------------------------------------------------------------
+# bookkeeping of the xL/yS budget
+# ----------------------------------------------------------------------------
+
+def mean_attention_sparsity(linear_frac: float, keep_frac: float, k_tile: int) -> float:
+    """Fraction of attention entries not computed exactly, averaged over stages.
+
+    In the xL/yS shorthand x is the fraction of layers that use linear
+    attention and y the sparsity of attention rows in the other layers
+    ([paper page] Table 20 and Table 21 captions). A linear stage computes no
+    softmax entries; a tile-sparse stage computes the kept fraction of keys
+    plus one landmark column per omitted tile of ``k_tile`` keys.
+    """
+    dense_frac = keep_frac + (1.0 - keep_frac) / k_tile
+    return linear_frac + (1.0 - linear_frac) * (1.0 - dense_frac)

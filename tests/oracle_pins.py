@@ -1,0 +1,341 @@
+"""Pins of the CPU oracle to facts outside itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+something the pages or the mathematics fix: exact rational means, brute-force
+top-k over all subsets, torch's scaled-dot-product attention and ELU (library
+routines), numpy's least squares, closed forms of special cases, and the
+figures the pages print. ``test_oracle_pins.py`` runs them; the mutation test
+plants mistakes in the oracle and checks that some pin fails for each.
+
+All calls go through the module object ``zo`` so a planted mistake in one
+oracle function is seen by every function that uses it.
+"""
+
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import oracle.zebra_oracle as zo
+from linear_hybrid_attention_zebra_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} != {b.shape}"
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
+
+
+def _qkv(seed, heads, nq, nk, d, scale_q=1.0):
+    rng = np.random.default_rng(seed)
+    q = scale_q * rng.standard_normal((heads, nq, d))
+    k = rng.standard_normal((heads, nk, d))
+    v = rng.standard_normal((heads, nk, d))
+    return q, k, v
+
+
+def _sdpa(q, k, v, scale):
+    """torch's scaled_dot_product_attention in float64 on the CPU (one head)."""
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(
+        t(q), t(k), t(v), scale=scale)[0, 0].numpy()
+
+
+# ----------------------------------------------------------------------------
+# tiles and landmarks
+# ----------------------------------------------------------------------------
+
+def pin_pool_exact_rational():
+    """Tile means equal exact rational means, including short last tiles."""
+    rng = np.random.default_rng(11)
+    for n, tile in [(70, 32), (65, 32), (5, 8), (64, 64), (3, 1)]:
+        x = synth.bf16_round(rng.standard_normal((n, 3)).astype(np.float32))
+        got = zo.pool_tiles(x, tile)
+        starts = list(range(0, n, tile))
+        assert got.shape == (len(starts), 3), f"pool shape {got.shape}"
+        for t, s in enumerate(starts):
+            e = min(n, s + tile)
+            for c in range(3):
+                exact = sum(Fraction(float(x[i, c])) for i in range(s, e)) / (e - s)
+                assert abs(got[t, c] - float(exact)) <= 1e-15 * max(1.0, abs(float(exact))), \
+                    f"pool n={n} tile={tile} t={t} c={c}"
+
+
+def _brute_topk(scores, k):
+    """The unique k-subset whose members all beat every non-member under
+    (score descending, index ascending), found by trying every subset."""
+    n = len(scores)
+
+    def beats(a, b):
+        return scores[a] > scores[b] or (scores[a] == scores[b] and a < b)
+
+    found = [sub for sub in itertools.combinations(range(n), k)
+             if all(beats(a, b) for a in sub for b in range(n) if b not in sub)]
+    assert len(found) == 1
+    return list(found[0])
+
+
+def pin_select_brute_force():
+    """Top-k with lowest-index tie breaks equals brute force over all subsets."""
+    rng = np.random.default_rng(12)
+    for trial in range(80):
+        n = int(rng.integers(1, 8))
+        k = int(rng.integers(0, n + 1))
+        if trial % 2:
+            s = rng.integers(-2, 3, size=n).astype(np.float64)  # many ties
+        else:
+            s = rng.standard_normal(n)
+        got = [int(j) for j in zo.select_top_tiles(s, k)]
+        assert got == _brute_topk(s, k), f"select trial {trial}: {s} k={k} -> {got}"
+
+
+def pin_select_tiles_orientation():
+    """Row i of the selection ranks kbar_j by qbar_i . kbar_j (exact dot via fsum)."""
+    rng = np.random.default_rng(13)
+    qbar = rng.standard_normal((3, 5))
+    kbar = rng.standard_normal((6, 5))
+    sel = zo.select_tiles(qbar, kbar, 2)
+    assert sel.shape == (3, 2), f"selection shape {sel.shape}"
+    for i in range(3):
+        s = [math.fsum(float(qbar[i, c]) * float(kbar[j, c]) for c in range(5)) for j in range(6)]
+        assert [int(j) for j in sel[i]] == _brute_topk(s, 2), f"row {i}"
+
+
+# ----------------------------------------------------------------------------
+# dense and tile-sparse attention
+# ----------------------------------------------------------------------------
+
+def pin_dense_vs_sdpa():
+    """Dense attention equals torch's scaled_dot_product_attention (float64)."""
+    q, k, v = _qkv(21, 1, 7, 33, 16)
+    for scale in (0.125, 0.7):
+        _close(zo.dense_attention(q[0], k[0], v[0], scale), _sdpa(q[0], k[0], v[0], scale),
+               1e-12, f"dense vs sdpa scale={scale}")
+
+
+def pin_dense_closed_forms():
+    """Identical keys give the mean value; two keys give sigmoid weights."""
+    rng = np.random.default_rng(22)
+    q = rng.standard_normal((4, 8))
+    k = np.tile(rng.standard_normal((1, 8)), (5, 1))
+    v = rng.standard_normal((5, 3))
+    _close(zo.dense_attention(q, k, v, 0.5), np.tile(v.mean(axis=0), (4, 1)), 1e-13,
+           "identical keys")
+    k2 = rng.standard_normal((2, 8))
+    v2 = rng.standard_normal((2, 3))
+    w0 = 1.0 / (1.0 + np.exp(-0.5 * (q @ k2[0] - q @ k2[1])))
+    _close(zo.dense_attention(q, k2, v2, 0.5), w0[:, None] * v2[0] + (1 - w0)[:, None] * v2[1],
+           1e-13, "two keys")
+
+
+def pin_keep_all_equals_dense():
+    """Keeping every key tile leaves no landmark: the stage is dense attention."""
+    for (nq, nk, bq, bk) in [(70, 70, 16, 32), (40, 97, 32, 16), (64, 64, 64, 64)]:
+        q, k, v = _qkv(23, 2, nq, nk, 8)
+        t_k = -(-nk // bk)
+        out, sel = zo.tile_sparse_attention(q, k, v, bq, bk, t_k, 0.35)
+        assert sel.shape == (2, -(-nq // bq), t_k)
+        for h in range(2):
+            _close(out[h], _sdpa(q[h], k[h], v[h], 0.35), 1e-12, f"keep-all nq={nq} nk={nk}")
+
+
+def pin_tile_one_is_exact():
+    """With one-token key tiles every landmark is its own key: exact for any top_k."""
+    q, k, v = _qkv(24, 1, 12, 9, 8)
+    for top_k in (1, 4, 9):
+        out, _ = zo.tile_sparse_attention(q, k, v, 4, 1, top_k, 0.4)
+        _close(out[0], _sdpa(q[0], k[0], v[0], 0.4), 1e-12, f"tile 1 top_k={top_k}")
+
+
+def pin_landmark_by_hand():
+    """One query, tile {k0,k1} kept and tile {k2,k3} omitted: three softmax columns."""
+    rng = np.random.default_rng(25)
+    q = rng.standard_normal((1, 4))
+    k = rng.standard_normal((4, 4))
+    v = rng.standard_normal((4, 2))
+    sc = 0.8
+    cols_k = [k[0], k[1], 0.5 * (k[2] + k[3])]
+    cols_v = [v[0], v[1], 0.5 * (v[2] + v[3])]
+    logits = [sc * math.fsum(float(a) * float(b) for a, b in zip(q[0], ck)) for ck in cols_k]
+    w = [math.exp(x) for x in logits]
+    expect = sum(wi * cv for wi, cv in zip(w, cols_v)) / sum(w)
+    got = zo.tile_sparse_attention_tile(q, k, v, 2, [0], sc)
+    _close(got[0], expect, 1e-13, "landmark by hand")
+    out, sel = zo.tile_sparse_attention(q[None], k[None], v[None], 1, 2, 1, sc,
+                                        sel=np.array([[[0]]]))
+    _close(out[0, 0], expect, 1e-13, "landmark by hand, full call")
+
+
+def pin_constant_tiles_closed_form():
+    """Key tiles filled with one repeated key/value (ragged last tile).
+
+    A kept tile j contributes its n_j identical columns, weight n_j e^l_j; an
+    omitted one contributes one landmark equal to that key, weight e^l_j.
+    """
+    rng = np.random.default_rng(26)
+    bk, nk, d, sc = 4, 14, 6, 0.6  # tiles of 4, 4, 4, 2 tokens
+    t_k = -(-nk // bk)
+    kap = rng.standard_normal((t_k, d))
+    nu = rng.standard_normal((t_k, 3))
+    k = np.repeat(kap, bk, axis=0)[:nk]
+    v = np.repeat(nu, bk, axis=0)[:nk]
+    n_j = np.array([min(bk, nk - j * bk) for j in range(t_k)], dtype=np.float64)
+    q = rng.standard_normal((5, d))
+    for kept in ([0, 2], [3], [1, 3], [0, 1, 2, 3]):
+        mult = np.where(np.isin(np.arange(t_k), kept), n_j, 1.0)
+        ell = sc * (q @ kap.T)
+        w = mult * np.exp(ell - ell.max(axis=1, keepdims=True))
+        expect = (w @ nu) / w.sum(axis=1, keepdims=True)
+        _close(zo.tile_sparse_attention_tile(q, k, v, bk, kept, sc), expect, 1e-12,
+               f"constant tiles kept={kept}")
+    # the oracle's own selection ranks the tiles by qbar . kappa_j
+    out, sel = zo.tile_sparse_attention(q[None], k[None], v[None], 5, bk, 2, sc)
+    s = q.mean(axis=0) @ kap.T
+    assert [int(j) for j in sel[0, 0]] == _brute_topk(list(s), 2), "constant tiles selection"
+
+
+def pin_convexity_and_constant_values():
+    """Outputs are convex combinations of the columns' values; constant V gives that constant."""
+    q, k, v = _qkv(27, 1, 40, 50, 8)
+    out, _ = zo.tile_sparse_attention(q, k, v, 8, 8, 2, 0.3)
+    vmin, vmax = v[0].min(axis=0), v[0].max(axis=0)
+    assert np.all(out[0] >= vmin - 1e-12) and np.all(out[0] <= vmax + 1e-12), "convexity"
+    c = np.full_like(v, 0.0) + np.arange(8)[None, None, :] * 0.25 - 0.6
+    out_c, _ = zo.tile_sparse_attention(q, k, c, 8, 8, 2, 0.3)
+    _close(out_c[0], c[0, :40], 1e-13, "constant V, sparse")
+
+
+def pin_permutation_within_tile():
+    """Reordering keys (with their values) inside a tile changes nothing."""
+    q, k, v = _qkv(28, 1, 24, 30, 8)
+    rng = np.random.default_rng(29)
+    perm = np.arange(30)
+    for s in range(0, 30, 8):
+        e = min(30, s + 8)
+        perm[s:e] = s + rng.permutation(e - s)
+    a, sa = zo.tile_sparse_attention(q, k, v, 8, 8, 2, 0.3)
+    b, sb = zo.tile_sparse_attention(q, k[:, perm], v[:, perm], 8, 8, 2, 0.3)
+    assert np.array_equal(sa, sb), "selection changed under an in-tile permutation"
+    _close(a, b, 1e-12, "in-tile permutation")
+
+
+def pin_tiny_workload_hot_tile():
+    """Tiny workload (2 views x 64 tokens, tile 32, seed 0): the one kept tile is the hot tile.
+
+    Each query is 2 * (a key of its hot tile) + 0.5 * noise, so the pooled
+    score of the hot tile stands far above the others.
+    """
+    w = synth.TINY
+    q, k, v, hot = synth.clustered_qkv_np(w.seed, w.heads, w.n_tokens, w.head_dim,
+                                          w.q_tile, w.k_tile, w.n_hot)
+    for arrs in ((q, k), (synth.bf16_round(q), synth.bf16_round(k))):
+        for h in range(w.heads):
+            sel = zo.select_tiles(zo.pool_tiles(arrs[0][h], w.q_tile),
+                                  zo.pool_tiles(arrs[1][h], w.k_tile), 1)
+            assert np.array_equal(sel[:, 0], hot[h, :, 0]), f"head {h}: {sel[:, 0]} vs {hot[h, :, 0]}"
+
+
+# ----------------------------------------------------------------------------
+# linear attention and the affine fit
+# ----------------------------------------------------------------------------
+
+def pin_elu_plus_one_vs_torch():
+    """phi equals torch's ELU plus one, on both sides of zero."""
+    x = np.concatenate([np.linspace(-30, 30, 601), np.random.default_rng(31).standard_normal(200)])
+    ref = (torch.nn.functional.elu(torch.from_numpy(x)) + 1.0).numpy()
+    _close(zo.elu_plus_one(x), ref, 1e-15, "elu+1")
+
+
+def pin_linear_brute_force():
+    """Linear attention equals its O(N^2) kernel sum with k(q, k) = phi(q) . phi(k)."""
+    q, k, v = _qkv(32, 1, 9, 23, 5)
+    q, k, v = q[0], k[0], v[0]
+    phi = lambda x: np.array([(t + 1.0) if t > 0 else math.exp(t) for t in x])
+    expect = np.zeros((9, 5))
+    for n in range(9):
+        wts = [math.fsum(phi(q[n]) * phi(k[m])) for m in range(23)]
+        expect[n] = sum(wt * v[m] for m, wt in enumerate(wts)) / math.fsum(wts)
+    got, state, z = zo.linear_attention(q, k, v)
+    _close(got, expect, 1e-12, "linear vs brute force")
+    assert np.all(z > 0), "normaliser must be positive"
+
+
+def pin_linear_closed_forms():
+    """Constant values pass through; one key gives its value; the affine map applies per channel."""
+    rng = np.random.default_rng(33)
+    q = rng.standard_normal((6, 4))
+    k = rng.standard_normal((10, 4))
+    c = np.tile(np.array([[0.5, -1.5, 2.0, 0.0]]), (10, 1))
+    o, _, _ = zo.linear_attention(q, k, c)
+    _close(o, c[:6], 1e-13, "constant V, linear")
+    a = np.array([2.0, -1.0, 0.5, 3.0])
+    b = np.array([0.25, 0.0, -1.0, 1.5])
+    o2, _, _ = zo.linear_attention(q, k, c, a, b)
+    _close(o2, np.tile(a * c[0] + b, (6, 1)), 1e-13, "constant V, affine")
+    v1 = rng.standard_normal((1, 4))
+    o3, _, _ = zo.linear_attention(q, k[:1], v1)
+    _close(o3, np.tile(v1, (6, 1)), 1e-13, "single key")
+
+
+def pin_fit_vs_lstsq():
+    """The closed-form fit equals numpy's least squares on [x, 1] per channel."""
+    rng = np.random.default_rng(34)
+    x = rng.standard_normal((40, 5))
+    y = 0.7 * x + rng.standard_normal((40, 5)) * 0.3 + 0.2
+    a, b, n_deg = zo.fit_affine(x, y)
+    assert n_deg == 0
+    for c in range(5):
+        sol = np.linalg.lstsq(np.stack([x[:, c], np.ones(40)], axis=1), y[:, c], rcond=None)[0]
+        _close([a[c], b[c]], sol, 1e-12, f"fit vs lstsq c={c}")
+
+
+def pin_fit_exact_and_degenerate():
+    """Exact affine data is recovered; y = x gives (1, 0); a constant x gives (0, mean y)."""
+    rng = np.random.default_rng(35)
+    x = rng.standard_normal((25, 3))
+    a, b, _ = zo.fit_affine(x, 1.75 * x - 0.4)
+    _close(a, [1.75] * 3, 1e-12, "recover scale")
+    _close(b, [-0.4] * 3, 1e-12, "recover bias")
+    a, b, _ = zo.fit_affine(x, x)
+    _close(a, [1.0] * 3, 1e-13, "identity scale")
+    _close(b, [0.0] * 3, 1e-13, "identity bias")
+    xc = x.copy()
+    xc[:, 1] = 0.3
+    y = rng.standard_normal((25, 3))
+    a, b, n_deg = zo.fit_affine(xc, y)
+    assert n_deg == 1 and a[1] == 0.0, "degenerate channel"
+    _close(b[1], y[:, 1].mean(), 1e-13, "degenerate bias")
+
+
+# ----------------------------------------------------------------------------
+# figures the pages print
+# ----------------------------------------------------------------------------
+
+def pin_mean_sparsity_pages():
+    """The xL/yS budgets land on the pages' 'about 79%' and 'about 94%' figures."""
+    with open(os.path.join(GOLDEN, "mean_sparsity.json")) as f:
+        g = json.load(f)
+    for p in g["points"]:
+        s = zo.mean_attention_sparsity(p["linear_frac"], 1.0 - p["row_sparsity"], g["tile"])
+        assert abs(100.0 * s - p["about_percent"]) <= 1.0, f"{p}: {100 * s:.2f}%"
+
+
+ALL_PINS = [
+    pin_pool_exact_rational, pin_select_brute_force, pin_select_tiles_orientation,
+    pin_dense_vs_sdpa, pin_dense_closed_forms, pin_keep_all_equals_dense,
+    pin_tile_one_is_exact, pin_landmark_by_hand, pin_constant_tiles_closed_form,
+    pin_convexity_and_constant_values, pin_permutation_within_tile,
+    pin_tiny_workload_hot_tile, pin_elu_plus_one_vs_torch, pin_linear_brute_force,
+    pin_linear_closed_forms, pin_fit_vs_lstsq, pin_fit_exact_and_degenerate,
+    pin_mean_sparsity_pages,
+]

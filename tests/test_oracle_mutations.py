@@ -1,0 +1,139 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that a pin catches each.
+
+Every mutation below replaces one oracle function with a copy that carries a
+single mistake: a dropped term, a wrong sign or index, a transposed operand,
+a wrong tie rule. The pins must fail for every one of them; a mutation that
+no pin notices would mean that part of the oracle is not really pinned.
+"""
+
+import numpy as np
+import pytest
+
+import oracle.zebra_oracle as zo
+from oracle_pins import ALL_PINS
+
+_orig = {name: getattr(zo, name) for name in dir(zo) if not name.startswith("__")}
+
+
+def _pool_full_tile_divisor(x, tile):
+    x = np.asarray(x, dtype=np.float64)
+    b = zo.tile_bounds(x.shape[0], tile)
+    return np.stack([x[s:e].sum(axis=0) / tile for s, e in b]) if b else np.zeros((0, x.shape[1]))
+
+
+def _select_ties_high(scores_row, top_k):
+    s = np.asarray(scores_row, dtype=np.float64)
+    idx = np.arange(s.shape[0])
+    return np.sort(np.lexsort((-idx, -s))[:top_k])
+
+
+def _select_lowest(scores_row, top_k):
+    s = np.asarray(scores_row, dtype=np.float64)
+    return np.sort(np.lexsort((np.arange(s.shape[0]), s))[:top_k])
+
+
+def _scores_transposed(qbar, kbar):
+    return np.asarray(kbar, np.float64) @ np.asarray(qbar, np.float64).T
+
+
+def _columns_with(kept_bias=False, landmarks_for_all=False, drop_landmarks=False):
+    def cols(k, v, k_tile, kept):
+        k = np.asarray(k, np.float64)
+        v = np.asarray(v, np.float64)
+        bounds = zo.tile_bounds(k.shape[0], k_tile)
+        kbar, vbar = zo.pool_tiles(k, k_tile), zo.pool_tiles(v, k_tile)
+        keys, vals = [], []
+        for j in sorted(int(t) for t in kept):
+            s, e = bounds[j]
+            keys.append(k[s:e])
+            vals.append(v[s:e])
+        for j in range(len(bounds)):
+            if drop_landmarks:
+                continue
+            if landmarks_for_all or j not in set(int(t) for t in kept):
+                n = bounds[j][1] - bounds[j][0]
+                rep = n if kept_bias else 1  # a landmark counted n_j times
+                keys.append(np.repeat(kbar[j:j + 1], rep, axis=0))
+                vals.append(np.repeat(vbar[j:j + 1], rep, axis=0))
+        return np.concatenate(keys), np.concatenate(vals)
+    return cols
+
+
+def _sparse_tile_no_scale(q_rows, k, v, k_tile, kept, scale):
+    return _orig["tile_sparse_attention_tile"](q_rows, k, v, k_tile, kept, 1.0)
+
+
+def _dense_wrong_axis(q, k, v, scale, row_block=1024):
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    lg = scale * (q @ k.T)
+    w = np.exp(lg - lg.max(axis=0, keepdims=True))
+    return (w / w.sum(axis=0, keepdims=True)) @ v
+
+
+def _phi_no_exp(x):
+    return np.asarray(x, np.float64) + 1.0
+
+
+def _linear_transposed_state(q, k, v, aff_scale=None, aff_bias=None):
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    fq, fk = zo.elu_plus_one(q), zo.elu_plus_one(k)
+    state = (fk.T @ v).T
+    z = fk.sum(axis=0)
+    o = (fq @ state) / (fq @ z)[:, None]
+    if aff_scale is not None or aff_bias is not None:
+        o = zo.affine_apply(o, aff_scale, aff_bias)
+    return o, state, z
+
+
+def _linear_no_normaliser(q, k, v, aff_scale=None, aff_bias=None):
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    fq, fk = zo.elu_plus_one(q), zo.elu_plus_one(k)
+    state = fk.T @ v
+    z = fk.sum(axis=0)
+    o = fq @ state
+    if aff_scale is not None or aff_bias is not None:
+        o = zo.affine_apply(o, aff_scale, aff_bias)
+    return o, state, z
+
+
+def _fit_uncentred(x, y, degenerate_rel=1e-30):
+    x, y = np.asarray(x, np.float64), np.asarray(y, np.float64)
+    a = (x * y).sum(axis=0) / (x * x).sum(axis=0)
+    return a, np.zeros_like(a), 0
+
+
+def _fit_bias_sign(x, y, degenerate_rel=1e-30):
+    a, b, n = _orig["fit_affine"](x, y, degenerate_rel)
+    xbar = np.asarray(x, np.float64).mean(axis=0)
+    return a, b + 2 * a * xbar, n
+
+
+MUTATIONS = {
+    "pool divides by the full tile size": ("pool_tiles", _pool_full_tile_divisor),
+    "ties go to the highest index": ("select_top_tiles", _select_ties_high),
+    "selection keeps the lowest scores": ("select_top_tiles", _select_lowest),
+    "tile scores transposed": ("block_scores", _scores_transposed),
+    "landmark counted n_j times": ("attention_columns", _columns_with(kept_bias=True)),
+    "landmarks also for kept tiles": ("attention_columns", _columns_with(landmarks_for_all=True)),
+    "omitted tiles dropped": ("attention_columns", _columns_with(drop_landmarks=True)),
+    "softmax scale dropped": ("tile_sparse_attention_tile", _sparse_tile_no_scale),
+    "dense softmax over the key axis": ("dense_attention", _dense_wrong_axis),
+    "phi without the exponential branch": ("elu_plus_one", _phi_no_exp),
+    "linear state transposed": ("linear_attention", _linear_transposed_state),
+    "linear normaliser dropped": ("linear_attention", _linear_no_normaliser),
+    "fit through the origin": ("fit_affine", _fit_uncentred),
+    "fit bias sign": ("fit_affine", _fit_bias_sign),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, bad = MUTATIONS[name]
+    monkeypatch.setattr(zo, attr, bad)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin()
+        except Exception as e:  # AssertionError or a crash both count as caught
+            caught.append(f"{pin.__name__}: {type(e).__name__}")
+    assert caught, f"no pin notices the planted mistake '{name}'"
