@@ -1,0 +1,180 @@
+/*
+ * zebra.h - C ABI of the MI355X (gfx950) library for Zebra3D's layerwise
+ * hybrid global attention.
+ *
+ * Every global-attention stage of a feed-forward 3D backbone runs one of two
+ * operators (Zebra3D paper page, thelatestinai.com: Abstract and Figure 1):
+ *   - tile-sparse softmax attention: each query tile attends exactly to the
+ *     tokens of its kept key tiles, and every omitted key tile enters as one
+ *     mean-key/mean-value landmark;
+ *   - linear attention with the feature map elu(x)+1, followed by a
+ *     per-head, per-channel affine map fitted in closed form (news.hamidun.com
+ *     article "Zebra3D speeds up 3D reconstruction...", section "How Zebra3D
+ *     works"; paper page Table 3(a)).
+ *
+ * Conventions shared by every call:
+ *   - Tensor arguments are DEVICE pointers owned by the caller. The library
+ *     allocates nothing and keeps no state between calls. Scratch memory is a
+ *     caller-provided device workspace whose size the *_workspace() query
+ *     returns; a NULL workspace is allowed when the query returns 0.
+ *   - A token sequence is described by zebra_seq: element (h, n, c) of a
+ *     tensor lives at base[h * stride_head + n * stride_token + c]. The
+ *     channel dimension is contiguous. Strides are in elements; for bf16
+ *     tensors the base must be 16-byte aligned and both strides multiples
+ *     of 8.
+ *   - head_dim must be 64 (ZEBRA_ERR_UNSUPPORTED otherwise).
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *     Calls enqueue work on that stream and return without synchronising.
+ *   - Arguments are validated before any HIP call; a bad argument returns a
+ *     status code and enqueues nothing. Launch failures return ZEBRA_ERR_HIP.
+ *   - Outputs are fully overwritten and must not overlap any input.
+ *     Non-finite inputs give undefined results.
+ *   - Results are deterministic: the same inputs give bitwise identical
+ *     outputs (no floating-point atomics).
+ */
+#ifndef ZEBRA_H_
+#define ZEBRA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZEBRA_ABI_VERSION 1
+
+typedef enum zebra_status {
+  ZEBRA_OK = 0,
+  ZEBRA_ERR_INVALID_ARG = 1, /* null pointer, negative size, overlap, bad top_k */
+  ZEBRA_ERR_UNSUPPORTED = 2, /* valid request outside the implemented shapes  */
+  ZEBRA_ERR_WORKSPACE = 3,   /* workspace smaller than the query returned      */
+  ZEBRA_ERR_HIP = 4          /* the HIP runtime rejected a launch              */
+} zebra_status;
+
+typedef enum zebra_dtype { ZEBRA_BF16 = 0, ZEBRA_F32 = 1 } zebra_dtype;
+
+typedef struct zebra_seq {
+  int64_t n_tokens;     /* N, tokens per head (0 allowed: nothing to do)   */
+  int32_t n_heads;      /* H                                               */
+  int32_t head_dim;     /* d, must be 64                                   */
+  int64_t stride_token; /* elements between consecutive tokens of a head   */
+  int64_t stride_head;  /* elements between consecutive heads              */
+} zebra_seq;
+
+/*
+ * Tile pooling (landmarks). Zebra3D paper page, Figure 1 caption: omitted
+ * key/value tiles are summarised by their mean key and mean value.
+ *
+ * x        bf16 sequence described by xs.
+ * tile     tokens per tile, 1..1024. Tile t covers tokens
+ *          [t*tile, min((t+1)*tile, N)); the last tile may be short and is
+ *          averaged over its valid tokens only.
+ * mean_out float32 [H][T][64], T = ceil(N / tile), contiguous.
+ * The same call pools query tiles (for the tile scores) and key/value tiles
+ * (the landmarks). Accumulation is in float32.
+ */
+zebra_status zebra_pool_landmarks(const void* x, zebra_seq xs, int32_t tile, float* mean_out,
+                                  void* stream);
+
+/*
+ * Tile selection. The tile-sparse stage computes only selected blocks
+ * (news.hamidun.com article, "How Zebra3D works"). Score of query tile i and
+ * key tile j: s_ij = qbar_i . kbar_j (float32, unscaled). For each (head, i)
+ * the top_k key tiles are kept under the order (s_ij descending, j ascending),
+ * so equal scores go to the lower tile index.
+ *
+ * qbar     float32 [H][t_q][64], kbar float32 [H][t_k][64], contiguous
+ *          (the outputs of zebra_pool_landmarks).
+ * top_k    1..t_k; t_k at most 32768.
+ * sel_out  int32 [H][t_q][top_k], each row in ascending tile order.
+ * workspace at least zebra_select_tiles_workspace(H, t_q, t_k) bytes (the
+ *          float32 score matrix).
+ */
+size_t zebra_select_tiles_workspace(int32_t n_heads, int32_t t_q, int32_t t_k);
+zebra_status zebra_select_tiles(const float* qbar, const float* kbar, int32_t n_heads,
+                                int32_t t_q, int32_t t_k, int32_t head_dim, int32_t top_k,
+                                int32_t* sel_out, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
+ * Tile-sparse softmax attention with landmarks. Zebra3D paper page, Figure 1
+ * caption: kept tiles retain full softmax interactions and omitted tiles
+ * become mean-key/value landmarks. For each query q of query tile i:
+ *   columns  = every token of every kept key tile j in sel[h][i][*]
+ *              + one landmark (kbar_j, vbar_j) for each omitted tile j,
+ *   o(q)     = softmax(scale * q . key over columns) . value over columns.
+ * A landmark is one ordinary softmax column (no multiplicity weight).
+ *
+ * q        bf16 query sequence (qs); k, v bf16 key/value sequences sharing kvs.
+ *          qs and kvs must have the same n_heads and head_dim; the query and
+ *          key sequences may differ in length.
+ * kbar     float32 [H][t_k][64] mean keys, vbar mean values (from
+ *          zebra_pool_landmarks with k_tile); NULL iff top_k == t_k.
+ * sel      int32 [H][t_q][top_k] kept tiles, each row strictly ascending
+ *          (from zebra_select_tiles); NULL iff top_k == t_k, which is exact
+ *          dense softmax attention.
+ * q_tile   32, 64 or 128 query tokens per tile; t_q = ceil(Nq / q_tile).
+ * k_tile   32 or 64 key tokens per tile; t_k = ceil(Nk / k_tile) <= 32768.
+ * scale    softmax scale (1/sqrt(64) = 0.125 for the pages' backbones).
+ * o        output sequence (os, same H and d as qs, n_tokens == qs.n_tokens),
+ *          bf16 or float32 per o_dtype. Softmax statistics and accumulators
+ *          are float32; products run on bf16 MFMA.
+ * workspace at least zebra_tile_sparse_attn_workspace(Nk, H, 64, k_tile)
+ *          bytes: the key/value tiles repacked in the kernel's tile order.
+ */
+size_t zebra_tile_sparse_attn_workspace(int64_t n_kv, int32_t n_heads, int32_t head_dim,
+                                        int32_t k_tile);
+zebra_status zebra_tile_sparse_attn(const void* q, zebra_seq qs, const void* k, const void* v,
+                                    zebra_seq kvs, const float* kbar, const float* vbar,
+                                    const int32_t* sel, int32_t q_tile, int32_t k_tile,
+                                    int32_t top_k, float scale, void* o, zebra_seq os,
+                                    zebra_dtype o_dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
+ * Linear attention plus affine map. Tolerant stages run linear(-centered)
+ * attention (Zebra3D paper page, Abstract; Table 3(a) "Linear-centered +
+ * fit"). With phi(x) = elu(x) + 1 per channel:
+ *   S = sum_n phi(k_n) v_n^T (64x64), z = sum_n phi(k_n),
+ *   o_m = (phi(q_m)^T S) / (phi(q_m)^T z),  out_m = a (*) o_m + b.
+ * q (qs) and k, v (kvs) bf16; the query sequence may differ in length from
+ * the key/value sequence (the state comes from all of k, v).
+ * aff_scale, aff_bias  float32 [H][64] or NULL (scale 1, bias 0).
+ * o        output (os), bf16 or float32.
+ * workspace at least zebra_linear_attn_workspace(Nk, H, 64) bytes (per-chunk
+ *          partial states, reduced in a fixed order).
+ */
+size_t zebra_linear_attn_workspace(int64_t n_kv, int32_t n_heads, int32_t head_dim);
+zebra_status zebra_linear_attn(const void* q, zebra_seq qs, const void* k, const void* v,
+                               zebra_seq kvs, const float* aff_scale, const float* aff_bias,
+                               void* o, zebra_seq os, zebra_dtype o_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * Closed-form affine fit (news.hamidun.com article, "How Zebra3D works": the
+ * linear components are fitted by a closed-form affine map, no gradient
+ * descent). Per (head h, channel c), over the m samples:
+ *   a = sum (x - xbar)(y - ybar) / sum (x - xbar)^2,  b = ybar - a xbar,
+ * the least-squares solution of min sum (a x + b - y)^2. A channel with
+ * sum (x - xbar)^2 <= 1e-30 * m gets a = 0, b = ybar. Statistics are
+ * accumulated in float64.
+ *
+ * x, y     float32 [H][m][64], contiguous: x the linear output before the
+ *          affine map, y the dense softmax output at the same m queries.
+ * scale_out, bias_out  float32 [H][64].
+ * n_degenerate_out     int32 [1] device counter of degenerate channels, or NULL.
+ */
+zebra_status zebra_fit_affine(const float* x, const float* y, int32_t m, int32_t n_heads,
+                              int32_t head_dim, float* scale_out, float* bias_out,
+                              int32_t* n_degenerate_out, void* stream);
+
+/* Static strings; never NULL. */
+const char* zebra_status_string(zebra_status status);
+const char* zebra_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZEBRA_H_ */

@@ -1,0 +1,277 @@
+// C ABI of libzebra: argument validation, then kernel dispatch. Every check
+// runs before the first HIP call, so a rejected call enqueues nothing.
+#include "../../include/zebra.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <utility>
+#include <vector>
+
+#include "common.h"
+
+namespace {
+
+constexpr int32_t kMaxTileTokens = 1024;
+constexpr int32_t kMaxKeyTiles = 32768;
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi) in bytes; empty when lo == hi
+};
+
+bool seq_shape_ok(const zebra_seq& s) {
+  return s.n_tokens >= 0 && s.n_heads >= 0 && s.stride_token >= 0 && s.stride_head >= 0;
+}
+
+bool seq_empty(const zebra_seq& s) { return s.n_tokens == 0 || s.n_heads == 0; }
+
+Range seq_range(const void* p, const zebra_seq& s, size_t elem) {
+  if (seq_empty(s) || p == nullptr) return {0, 0};
+  const uintptr_t base = (uintptr_t)p;
+  const uint64_t last = (uint64_t)(s.n_heads - 1) * (uint64_t)s.stride_head +
+                        (uint64_t)(s.n_tokens - 1) * (uint64_t)s.stride_token +
+                        (uint64_t)s.head_dim;
+  return {base, base + (uintptr_t)(last * elem)};
+}
+
+Range flat_range(const void* p, uint64_t count, size_t elem) {
+  if (p == nullptr || count == 0) return {0, 0};
+  return {(uintptr_t)p, (uintptr_t)p + (uintptr_t)(count * elem)};
+}
+
+bool overlaps(Range a, Range b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+// An output sequence must not write one element twice: the (stride, extent)
+// pairs of its three dimensions, sorted by stride, must nest.
+bool seq_self_disjoint(const zebra_seq& s) {
+  if (seq_empty(s)) return true;
+  std::vector<std::pair<int64_t, int64_t>> dims = {{1, s.head_dim}};
+  if (s.n_tokens > 1) dims.push_back({s.stride_token, s.n_tokens});
+  if (s.n_heads > 1) dims.push_back({s.stride_head, s.n_heads});
+  std::sort(dims.begin(), dims.end());
+  int64_t extent = 0;
+  for (auto& d : dims) {
+    if (d.first < extent) return false;
+    extent = d.first * d.second;
+  }
+  return true;
+}
+
+// bf16 or f32 sequence with 16-byte aligned rows
+zebra_status check_seq(const void* p, const zebra_seq& s, bool is_output) {
+  if (!seq_shape_ok(s)) return ZEBRA_ERR_INVALID_ARG;
+  if (s.head_dim != zebra::kHeadDim) return ZEBRA_ERR_UNSUPPORTED;
+  if (seq_empty(s)) return ZEBRA_OK;
+  if (p == nullptr) return ZEBRA_ERR_INVALID_ARG;
+  if (((uintptr_t)p % 16) != 0 || (s.stride_token % 8) != 0 || (s.stride_head % 8) != 0)
+    return ZEBRA_ERR_UNSUPPORTED;
+  if (is_output && !seq_self_disjoint(s)) return ZEBRA_ERR_INVALID_ARG;
+  return ZEBRA_OK;
+}
+
+zebra_status hip_status(hipError_t e) { return e == hipSuccess ? ZEBRA_OK : ZEBRA_ERR_HIP; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" {
+
+const char* zebra_status_string(zebra_status status) {
+  switch (status) {
+    case ZEBRA_OK:
+      return "ZEBRA_OK";
+    case ZEBRA_ERR_INVALID_ARG:
+      return "ZEBRA_ERR_INVALID_ARG: bad pointer, size, stride, overlap or top_k";
+    case ZEBRA_ERR_UNSUPPORTED:
+      return "ZEBRA_ERR_UNSUPPORTED: head_dim, tile size, alignment or length not implemented";
+    case ZEBRA_ERR_WORKSPACE:
+      return "ZEBRA_ERR_WORKSPACE: workspace smaller than the size query returned";
+    case ZEBRA_ERR_HIP:
+      return "ZEBRA_ERR_HIP: the HIP runtime rejected a launch";
+  }
+  return "unknown zebra_status";
+}
+
+const char* zebra_version(void) { return "zebra 0.1.0 (gfx950, ABI 1)"; }
+
+zebra_status zebra_pool_landmarks(const void* x, zebra_seq xs, int32_t tile, float* mean_out,
+                                  void* stream) {
+  zebra_status st = check_seq(x, xs, false);
+  if (st != ZEBRA_OK) return st;
+  if (tile < 1) return ZEBRA_ERR_INVALID_ARG;
+  if (tile > kMaxTileTokens) return ZEBRA_ERR_UNSUPPORTED;
+  if (seq_empty(xs)) return ZEBRA_OK;
+  if (mean_out == nullptr || ((uintptr_t)mean_out % 16) != 0) return ZEBRA_ERR_INVALID_ARG;
+  const int64_t t = ceil_div(xs.n_tokens, tile);
+  const Range out = flat_range(mean_out, (uint64_t)xs.n_heads * t * zebra::kHeadDim, 4);
+  if (overlaps(out, seq_range(x, xs, 2))) return ZEBRA_ERR_INVALID_ARG;
+  return hip_status(zebra::launch_pool((const uint16_t*)x, xs.n_tokens, xs.n_heads,
+                                       xs.stride_token, xs.stride_head, tile, mean_out,
+                                       (hipStream_t)stream));
+}
+
+size_t zebra_select_tiles_workspace(int32_t n_heads, int32_t t_q, int32_t t_k) {
+  if (n_heads <= 0 || t_q <= 0 || t_k <= 0) return 0;
+  return (size_t)n_heads * (size_t)t_q * (size_t)t_k * sizeof(float);
+}
+
+zebra_status zebra_select_tiles(const float* qbar, const float* kbar, int32_t n_heads,
+                                int32_t t_q, int32_t t_k, int32_t head_dim, int32_t top_k,
+                                int32_t* sel_out, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (n_heads < 0 || t_q < 0 || t_k < 0) return ZEBRA_ERR_INVALID_ARG;
+  if (head_dim != zebra::kHeadDim) return ZEBRA_ERR_UNSUPPORTED;
+  if (t_k > kMaxKeyTiles) return ZEBRA_ERR_UNSUPPORTED;
+  if (n_heads == 0 || t_q == 0) return ZEBRA_OK;
+  if (t_k == 0 || top_k < 1 || top_k > t_k) return ZEBRA_ERR_INVALID_ARG;
+  if (qbar == nullptr || kbar == nullptr || sel_out == nullptr) return ZEBRA_ERR_INVALID_ARG;
+  const size_t need = zebra_select_tiles_workspace(n_heads, t_q, t_k);
+  if (workspace == nullptr || workspace_bytes < need) return ZEBRA_ERR_WORKSPACE;
+  if (((uintptr_t)workspace % 16) != 0 || ((uintptr_t)qbar % 16) != 0 ||
+      ((uintptr_t)kbar % 16) != 0 || ((uintptr_t)sel_out % 4) != 0)
+    return ZEBRA_ERR_INVALID_ARG;
+  const Range sel = flat_range(sel_out, (uint64_t)n_heads * t_q * top_k, 4);
+  const Range ws = flat_range(workspace, need, 1);
+  const Range qr = flat_range(qbar, (uint64_t)n_heads * t_q * head_dim, 4);
+  const Range kr = flat_range(kbar, (uint64_t)n_heads * t_k * head_dim, 4);
+  if (overlaps(sel, qr) || overlaps(sel, kr) || overlaps(sel, ws) || overlaps(ws, qr) ||
+      overlaps(ws, kr))
+    return ZEBRA_ERR_INVALID_ARG;
+  return hip_status(zebra::launch_select(qbar, kbar, n_heads, t_q, t_k, top_k, sel_out,
+                                         (float*)workspace, (hipStream_t)stream));
+}
+
+size_t zebra_tile_sparse_attn_workspace(int64_t n_kv, int32_t n_heads, int32_t head_dim,
+                                        int32_t k_tile) {
+  if (n_kv <= 0 || n_heads <= 0 || head_dim != zebra::kHeadDim) return 0;
+  if (k_tile != 32 && k_tile != 64) return 0;
+  return zebra::sparse_workspace_bytes(n_kv, n_heads, k_tile);
+}
+
+zebra_status zebra_tile_sparse_attn(const void* q, zebra_seq qs, const void* k, const void* v,
+                                    zebra_seq kvs, const float* kbar, const float* vbar,
+                                    const int32_t* sel, int32_t q_tile, int32_t k_tile,
+                                    int32_t top_k, float scale, void* o, zebra_seq os,
+                                    zebra_dtype o_dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  zebra_status st;
+  if ((st = check_seq(q, qs, false)) != ZEBRA_OK) return st;
+  if ((st = check_seq(k, kvs, false)) != ZEBRA_OK) return st;
+  if ((st = check_seq(v, kvs, false)) != ZEBRA_OK) return st;
+  if ((st = check_seq(o, os, true)) != ZEBRA_OK) return st;
+  if (o_dtype != ZEBRA_BF16 && o_dtype != ZEBRA_F32) return ZEBRA_ERR_INVALID_ARG;
+  if (qs.n_heads != kvs.n_heads || os.n_heads != qs.n_heads || os.n_tokens != qs.n_tokens)
+    return ZEBRA_ERR_INVALID_ARG;
+  if (q_tile != 32 && q_tile != 64 && q_tile != 128) return ZEBRA_ERR_UNSUPPORTED;
+  if (k_tile != 32 && k_tile != 64) return ZEBRA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || scale > 1e30f) return ZEBRA_ERR_INVALID_ARG;
+  if (seq_empty(qs)) return ZEBRA_OK;
+  if (kvs.n_tokens == 0) return ZEBRA_ERR_INVALID_ARG;  // no keys to attend to
+  const int64_t tk = ceil_div(kvs.n_tokens, k_tile);
+  if (tk > kMaxKeyTiles) return ZEBRA_ERR_UNSUPPORTED;
+  const int64_t tq = ceil_div(qs.n_tokens, q_tile);
+  if (tq * qs.n_heads > (int64_t)UINT32_MAX) return ZEBRA_ERR_UNSUPPORTED;
+  if (top_k < 1 || top_k > tk) return ZEBRA_ERR_INVALID_ARG;
+  const bool dense = top_k == tk;
+  if (!dense && (kbar == nullptr || vbar == nullptr || sel == nullptr))
+    return ZEBRA_ERR_INVALID_ARG;
+  const size_t need = dense ? 0 : zebra::sparse_workspace_bytes(kvs.n_tokens, kvs.n_heads, k_tile);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ZEBRA_ERR_WORKSPACE;
+  if (need > 0 && ((uintptr_t)workspace % 16) != 0) return ZEBRA_ERR_INVALID_ARG;
+  if (!dense && (((uintptr_t)kbar % 16) != 0 || ((uintptr_t)vbar % 16) != 0 ||
+                 ((uintptr_t)sel % 4) != 0))
+    return ZEBRA_ERR_INVALID_ARG;
+  const size_t oel = o_dtype == ZEBRA_F32 ? 4 : 2;
+  if (o_dtype == ZEBRA_F32 && (os.stride_token % 8 != 0 || os.stride_head % 8 != 0))
+    return ZEBRA_ERR_UNSUPPORTED;
+  const Range orng = seq_range(o, os, oel);
+  std::vector<Range> inputs = {seq_range(q, qs, 2), seq_range(k, kvs, 2), seq_range(v, kvs, 2)};
+  if (!dense) {
+    inputs.push_back(flat_range(kbar, (uint64_t)kvs.n_heads * tk * zebra::kHeadDim, 4));
+    inputs.push_back(flat_range(vbar, (uint64_t)kvs.n_heads * tk * zebra::kHeadDim, 4));
+    inputs.push_back(flat_range(sel, (uint64_t)kvs.n_heads * tq * top_k, 4));
+    const Range ws = flat_range(workspace, need, 1);
+    if (overlaps(ws, orng)) return ZEBRA_ERR_INVALID_ARG;
+    for (const Range& r : inputs)
+      if (overlaps(ws, r)) return ZEBRA_ERR_INVALID_ARG;
+  }
+  for (const Range& r : inputs)
+    if (overlaps(orng, r)) return ZEBRA_ERR_INVALID_ARG;
+  return hip_status(zebra::launch_tile_sparse(
+      (const uint16_t*)q, qs.n_tokens, qs.stride_token, qs.stride_head, (const uint16_t*)k,
+      (const uint16_t*)v, kvs.n_tokens, kvs.stride_token, kvs.stride_head, qs.n_heads,
+      dense ? nullptr : kbar, dense ? nullptr : vbar, dense ? nullptr : sel, q_tile, k_tile,
+      top_k, scale, o, os.stride_token, os.stride_head, o_dtype == ZEBRA_F32, workspace,
+      (hipStream_t)stream));
+}
+
+size_t zebra_linear_attn_workspace(int64_t n_kv, int32_t n_heads, int32_t head_dim) {
+  if (n_kv < 0 || n_heads <= 0 || head_dim != zebra::kHeadDim) return 0;
+  return zebra::linear_workspace_bytes(n_kv, n_heads);
+}
+
+zebra_status zebra_linear_attn(const void* q, zebra_seq qs, const void* k, const void* v,
+                               zebra_seq kvs, const float* aff_scale, const float* aff_bias,
+                               void* o, zebra_seq os, zebra_dtype o_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  zebra_status st;
+  if ((st = check_seq(q, qs, false)) != ZEBRA_OK) return st;
+  if ((st = check_seq(k, kvs, false)) != ZEBRA_OK) return st;
+  if ((st = check_seq(v, kvs, false)) != ZEBRA_OK) return st;
+  if ((st = check_seq(o, os, true)) != ZEBRA_OK) return st;
+  if (o_dtype != ZEBRA_BF16 && o_dtype != ZEBRA_F32) return ZEBRA_ERR_INVALID_ARG;
+  if (qs.n_heads != kvs.n_heads || os.n_heads != qs.n_heads || os.n_tokens != qs.n_tokens)
+    return ZEBRA_ERR_INVALID_ARG;
+  if (seq_empty(qs)) return ZEBRA_OK;
+  if (kvs.n_tokens == 0) return ZEBRA_ERR_INVALID_ARG;  // the normaliser would be zero
+  const size_t need = zebra::linear_workspace_bytes(kvs.n_tokens, kvs.n_heads);
+  if (workspace == nullptr || workspace_bytes < need) return ZEBRA_ERR_WORKSPACE;
+  if (((uintptr_t)workspace % 16) != 0) return ZEBRA_ERR_INVALID_ARG;
+  if (((uintptr_t)aff_scale % 4) != 0 || ((uintptr_t)aff_bias % 4) != 0)
+    return ZEBRA_ERR_INVALID_ARG;
+  if (o_dtype == ZEBRA_F32 && (os.stride_token % 8 != 0 || os.stride_head % 8 != 0))
+    return ZEBRA_ERR_UNSUPPORTED;
+  const size_t oel = o_dtype == ZEBRA_F32 ? 4 : 2;
+  const Range orng = seq_range(o, os, oel);
+  const Range ws = flat_range(workspace, need, 1);
+  const uint64_t aff_n = (uint64_t)qs.n_heads * zebra::kHeadDim;
+  const Range inputs[] = {seq_range(q, qs, 2), seq_range(k, kvs, 2), seq_range(v, kvs, 2),
+                          flat_range(aff_scale, aff_n, 4), flat_range(aff_bias, aff_n, 4)};
+  if (overlaps(ws, orng)) return ZEBRA_ERR_INVALID_ARG;
+  for (const Range& r : inputs)
+    if (overlaps(orng, r) || overlaps(ws, r)) return ZEBRA_ERR_INVALID_ARG;
+  return hip_status(zebra::launch_linear(
+      (const uint16_t*)q, qs.n_tokens, qs.stride_token, qs.stride_head, (const uint16_t*)k,
+      (const uint16_t*)v, kvs.n_tokens, kvs.stride_token, kvs.stride_head, qs.n_heads,
+      aff_scale, aff_bias, o, os.stride_token, os.stride_head, o_dtype == ZEBRA_F32, workspace,
+      (hipStream_t)stream));
+}
+
+zebra_status zebra_fit_affine(const float* x, const float* y, int32_t m, int32_t n_heads,
+                              int32_t head_dim, float* scale_out, float* bias_out,
+                              int32_t* n_degenerate_out, void* stream) {
+  if (m < 1 || n_heads < 0) return ZEBRA_ERR_INVALID_ARG;
+  if (head_dim != zebra::kHeadDim) return ZEBRA_ERR_UNSUPPORTED;
+  if (x == nullptr || y == nullptr || scale_out == nullptr || bias_out == nullptr)
+    return ZEBRA_ERR_INVALID_ARG;
+  if (((uintptr_t)x % 4) != 0 || ((uintptr_t)y % 4) != 0 || ((uintptr_t)scale_out % 4) != 0 ||
+      ((uintptr_t)bias_out % 4) != 0 || ((uintptr_t)n_degenerate_out % 4) != 0)
+    return ZEBRA_ERR_INVALID_ARG;
+  const uint64_t nin = (uint64_t)n_heads * m * head_dim, nout = (uint64_t)n_heads * head_dim;
+  const Range xr = flat_range(x, nin, 4), yr = flat_range(y, nin, 4);
+  const Range ar = flat_range(scale_out, nout, 4), br = flat_range(bias_out, nout, 4);
+  const Range dr = flat_range(n_degenerate_out, 1, 4);
+  const Range outs[] = {ar, br, dr};
+  for (const Range& o : outs)
+    if (overlaps(o, xr) || overlaps(o, yr)) return ZEBRA_ERR_INVALID_ARG;
+  if (overlaps(ar, br) || overlaps(ar, dr) || overlaps(br, dr)) return ZEBRA_ERR_INVALID_ARG;
+  return hip_status(zebra::launch_fit(x, y, m, n_heads, scale_out, bias_out, n_degenerate_out,
+                                      (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+"""Stage runners: one global-attention stage as a sequence of libzebra calls.
+
+A tile-sparse stage is pool(Q) + pool(K) + pool(V) -> select -> attend; a
+linear stage is one zebra_linear_attn call with the stage's fitted affine
+map. The affine map is fitted once per linear stage (calibration) against
+dense softmax attention of the same stage at sampled queries. Every step runs
+in libzebra's kernels; this module only allocates buffers and sequences calls
+on the current stream.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import (ceil_div, zebra_fit_affine, zebra_linear_attn, zebra_pool_landmarks,
+               zebra_select_tiles, zebra_tile_sparse_attn)
+
+
+@dataclasses.dataclass
+class SparseBuffers:
+    """Reusable outputs and workspaces of one tile-sparse stage shape."""
+
+    qbar: torch.Tensor
+    kbar: torch.Tensor
+    vbar: torch.Tensor
+    sel: torch.Tensor
+    out: torch.Tensor
+    select_ws: Optional[torch.Tensor] = None
+    attn_ws: Optional[torch.Tensor] = None
+
+    @classmethod
+    def allocate(cls, heads: int, n_q: int, n_kv: int, q_tile: int, k_tile: int, top_k: int,
+                 device, out_dtype=torch.bfloat16):
+        from . import library
+        t_q, t_k = ceil_div(n_q, q_tile), ceil_div(n_kv, k_tile)
+        lib = library()
+        f32 = dict(dtype=torch.float32, device=device)
+        sws = lib.zebra_select_tiles_workspace(heads, t_q, t_k)
+        aws = lib.zebra_tile_sparse_attn_workspace(n_kv, heads, 64, k_tile)
+        return cls(
+            qbar=torch.empty((heads, t_q, 64), **f32),
+            kbar=torch.empty((heads, t_k, 64), **f32),
+            vbar=torch.empty((heads, t_k, 64), **f32),
+            sel=torch.empty((heads, t_q, top_k), dtype=torch.int32, device=device),
+            out=torch.empty((heads, n_q, 64), dtype=out_dtype, device=device),
+            select_ws=torch.empty(max(sws, 1), dtype=torch.uint8, device=device),
+            attn_ws=torch.empty(max(aws, 1), dtype=torch.uint8, device=device),
+        )
+
+
+def sparse_stage(q, k, v, q_tile: int, k_tile: int, top_k: int, scale: float,
+                 bufs: Optional[SparseBuffers] = None) -> SparseBuffers:
+    """One tile-sparse stage; returns the buffers (out, sel, means) it filled."""
+    if bufs is None:
+        bufs = SparseBuffers.allocate(q.shape[0], q.shape[1], k.shape[1], q_tile, k_tile, top_k,
+                                      q.device)
+    zebra_pool_landmarks(q, q_tile, out=bufs.qbar)
+    zebra_pool_landmarks(k, k_tile, out=bufs.kbar)
+    zebra_pool_landmarks(v, k_tile, out=bufs.vbar)
+    zebra_select_tiles(bufs.qbar, bufs.kbar, top_k, out=bufs.sel, workspace=bufs.select_ws)
+    zebra_tile_sparse_attn(q, k, v, bufs.kbar, bufs.vbar, bufs.sel, q_tile, k_tile, top_k, scale,
+                           out=bufs.out, workspace=bufs.attn_ws)
+    return bufs
+
+
+def linear_stage(q, k, v, aff_scale=None, aff_bias=None, out=None, workspace=None):
+    """One linear stage with its affine map."""
+    return zebra_linear_attn(q, k, v, aff_scale, aff_bias, out=out, workspace=workspace)
+
+
+@dataclasses.dataclass
+class Calibration:
+    aff_scale: torch.Tensor  # [H][64]
+    aff_bias: torch.Tensor   # [H][64]
+    n_degenerate: int
+    sample_index: torch.Tensor
+    x: torch.Tensor  # unfitted linear output at the samples, float32 [H][M][64]
+    y: torch.Tensor  # dense softmax output at the samples, float32 [H][M][64]
+
+
+def calibrate_linear(q, k, v, sample_index: torch.Tensor, scale: float, k_tile: int = 64,
+                     q_tile: int = 64) -> Calibration:
+    """Fit a, b of one linear stage against dense softmax attention at the sampled queries."""
+    qs = q.index_select(1, sample_index).contiguous()
+    t_k = ceil_div(k.shape[1], k_tile)
+    y = zebra_tile_sparse_attn(qs, k, v, None, None, None, q_tile, k_tile, t_k, scale,
+                               out_dtype=torch.float32)
+    x = zebra_linear_attn(qs, k, v, out_dtype=torch.float32)
+    a, b, n_deg = zebra_fit_affine(x, y)
+    return Calibration(a, b, int(n_deg.item()), sample_index, x, y)

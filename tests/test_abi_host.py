@@ -1,0 +1,142 @@
+"""Host-side checks of the C ABI: exported symbols and argument validation.
+
+Nothing here launches a kernel: every call below is rejected by validation,
+which the library performs before any HIP call, so these run without a GPU.
+Device pointers are stand-in integers that are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_hybrid_attention_zebra_amd as zb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zebra.h")
+P = lambda a: ctypes.c_void_p(a)  # fake, 16-byte aligned device addresses
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zebra_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return zb.library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 10, names
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in zebra.h but not exported"
+    assert set(names) == set(zb.ENTRY_POINTS)
+
+
+def test_version_and_status_strings(lib):
+    assert "gfx950" in zb.version()
+    for s in range(5):
+        assert zb.status_string(s).startswith("ZEBRA_")
+
+
+def seq(n, h=2, d=64, st=64, sh=None):
+    return zb.ZebraSeq(n, h, d, st, n * st if sh is None else sh)
+
+
+def test_pool_validation(lib):
+    f = lib.zebra_pool_landmarks
+    assert f(None, seq(128), 32, P(1 << 20), None) == zb.ZEBRA_ERR_INVALID_ARG
+    assert f(P(1 << 16), seq(128, d=32), 32, P(1 << 20), None) == zb.ZEBRA_ERR_UNSUPPORTED
+    assert f(P(1 << 16), seq(128), 0, P(1 << 20), None) == zb.ZEBRA_ERR_INVALID_ARG
+    assert f(P(1 << 16), seq(128), 2048, P(1 << 20), None) == zb.ZEBRA_ERR_UNSUPPORTED
+    assert f(P(1 << 16), seq(128), 32, None, None) == zb.ZEBRA_ERR_INVALID_ARG
+    assert f(P((1 << 16) + 2), seq(128), 32, P(1 << 20), None) == zb.ZEBRA_ERR_UNSUPPORTED
+    assert f(P(1 << 16), seq(128, st=60), 32, P(1 << 20), None) == zb.ZEBRA_ERR_UNSUPPORTED
+    assert f(P(1 << 16), seq(-1), 32, P(1 << 20), None) == zb.ZEBRA_ERR_INVALID_ARG
+    # output overlapping the input
+    assert f(P(1 << 16), seq(128), 32, P((1 << 16) + 64), None) == zb.ZEBRA_ERR_INVALID_ARG
+    # empty input: nothing to do, no launch
+    assert f(P(1 << 16), seq(0), 32, None, None) == zb.ZEBRA_OK
+
+
+def test_select_validation(lib):
+    f = lib.zebra_select_tiles
+    ws = lib.zebra_select_tiles_workspace(2, 10, 20)
+    assert ws == 2 * 10 * 20 * 4
+    args = lambda top_k=5, hd=64, ws_ptr=P(1 << 30), ws_b=ws, tk=20: (
+        P(1 << 16), P(1 << 20), 2, 10, tk, hd, top_k, P(1 << 24), ws_ptr, ws_b, None)
+    assert f(*args(top_k=0)) == zb.ZEBRA_ERR_INVALID_ARG
+    assert f(*args(top_k=21)) == zb.ZEBRA_ERR_INVALID_ARG
+    assert f(*args(hd=128)) == zb.ZEBRA_ERR_UNSUPPORTED
+    assert f(*args(ws_ptr=None)) == zb.ZEBRA_ERR_WORKSPACE
+    assert f(*args(ws_b=ws - 1)) == zb.ZEBRA_ERR_WORKSPACE
+    assert f(*args(tk=40000)) == zb.ZEBRA_ERR_UNSUPPORTED
+    assert f(P(1 << 16), P(1 << 20), 2, 10, 20, 64, 5, P(1 << 16), P(1 << 30), ws, None) == \
+        zb.ZEBRA_ERR_INVALID_ARG  # selection written over qbar
+
+
+def test_sparse_validation(lib):
+    f = lib.zebra_tile_sparse_attn
+    s = seq(256)
+    ws = lib.zebra_tile_sparse_attn_workspace(256, 2, 64, 64)
+    assert ws > 0
+
+    def call(q_tile=64, k_tile=64, top_k=2, scale=0.125, o=P(1 << 28), sel=P(1 << 24),
+             kbar=P(1 << 22), ws_p=P(1 << 30), ws_b=ws, os_=s, dtype=0):
+        return f(P(1 << 16), s, P(1 << 18), P(1 << 20), s, kbar, P(1 << 23), sel, q_tile, k_tile,
+                 top_k, scale, o, os_, dtype, ws_p, ws_b, None)
+
+    assert call(q_tile=48) == zb.ZEBRA_ERR_UNSUPPORTED
+    assert call(k_tile=128) == zb.ZEBRA_ERR_UNSUPPORTED
+    assert call(top_k=0) == zb.ZEBRA_ERR_INVALID_ARG
+    assert call(top_k=5) == zb.ZEBRA_ERR_INVALID_ARG  # t_k = 4
+    assert call(scale=0.0) == zb.ZEBRA_ERR_INVALID_ARG
+    assert call(sel=None) == zb.ZEBRA_ERR_INVALID_ARG  # sparse needs sel
+    assert call(kbar=None) == zb.ZEBRA_ERR_INVALID_ARG
+    assert call(ws_p=None) == zb.ZEBRA_ERR_WORKSPACE
+    assert call(ws_b=ws - 1) == zb.ZEBRA_ERR_WORKSPACE
+    assert call(o=P(1 << 16)) == zb.ZEBRA_ERR_INVALID_ARG  # output over q
+    assert call(os_=seq(255)) == zb.ZEBRA_ERR_INVALID_ARG  # output length != query length
+    assert call(os_=seq(256, st=32)) == zb.ZEBRA_ERR_UNSUPPORTED or \
+        call(os_=seq(256, st=32)) == zb.ZEBRA_ERR_INVALID_ARG  # rows overlap themselves
+    assert call(dtype=7) == zb.ZEBRA_ERR_INVALID_ARG
+
+
+def test_linear_validation(lib):
+    f = lib.zebra_linear_attn
+    s = seq(300)
+    ws = lib.zebra_linear_attn_workspace(300, 2, 64)
+    assert ws > 0
+
+    def call(o=P(1 << 28), ws_p=P(1 << 30), ws_b=ws, kvs=s, a=None):
+        return f(P(1 << 16), s, P(1 << 18), P(1 << 20), kvs, a, None, o, s, 0, ws_p, ws_b, None)
+
+    assert call(ws_p=None) == zb.ZEBRA_ERR_WORKSPACE
+    assert call(ws_b=ws - 4) == zb.ZEBRA_ERR_WORKSPACE
+    assert call(o=P(1 << 18)) == zb.ZEBRA_ERR_INVALID_ARG  # output over k
+    assert call(kvs=seq(0)) == zb.ZEBRA_ERR_INVALID_ARG
+    assert call(a=P(1 << 28)) == zb.ZEBRA_ERR_INVALID_ARG  # affine scale inside the output
+    assert call(kvs=seq(300, h=3)) == zb.ZEBRA_ERR_INVALID_ARG  # head count mismatch
+
+
+def test_fit_validation(lib):
+    f = lib.zebra_fit_affine
+    assert f(P(1 << 16), P(1 << 20), 0, 2, 64, P(1 << 24), P(1 << 25), None, None) == \
+        zb.ZEBRA_ERR_INVALID_ARG
+    assert f(P(1 << 16), P(1 << 20), 10, 2, 32, P(1 << 24), P(1 << 25), None, None) == \
+        zb.ZEBRA_ERR_UNSUPPORTED
+    assert f(None, P(1 << 20), 10, 2, 64, P(1 << 24), P(1 << 25), None, None) == \
+        zb.ZEBRA_ERR_INVALID_ARG
+    assert f(P(1 << 16), P(1 << 20), 10, 2, 64, P(1 << 16), P(1 << 25), None, None) == \
+        zb.ZEBRA_ERR_INVALID_ARG  # scale written over x
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((1, 64, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        zb.zebra_pool_landmarks(x, 64)

@@ -1,0 +1,259 @@
+"""GPU parity of every libzebra entry point against the CPU oracle, small and ragged shapes.
+
+All calls go through the C ABI (the ctypes binding). Inputs are seeded
+synthetic draws; the oracle receives the same bf16-rounded values in float64.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.zebra_oracle as zo
+import linear_hybrid_attention_zebra_amd as zb
+from linear_hybrid_attention_zebra_amd import stage, synth
+from parity_util import assert_close, bf16_gpu, check_selection, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _clustered(seed, heads, n_q, n_kv, q_tile, k_tile, n_hot):
+    q, k, v, _ = synth.clustered_qkv_np(seed, heads, n_q, 64, q_tile, k_tile, n_hot, n_kv=n_kv)
+    return synth.bf16_round(q), synth.bf16_round(k), synth.bf16_round(v)
+
+
+# ----------------------------------------------------------------------------
+# pool
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("heads,n,tile,layout", [
+    (2, 128, 32, "hnd"), (3, 70, 32, "hnd"), (2, 300, 64, "nhd"), (1, 1, 64, "hnd"),
+    (2, 1000, 128, "nhd"), (2, 65, 1, "hnd"), (2, 3000, 1024, "hnd"), (16, 21984, 64, "hnd"),
+])
+def test_pool_parity(heads, n, tile, layout):
+    print(f"[case] pool H={heads} N={n} tile={tile} {layout}", flush=True)
+    rng = np.random.default_rng(n + tile)
+    x = synth.bf16_round(rng.standard_normal((heads, n, 64)).astype(np.float32) * 3)
+    xg = bf16_gpu(x)
+    if layout == "nhd":
+        xg = xg.permute(1, 0, 2).contiguous().permute(1, 0, 2)  # token-major storage
+    got = zb.zebra_pool_landmarks(xg, tile)
+    torch.cuda.synchronize()
+    ref = np.stack([zo.pool_tiles(x[h], tile) for h in range(heads)])
+    err = np.max(np.abs(to_f64(got) - ref) / np.maximum(1.0, np.abs(ref)))
+    assert err <= 2e-6, f"pool relative error {err:.2e}"
+
+
+def test_pool_empty_is_noop():
+    x = torch.empty((2, 0, 64), dtype=torch.bfloat16, device=DEV)
+    out = zb.zebra_pool_landmarks(x, 64)
+    assert out.shape == (2, 0, 64)
+
+
+# ----------------------------------------------------------------------------
+# select
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("tq,tk,top_k", [(7, 300, 1), (7, 300, 69), (7, 300, 300), (5, 4, 1),
+                                         (3, 9000, 1320), (4, 21984, 1320)])
+def test_select_parity(tq, tk, top_k):
+    print(f"[case] select Tq={tq} Tk={tk} k={top_k}", flush=True)
+    rng = np.random.default_rng(tk + top_k)
+    qbar = rng.standard_normal((2, tq, 64)).astype(np.float32)
+    kbar = rng.standard_normal((2, tk, 64)).astype(np.float32)
+    sel = zb.zebra_select_tiles(torch.from_numpy(qbar).to(DEV), torch.from_numpy(kbar).to(DEV),
+                                top_k)
+    torch.cuda.synchronize()
+    scores = np.stack([zo.block_scores(qbar[h], kbar[h]) for h in range(2)])
+    swaps = check_selection(sel.cpu().numpy(), scores, top_k)
+    print(f"[parity] select near-tie rows with swaps: {swaps}", flush=True)
+
+
+def test_select_exact_ties_go_to_lowest_index():
+    """Duplicated key means tie bitwise; the lower tile index must win every tie."""
+    rng = np.random.default_rng(7)
+    base = rng.integers(-3, 4, size=(6, 64)).astype(np.float32)
+    kbar = base[rng.integers(0, 6, size=500)][None]  # 500 tiles, 6 distinct rows
+    qbar = rng.integers(-2, 3, size=(1, 9, 64)).astype(np.float32)
+    for top_k in (1, 37, 250, 499):
+        sel = zb.zebra_select_tiles(torch.from_numpy(qbar).to(DEV), torch.from_numpy(kbar).to(DEV),
+                                    top_k).cpu().numpy()
+        ref = zo.select_tiles(qbar[0], kbar[0], top_k)
+        assert np.array_equal(sel[0], ref), f"top_k={top_k}"
+
+
+def test_select_all_equal_scores():
+    qbar = torch.zeros((1, 3, 64), device=DEV)
+    kbar = torch.ones((1, 2000, 64), device=DEV)
+    sel = zb.zebra_select_tiles(qbar, kbar, 700).cpu().numpy()
+    assert np.array_equal(sel[0, 0], np.arange(700))
+
+
+# ----------------------------------------------------------------------------
+# tile-sparse attention
+# ----------------------------------------------------------------------------
+
+SPARSE_CASES = [
+    # (q_tile, k_tile, n_q, n_kv, top_k, n_hot, heads)
+    (32, 32, 128, 128, 1, 1, 2),      # the tiny two-view workload
+    (64, 64, 300, 300, 2, 2, 2),      # ragged last tiles on both sides
+    (128, 64, 300, 450, 3, 2, 2),     # 128-token query tiles, Nq != Nk
+    (32, 32, 200, 97, 2, 1, 3),
+    (64, 32, 130, 200, 3, 2, 2),
+    (128, 32, 257, 300, 4, 2, 1),
+    (64, 64, 64, 64, 1, 1, 1),        # a single key tile
+    (64, 64, 1000, 1000, 16, 3, 2),   # every tile kept: sel given, no landmarks
+    (64, 64, 2000, 2000, 7, 3, 2),
+]
+
+
+@pytest.mark.parametrize("case", SPARSE_CASES, ids=[str(c) for c in SPARSE_CASES])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_sparse_stage_parity(case, out_dtype):
+    q_tile, k_tile, n_q, n_kv, top_k, n_hot, heads = case
+    print(f"[case] sparse {case} {out_dtype}", flush=True)
+    q, k, v = _clustered(sum(case), heads, n_q, n_kv, q_tile, k_tile, n_hot)
+    qg, kg, vg = bf16_gpu(q), bf16_gpu(k), bf16_gpu(v)
+    bufs = stage.SparseBuffers.allocate(heads, n_q, n_kv, q_tile, k_tile, top_k, DEV, out_dtype)
+    stage.sparse_stage(qg, kg, vg, q_tile, k_tile, top_k, 0.125, bufs)
+    torch.cuda.synchronize()
+    sel = bufs.sel.cpu().numpy()
+    scores = np.stack([zo.block_scores(zo.pool_tiles(q[h], q_tile), zo.pool_tiles(k[h], k_tile))
+                       for h in range(heads)])
+    swaps = check_selection(sel, scores, top_k)
+    ref, _ = zo.tile_sparse_attention(q, k, v, q_tile, k_tile, top_k, 0.125, sel=sel)
+    assert_close(bufs.out, ref, f"sparse {case}")
+    print(f"[parity] near-tie swaps {swaps}", flush=True)
+
+
+@pytest.mark.parametrize("q_tile,k_tile,n_q,n_kv", [(64, 64, 300, 300), (128, 64, 130, 700),
+                                                    (32, 32, 100, 65)])
+def test_dense_mode_parity(q_tile, k_tile, n_q, n_kv):
+    """sel = NULL with top_k = T_k is exact dense softmax attention."""
+    print(f"[case] dense q_tile={q_tile} k_tile={k_tile} Nq={n_q} Nk={n_kv}", flush=True)
+    q, k, v = _clustered(5, 2, n_q, n_kv, q_tile, k_tile, 2)
+    t_k = -(-n_kv // k_tile)
+    out = zb.zebra_tile_sparse_attn(bf16_gpu(q), bf16_gpu(k), bf16_gpu(v), None, None, None,
+                                    q_tile, k_tile, t_k, 0.125, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = np.stack([zo.dense_attention(q[h], k[h], v[h], 0.125) for h in range(2)])
+    assert_close(out, ref, "dense mode")
+
+
+def test_sparse_strided_layout():
+    """Token-major [N][H][64] storage for q, k, v and the output."""
+    q, k, v = _clustered(9, 3, 250, 250, 64, 64, 2)
+    tm = lambda x: bf16_gpu(x).permute(1, 0, 2).contiguous().permute(1, 0, 2)
+    qg, kg, vg = tm(q), tm(k), tm(v)
+    out = torch.empty((250, 3, 64), dtype=torch.bfloat16, device=DEV).permute(1, 0, 2)
+    bufs = stage.SparseBuffers.allocate(3, 250, 250, 64, 64, 2, DEV)
+    bufs.out = out
+    stage.sparse_stage(qg, kg, vg, 64, 64, 2, 0.125, bufs)
+    torch.cuda.synchronize()
+    sel = bufs.sel.cpu().numpy()
+    ref, _ = zo.tile_sparse_attention(q, k, v, 64, 64, 2, 0.125, sel=sel)
+    assert_close(out, ref, "strided sparse")
+
+
+def test_sparse_is_deterministic():
+    q, k, v = _clustered(11, 2, 700, 700, 64, 64, 3)
+    outs = []
+    for _ in range(2):
+        bufs = stage.sparse_stage(bf16_gpu(q), bf16_gpu(k), bf16_gpu(v), 64, 64, 3, 0.125)
+        outs.append((bufs.out.clone(), bufs.sel.clone()))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_constant_tiles_closed_form_on_gpu():
+    """Key tiles of one repeated key/value: the landmark counts once, a kept
+    tile n_j times (pins the single-column landmark reading on the GPU)."""
+    rng = np.random.default_rng(3)
+    n_kv, bk = 64 * 5 + 20, 64
+    t_k = -(-n_kv // bk)
+    kap = synth.bf16_round(rng.standard_normal((t_k, 64)).astype(np.float32))
+    nu = synth.bf16_round(rng.standard_normal((t_k, 64)).astype(np.float32))
+    k = np.repeat(kap, bk, axis=0)[:n_kv][None]
+    v = np.repeat(nu, bk, axis=0)[:n_kv][None]
+    q = synth.bf16_round(rng.standard_normal((1, 64, 64)).astype(np.float32))
+    bufs = stage.sparse_stage(bf16_gpu(q), bf16_gpu(k), bf16_gpu(v), 64, 64, 2, 0.125)
+    torch.cuda.synchronize()
+    kept = bufs.sel.cpu().numpy()[0, 0]
+    n_j = np.array([min(bk, n_kv - j * bk) for j in range(t_k)], dtype=np.float64)
+    mult = np.where(np.isin(np.arange(t_k), kept), n_j, 1.0)
+    ell = 0.125 * (q[0].astype(np.float64) @ kap.T.astype(np.float64))
+    w = mult * np.exp(ell - ell.max(axis=1, keepdims=True))
+    expect = (w @ nu) / w.sum(axis=1, keepdims=True)
+    assert_close(bufs.out[0], expect, "constant tiles")
+
+
+# ----------------------------------------------------------------------------
+# linear attention and the fit
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n_q,n_kv,affine,out_dtype", [
+    (128, 128, False, torch.bfloat16), (300, 300, True, torch.bfloat16),
+    (70, 1000, True, torch.float32), (1, 5, False, torch.float32), (5000, 5000, True, torch.bfloat16),
+])
+def test_linear_parity(n_q, n_kv, affine, out_dtype):
+    print(f"[case] linear Nq={n_q} Nk={n_kv} affine={affine} {out_dtype}", flush=True)
+    rng = np.random.default_rng(n_q + n_kv)
+    heads = 3
+    q = synth.bf16_round(rng.standard_normal((heads, n_q, 64)).astype(np.float32))
+    k = synth.bf16_round(rng.standard_normal((heads, n_kv, 64)).astype(np.float32))
+    v = synth.bf16_round(rng.standard_normal((heads, n_kv, 64)).astype(np.float32))
+    a = rng.uniform(0.5, 2.0, (heads, 64)).astype(np.float32) if affine else None
+    b = rng.uniform(-0.1, 0.1, (heads, 64)).astype(np.float32) if affine else None
+    tg = lambda x: None if x is None else torch.from_numpy(x).to(DEV)
+    out = zb.zebra_linear_attn(bf16_gpu(q), bf16_gpu(k), bf16_gpu(v), tg(a), tg(b),
+                               out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ref = np.stack([zo.linear_attention(q[h], k[h], v[h], None if a is None else a[h],
+                                        None if b is None else b[h])[0] for h in range(heads)])
+    tol = 5e-3 if out_dtype == torch.bfloat16 else 1e-4
+    assert_close(out, ref, f"linear Nq={n_q} Nk={n_kv}", rel_fro=tol)
+
+
+def test_linear_is_deterministic():
+    rng = np.random.default_rng(1)
+    q, k, v = (bf16_gpu(rng.standard_normal((2, 4000, 64)).astype(np.float32)) for _ in range(3))
+    o1 = zb.zebra_linear_attn(q, k, v, out_dtype=torch.float32)
+    o2 = zb.zebra_linear_attn(q, k, v, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_fit_parity():
+    rng = np.random.default_rng(4)
+    heads, m = 4, 4096
+    x = rng.standard_normal((heads, m, 64)).astype(np.float32) * 0.01
+    y = (0.8 * x + 0.003 * rng.standard_normal((heads, m, 64)) + 0.001).astype(np.float32)
+    x[1, :, 5] = 0.25  # a degenerate channel
+    a, b, nd = zb.zebra_fit_affine(torch.from_numpy(x).to(DEV), torch.from_numpy(y).to(DEV))
+    torch.cuda.synchronize()
+    for h in range(heads):
+        ra, rb, _ = zo.fit_affine(x[h], y[h])
+        np.testing.assert_allclose(to_f64(a[h]), ra, rtol=1e-5, atol=1e-7)
+        np.testing.assert_allclose(to_f64(b[h]), rb, rtol=1e-5, atol=1e-7)
+    assert int(nd.item()) == 1
+
+
+def test_calibration_pipeline_small():
+    """Fit against dense attention at sampled queries: the GPU's fit equals the
+    oracle's on the same (x, y), and x, y each match the oracle."""
+    rng = np.random.default_rng(8)
+    heads, n = 2, 3000
+    q, k, v = (synth.bf16_round(rng.standard_normal((heads, n, 64)).astype(np.float32))
+               for _ in range(3))
+    idx = synth.fit_sample_indices(n, 512, 8)
+    cal = stage.calibrate_linear(bf16_gpu(q), bf16_gpu(k), bf16_gpu(v),
+                                 torch.from_numpy(idx).to(DEV), 0.125)
+    torch.cuda.synchronize()
+    for h in range(heads):
+        y_ref = zo.dense_attention(q[h, idx], k[h], v[h], 0.125)
+        x_ref = zo.linear_attention(q[h, idx], k[h], v[h])[0]
+        assert_close(cal.y[h], y_ref, "fit target y")
+        assert_close(cal.x[h], x_ref, "fit input x", rel_fro=1e-4)
+        ra, rb, _ = zo.fit_affine(to_f64(cal.x[h]), to_f64(cal.y[h]))
+        np.testing.assert_allclose(to_f64(cal.aff_scale[h]), ra, rtol=1e-4, atol=1e-6)
+        np.testing.assert_allclose(to_f64(cal.aff_bias[h]), rb, rtol=1e-4, atol=1e-7)
