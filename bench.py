@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of the hybrid global-attention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Default workload: the 24-stage global-attention stack of a VGGT-shaped
+backbone at 512 views (703,488 tokens, 16 heads x 64), stages 0-8 and 21-23
+linear, 9-20 tile-sparse with 64x64 tiles keeping 20% of key tiles (80%
+omitted as landmarks). One step is one pass over all 24 stages:
+  * tile-sparse stage: pool Q/K/V -> select -> tile-sparse attention;
+  * linear stage: calibration (dense softmax target at 4,096 sampled queries,
+    unfitted linear output there, closed-form fit) then the linear forward
+    with the fitted affine map.
+Inputs (all 24 stages' Q/K/V, seeded synthetic draws) are resident in HBM
+before timing starts. Prints ONE JSON line.
+
+Other workloads (--workload): sparse-16v, linear-128v, sparse-1024v (one
+stage each) report the same fields for that stage.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "hybrid global-attn ms/stage + % bf16 MFMA / % HBM peak, 16→1,024 views"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+SCALE = 0.125
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[1])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=1)
+    p.add_argument("--workload", default="stack24-512v")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=8,
+                   help="sampled (head, query tile) rows for the oracle's attention step")
+    return p.parse_args()
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work (what the method must compute)
+# ----------------------------------------------------------------------------
+
+def sparse_flops(n_q, n_kv, q_tile, k_tile, top_k, sel):
+    """Algorithmic flops of one tile-sparse launch, from its selection sel [H][Tq][k].
+
+    Kept pairs: 4*d*|q tile i|*|k tile j| summed over every kept (h, i, j)
+    (QK^T and PV, 2*d each). Landmarks: 4*d*|q tile i| per omitted tile.
+    """
+    d = 64
+    heads, t_q = sel.shape[0], sel.shape[1]
+    t_k = -(-n_kv // k_tile)
+    q_sizes = np.full(t_q, q_tile, dtype=np.float64)
+    q_sizes[-1] = n_q - (t_q - 1) * q_tile
+    k_last = n_kv - (t_k - 1) * k_tile
+    has_last = (sel == t_k - 1).any(axis=-1)  # [H][Tq]
+    kept_tokens = top_k * k_tile - has_last * (k_tile - k_last)
+    selected = 4.0 * d * float(np.sum(q_sizes[None, :] * kept_tokens))
+    landmark = 4.0 * d * float(heads * np.sum(q_sizes) * (t_k - top_k))
+    return selected, landmark
+
+
+# ----------------------------------------------------------------------------
+# GPU side
+# ----------------------------------------------------------------------------
+
+class Timer:
+    """HIP events on the current stream, accumulated per label."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.open = {}
+        self.pairs = {}
+
+    def start(self, label):
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record()
+        self.open[label] = ev
+
+    def stop(self, label):
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record()
+        self.pairs.setdefault(label, []).append((self.open.pop(label), ev))
+
+    def ms(self, label):
+        return [a.elapsed_time(b) for a, b in self.pairs.get(label, [])]
+
+    def reset(self):
+        self.pairs = {}
+
+
+def run_gpu(args, w, torch, zb, stage_mod, synth):
+    dev = torch.device("cuda", 0)
+    heads, n = w.heads, w.n_tokens
+    stages = list(range(w.n_stages)) if w.kind == "stack" else [0]
+    kinds = {s: w.stage_kind(s) for s in stages}
+    t_gen = time.time()
+    inputs = {s: synth.stage_inputs(w, s, dev) for s in stages}
+    torch.cuda.synchronize()
+    gen_s = time.time() - t_gen
+
+    t_k = -(-n // w.k_tile)
+    top_k = w.k if any(k == "sparse" for k in kinds.values()) else None
+    sparse_bufs = None
+    if top_k is not None:
+        sparse_bufs = stage_mod.SparseBuffers.allocate(heads, n, n, w.q_tile, w.k_tile, top_k, dev)
+    lin_out = torch.empty((heads, n, 64), dtype=torch.bfloat16, device=dev)
+    lin_ws = torch.empty(zb.library().zebra_linear_attn_workspace(n, heads, 64),
+                         dtype=torch.uint8, device=dev)
+    fit_idx = {s: torch.from_numpy(synth.fit_sample_indices(n, w.fit_samples, w.stage_seed(s)))
+               .to(dev) for s in stages if kinds[s] == "linear"}
+    timer = Timer(torch)
+
+    def step():
+        for s in stages:
+            q, k, v = inputs[s]
+            if kinds[s] == "sparse":
+                timer.start("sparse_stage")
+                zb.zebra_pool_landmarks(q, w.q_tile, out=sparse_bufs.qbar)
+                zb.zebra_pool_landmarks(k, w.k_tile, out=sparse_bufs.kbar)
+                zb.zebra_pool_landmarks(v, w.k_tile, out=sparse_bufs.vbar)
+                zb.zebra_select_tiles(sparse_bufs.qbar, sparse_bufs.kbar, top_k,
+                                      out=sparse_bufs.sel, workspace=sparse_bufs.select_ws)
+                timer.start("sparse_attn")
+                zb.zebra_tile_sparse_attn(q, k, v, sparse_bufs.kbar, sparse_bufs.vbar,
+                                          sparse_bufs.sel, w.q_tile, w.k_tile, top_k, SCALE,
+                                          out=sparse_bufs.out, workspace=sparse_bufs.attn_ws)
+                timer.stop("sparse_attn")
+                timer.stop("sparse_stage")
+            else:
+                timer.start("calibration")
+                cal = stage_mod.calibrate_linear(q, k, v, fit_idx[s], SCALE, w.k_tile)
+                timer.stop("calibration")
+                timer.start("linear_stage")
+                zb.zebra_linear_attn(q, k, v, cal.aff_scale, cal.aff_bias, out=lin_out,
+                                     workspace=lin_ws)
+                timer.stop("linear_stage")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timer.reset()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    res = {"wall_s": wall, "gen_s": gen_s, "stages": len(stages),
+           "n_sparse": sum(k == "sparse" for k in kinds.values()),
+           "n_linear": sum(k == "linear" for k in kinds.values())}
+    for label in ("sparse_stage", "sparse_attn", "calibration", "linear_stage"):
+        vals = timer.ms(label)
+        if vals:
+            res[label + "_ms"] = float(np.mean(vals))
+            res[label + "_ms_median"] = float(np.median(vals))
+    if top_k is not None:
+        sel = sparse_bufs.sel.cpu().numpy()
+        res["selected_flops"], res["landmark_flops"] = sparse_flops(
+            n, n, w.q_tile, w.k_tile, top_k, sel)
+        res["top_k"] = top_k
+        res["t_k"] = t_k
+    res["linear_bytes"] = heads * 64 * 4 * n * 2  # Q, K, V in and O out, bf16
+    return res, inputs
+
+
+# ----------------------------------------------------------------------------
+# CPU oracle baseline on a bounded sample of the same workload
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(args, w, torch, inputs, synth):
+    import oracle.zebra_oracle as zo
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    n, heads = w.n_tokens, w.heads
+    stages = list(range(w.n_stages)) if w.kind == "stack" else [0]
+    sparse_s = [s for s in stages if w.stage_kind(s) == "sparse"]
+    linear_s = [s for s in stages if w.stage_kind(s) == "linear"]
+    f64 = lambda t: t.to("cpu", torch.float32).numpy().astype(np.float64)
+    est = {}
+    sample = []
+    if sparse_s:
+        s = sparse_s[0]
+        q, k, v = (f64(t[0]) for t in inputs[s])  # head 0
+        t0 = time.perf_counter()
+        qbar, kbar = zo.pool_tiles(q, w.q_tile), zo.pool_tiles(k, w.k_tile)
+        zo.pool_tiles(v, w.k_tile)
+        sel = zo.select_tiles(qbar, kbar, w.k)
+        per_head = time.perf_counter() - t0
+        rows = synth.sample_rows(1, qbar.shape[0], args.cpu_rows, 17)[:, 1]
+        t0 = time.perf_counter()
+        for i in rows:
+            s0, e0 = i * w.q_tile, min(n, (i + 1) * w.q_tile)
+            zo.tile_sparse_attention_tile(q[s0:e0], k, v, w.k_tile, sel[i], SCALE)
+        per_row = (time.perf_counter() - t0) / len(rows)
+        est["sparse_stage_s"] = heads * per_head + heads * qbar.shape[0] * per_row
+        sample.append(f"sparse stage {s}: pool+select of head 0 in full, attention of "
+                      f"{len(rows)} query tiles of head 0")
+    if linear_s:
+        s = linear_s[0]
+        q, k, v = (f64(t[0]) for t in inputs[s])
+        t0 = time.perf_counter()
+        zo.linear_attention(q, k, v)
+        lin_head = time.perf_counter() - t0
+        m_sub = 64
+        idx = synth.fit_sample_indices(n, m_sub, 23)
+        t0 = time.perf_counter()
+        y = zo.dense_attention(q[idx], k, v, SCALE)
+        x = zo.linear_attention(q[idx], k, v)[0]
+        zo.fit_affine(x, y)
+        cal_part = time.perf_counter() - t0
+        est["linear_stage_s"] = heads * lin_head
+        est["calibration_s"] = heads * cal_part * (w.fit_samples / m_sub)
+        sample.append(f"linear stage {s}: head 0 in full; calibration of head 0 on "
+                      f"{m_sub} of {w.fit_samples} sampled queries")
+    total = (len(sparse_s) * est.get("sparse_stage_s", 0.0)
+             + len(linear_s) * (est.get("linear_stage_s", 0.0) + est.get("calibration_s", 0.0)))
+    return {"value": 1000.0 * total / len(stages), "unit": "ms/stage", "cores": int(threads),
+            "kind": "oracle",
+            "sample": "; ".join(sample) + "; scaled to all heads, query tiles and samples "
+                      "(extrapolated)",
+            "per_stage_s": est}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path "
+              "shards by head across GPUs, which this build does not run.", file=sys.stderr)
+        sys.exit(2)
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import torch
+    import linear_hybrid_attention_zebra_amd as zb
+    from linear_hybrid_attention_zebra_amd import stage as stage_mod, synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    zb.library()  # fails loudly if libzebra.so is missing
+    w = synth.WORKLOADS[args.workload]
+    res, inputs = run_gpu(args, w, torch, zb, stage_mod, synth)
+    print(f"[bench] gpu done: {json.dumps(res)}", file=sys.stderr, flush=True)
+
+    ms_per_step = 1000.0 * res["wall_s"] / args.steps
+    n_stages = res["stages"]
+    out = {
+        "metric": METRIC, "value": ms_per_step / n_stages, "unit": "ms/stage", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "views": w.n_views, "tokens": w.n_tokens,
+                   "heads": w.heads, "head_dim": w.head_dim, "stages": n_stages,
+                   "linear_stages": list(w.linear_stages) if w.kind == "stack" else None,
+                   "q_tile": w.q_tile, "k_tile": w.k_tile, "keep_percent": w.keep_percent,
+                   "top_k": res.get("top_k"), "fit_samples": w.fit_samples,
+                   "parallelism": "single GPU"},
+    }
+    stage_ms = {}
+    for key in ("sparse_stage_ms", "sparse_attn_ms", "linear_stage_ms", "calibration_ms"):
+        if key in res:
+            stage_ms[key] = res[key]
+    if "linear_stage_ms" in res:
+        stage_ms["linear_hbm_frac"] = (res["linear_bytes"] / (res["linear_stage_ms"] * 1e-3)
+                                       / 1e9) / PEAK_HBM_GBS
+    out["stage_ms"] = stage_ms
+    if "sparse_attn_ms" in res:
+        sec = res["sparse_attn_ms"] * 1e-3
+        achieved = res["selected_flops"] / sec / 1e12
+        out["roofline"] = {"kernel": "tile_sparse_kernel", "bound": "mfma",
+                           "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                           "achieved_with_landmarks": (res["selected_flops"]
+                                                       + res["landmark_flops"]) / sec / 1e12,
+                           "flops_per_launch": res["selected_flops"]}
+    elif "linear_stage_ms" in res:
+        sec = res["linear_stage_ms"] * 1e-3
+        achieved = res["linear_bytes"] / sec / 1e9
+        out["roofline"] = {"kernel": "linear attention (state+reduce+apply)", "bound": "hbm",
+                           "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                           "bytes_per_launch": res["linear_bytes"]}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args, w, torch, inputs, synth)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -120,11 +120,13 @@ zebra_status zebra_select_tiles(const float* qbar, const float* kbar, int32_t n_
  * o        output sequence (os, same H and d as qs, n_tokens == qs.n_tokens),
  *          bf16 or float32 per o_dtype. Softmax statistics and accumulators
  *          are float32; products run on bf16 MFMA.
- * workspace at least zebra_tile_sparse_attn_workspace(Nk, H, 64, k_tile)
- *          bytes: the key/value tiles repacked in the kernel's tile order.
+ * workspace at least zebra_tile_sparse_attn_workspace(Nq, Nk, H, 64, q_tile,
+ *          k_tile, top_k) bytes (0 when top_k == t_k): the landmarks as bf16
+ *          and, per (head, query tile), the ascending list of omitted tiles.
  */
-size_t zebra_tile_sparse_attn_workspace(int64_t n_kv, int32_t n_heads, int32_t head_dim,
-                                        int32_t k_tile);
+size_t zebra_tile_sparse_attn_workspace(int64_t n_q, int64_t n_kv, int32_t n_heads,
+                                        int32_t head_dim, int32_t q_tile, int32_t k_tile,
+                                        int32_t top_k);
 zebra_status zebra_tile_sparse_attn(const void* q, zebra_seq qs, const void* k, const void* v,
                                     zebra_seq kvs, const float* kbar, const float* vbar,
                                     const int32_t* sel, int32_t q_tile, int32_t k_tile,

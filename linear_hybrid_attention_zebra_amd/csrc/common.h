@@ -70,7 +70,8 @@ hipError_t launch_pool(const uint16_t* x, int64_t n, int32_t heads, int64_t st, 
 hipError_t launch_select(const float* qbar, const float* kbar, int32_t heads, int32_t tq,
                          int32_t tk, int32_t top_k, int32_t* sel, float* scores,
                          hipStream_t s);
-size_t sparse_workspace_bytes(int64_t n_kv, int32_t heads, int32_t k_tile);
+size_t sparse_workspace_bytes(int64_t n_q, int64_t n_kv, int32_t heads, int32_t q_tile,
+                              int32_t k_tile, int32_t top_k);
 hipError_t launch_tile_sparse(const uint16_t* q, int64_t nq, int64_t qst, int64_t qsh,
                               const uint16_t* k, const uint16_t* v, int64_t nk, int64_t kst,
                               int64_t ksh, int32_t heads, const float* kbar, const float* vbar,

@@ -146,11 +146,14 @@ zebra_status zebra_select_tiles(const float* qbar, const float* kbar, int32_t n_
                                          (float*)workspace, (hipStream_t)stream));
 }
 
-size_t zebra_tile_sparse_attn_workspace(int64_t n_kv, int32_t n_heads, int32_t head_dim,
-                                        int32_t k_tile) {
-  if (n_kv <= 0 || n_heads <= 0 || head_dim != zebra::kHeadDim) return 0;
+size_t zebra_tile_sparse_attn_workspace(int64_t n_q, int64_t n_kv, int32_t n_heads,
+                                        int32_t head_dim, int32_t q_tile, int32_t k_tile,
+                                        int32_t top_k) {
+  if (n_q <= 0 || n_kv <= 0 || n_heads <= 0 || head_dim != zebra::kHeadDim) return 0;
   if (k_tile != 32 && k_tile != 64) return 0;
-  return zebra::sparse_workspace_bytes(n_kv, n_heads, k_tile);
+  if (q_tile != 32 && q_tile != 64 && q_tile != 128) return 0;
+  if (top_k < 1) return 0;
+  return zebra::sparse_workspace_bytes(n_q, n_kv, n_heads, q_tile, k_tile, top_k);
 }
 
 zebra_status zebra_tile_sparse_attn(const void* q, zebra_seq qs, const void* k, const void* v,
@@ -180,7 +183,9 @@ zebra_status zebra_tile_sparse_attn(const void* q, zebra_seq qs, const void* k, 
   const bool dense = top_k == tk;
   if (!dense && (kbar == nullptr || vbar == nullptr || sel == nullptr))
     return ZEBRA_ERR_INVALID_ARG;
-  const size_t need = dense ? 0 : zebra::sparse_workspace_bytes(kvs.n_tokens, kvs.n_heads, k_tile);
+  const size_t need = dense ? 0
+                            : zebra::sparse_workspace_bytes(qs.n_tokens, kvs.n_tokens,
+                                                            kvs.n_heads, q_tile, k_tile, top_k);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ZEBRA_ERR_WORKSPACE;
   if (need > 0 && ((uintptr_t)workspace % 16) != 0) return ZEBRA_ERR_INVALID_ARG;
   if (!dense && (((uintptr_t)kbar % 16) != 0 || ((uintptr_t)vbar % 16) != 0 ||

@@ -39,7 +39,7 @@ class SparseBuffers:
         lib = library()
         f32 = dict(dtype=torch.float32, device=device)
         sws = lib.zebra_select_tiles_workspace(heads, t_q, t_k)
-        aws = lib.zebra_tile_sparse_attn_workspace(n_kv, heads, 64, k_tile)
+        aws = lib.zebra_tile_sparse_attn_workspace(n_q, n_kv, heads, 64, q_tile, k_tile, top_k)
         return cls(
             qbar=torch.empty((heads, t_q, 64), **f32),
             kbar=torch.empty((heads, t_k, 64), **f32),

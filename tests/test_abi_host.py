@@ -82,7 +82,7 @@ def test_select_validation(lib):
 def test_sparse_validation(lib):
     f = lib.zebra_tile_sparse_attn
     s = seq(256)
-    ws = lib.zebra_tile_sparse_attn_workspace(256, 2, 64, 64)
+    ws = lib.zebra_tile_sparse_attn_workspace(256, 256, 2, 64, 64, 64, 2)
     assert ws > 0
 
     def call(q_tile=64, k_tile=64, top_k=2, scale=0.125, o=P(1 << 28), sel=P(1 << 24),
