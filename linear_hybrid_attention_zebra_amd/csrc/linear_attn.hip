@@ -34,8 +34,12 @@ constexpr int kBlockTok = 64;
 constexpr int kStateFloats = kHeadDim * kHeadDim + kHeadDim;  // S then z
 constexpr int kTargetStateBlocks = 2048;
 
+// Byte offset of 16-byte chunk `chunk` of 128-byte row `row`: chunks are
+// XORed with a function of the row that keeps the transposed operand reads
+// (4 consecutive rows, 64 contiguous bytes each) bank-conflict free.
 __device__ __forceinline__ uint32_t swz(int row, int chunk) {
-  return (uint32_t)(row * 128 + ((chunk ^ (row & 7)) << 4));
+  const int f = (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  return (uint32_t)(row * 128 + ((chunk ^ f) << 4));
 }
 
 __device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }

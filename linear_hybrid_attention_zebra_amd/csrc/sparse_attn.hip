@@ -58,8 +58,14 @@ struct SparseParams {
   int32_t o_f32;
 };
 
+// Byte offset of 16-byte chunk `chunk` of 128-byte row `row` in a tile. The
+// chunk index is XORed with a function of the row chosen so that both MFMA
+// operand reads are bank-conflict free on gfx950's LDS: the K read (16 lanes
+// on 16 consecutive rows, same chunk) and the transposed V read (4
+// consecutive rows, 64 contiguous bytes each).
+__device__ __forceinline__ int swz_f(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
 __device__ __forceinline__ uint32_t swz(int row, int chunk) {
-  return (uint32_t)(row * 128 + ((chunk ^ (row & 7)) << 4));
+  return (uint32_t)(row * 128 + ((chunk ^ swz_f(row)) << 4));
 }
 
 // Workgroup barrier without the memory fence of __syncthreads(): that fence
@@ -183,14 +189,17 @@ __global__ __launch_bounds__(QT * 2) void tile_sparse_kernel(SparseParams p,
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 
   // ---- direct-to-LDS staging. 1 KB block u of a tile holds rows 8u..8u+7;
-  // lane i writes physical chunk i%8 of row 8u + i/8, i.e. logical chunk
-  // (i%8) ^ (i/8). This wave stages blocks u = wave + W v.
+  // lane i writes physical chunk i%8 of row r = 8u + i/8, i.e. logical chunk
+  // (i%8) ^ swz_f(r). This wave stages blocks u = wave + W v.
   const int lrow = lane >> 3;
-  const int lchunk = (lane & 7) ^ lrow;
+  int lchunk[NU];
   uint32_t off_kv[NU];
 #pragma unroll
-  for (int v = 0; v < NU; ++v)
-    off_kv[v] = (uint32_t)((8 * (wave + W * v) + lrow) * p.kst * 2 + lchunk * 16);
+  for (int v = 0; v < NU; ++v) {
+    const int r = 8 * (wave + W * v) + lrow;
+    lchunk[v] = (lane & 7) ^ swz_f(r);
+    off_kv[v] = (uint32_t)(r * p.kst * 2 + lchunk[v] * 16);
+  }
   auto dma = [&](const void* src, lds_blk* dst, int u) {
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&dst[u][0], 16,
                                      0, 0);
@@ -217,7 +226,7 @@ __global__ __launch_bounds__(QT * 2) void tile_sparse_kernel(SparseParams p,
 #pragma unroll
       for (int v = 0; v < NU; ++v) {
         const int r = min(8 * (wave + W * v) + lrow, tail_rows - 1);
-        off[v] = short_tile ? (uint32_t)(r * p.kst * 2 + lchunk * 16) : off_kv[v];
+        off[v] = short_tile ? (uint32_t)(r * p.kst * 2 + lchunk[v] * 16) : off_kv[v];
       }
     } else {
       const int e0 = n_kept + (t - n_kept) * KT - win_lo;
@@ -227,7 +236,7 @@ __global__ __launch_bounds__(QT * 2) void tile_sparse_kernel(SparseParams p,
 #pragma unroll
       for (int v = 0; v < NU; ++v) {
         const int r = min(8 * (wave + W * v) + lrow, rows - 1);
-        off[v] = (uint32_t)win[e0 + r] * 128u + (uint32_t)lchunk * 16u;
+        off[v] = (uint32_t)win[e0 + r] * 128u + (uint32_t)lchunk[v] * 16u;
       }
     }
     lds_blk* kd = kbuf(stc);
