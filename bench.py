@@ -43,7 +43,23 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=8,
                    help="sampled (head, query tile) rows for the oracle's attention step")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB three times (the "
+                        "reference kernel that scales the HBM byte counters) and exit")
     return p.parse_args()
+
+
+def copy_probe(mib: int):
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters, divided by
+    the bytes it must move, give the scale applied to the attention kernel's counters."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
 
 
 # ----------------------------------------------------------------------------
@@ -236,6 +252,9 @@ def cpu_baseline(args, w, torch, inputs, synth):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path "
               "shards by head across GPUs, which this build does not run.", file=sys.stderr)
@@ -270,6 +289,9 @@ def main():
     for key in ("sparse_stage_ms", "sparse_attn_ms", "linear_stage_ms", "calibration_ms"):
         if key in res:
             stage_ms[key] = res[key]
+    fwd = res.get("n_sparse", 0) * res.get("sparse_stage_ms", 0.0) + res.get("n_linear", 0) * \
+        res.get("linear_stage_ms", 0.0)
+    stage_ms["forward_ms_per_stage"] = fwd / n_stages  # without the one-off affine fit
     if "linear_stage_ms" in res:
         stage_ms["linear_hbm_frac"] = (res["linear_bytes"] / (res["linear_stage_ms"] * 1e-3)
                                        / 1e9) / PEAK_HBM_GBS

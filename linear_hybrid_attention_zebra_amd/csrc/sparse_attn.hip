@@ -547,8 +547,8 @@ hipError_t launch_tile_sparse(const uint16_t* q, int64_t nq, int64_t qst, int64_
   }
   if (k_tile == 64) {
     if (q_tile == 32) return launch_kernel<32, 64, 2>(p, sel, heads, s);
-    if (q_tile == 64) return launch_kernel<64, 64, 3>(p, sel, heads, s);
-    return launch_kernel<128, 64, 3>(p, sel, heads, s);
+    if (q_tile == 64) return launch_kernel<64, 64, 2>(p, sel, heads, s);
+    return launch_kernel<128, 64, 2>(p, sel, heads, s);
   }
   if (q_tile == 32) return launch_kernel<32, 32, 3>(p, sel, heads, s);
   if (q_tile == 64) return launch_kernel<64, 32, 3>(p, sel, heads, s);
