@@ -14,9 +14,9 @@
  *
  * Conventions shared by every call:
  *   - Tensor arguments are DEVICE pointers owned by the caller. The library
- *     allocates nothing and keeps no state between calls. Scratch memory is a
- *     caller-provided device workspace whose size the *_workspace() query
- *     returns; a NULL workspace is allowed when the query returns 0.
+ *     allocates nothing and keeps no state between calls. Scratch memory is
+ *     a caller-provided device workspace whose size the *_workspace() query
+ *     returns.
  *   - A token sequence is described by zebra_seq: element (h, n, c) of a
  *     tensor lives at base[h * stride_head + n * stride_token + c]. The
  *     channel dimension is contiguous. Strides are in elements; for bf16
@@ -121,8 +121,11 @@ zebra_status zebra_select_tiles(const float* qbar, const float* kbar, int32_t n_
  *          bf16 or float32 per o_dtype. Softmax statistics and accumulators
  *          are float32; products run on bf16 MFMA.
  * workspace at least zebra_tile_sparse_attn_workspace(Nq, Nk, H, 64, q_tile,
- *          k_tile, top_k) bytes (0 when top_k == t_k): the landmarks as bf16
- *          and, per (head, query tile), the ascending list of omitted tiles.
+ *          k_tile, top_k) bytes, 16-byte aligned: the landmarks as bf16 (when
+ *          top_k < t_k) and per-head maxima of the key norms and value
+ *          magnitudes. Never 0; the contents on return are unspecified.
+ * The key/value token stride must be at most 2^24 elements
+ * (ZEBRA_ERR_UNSUPPORTED otherwise).
  */
 size_t zebra_tile_sparse_attn_workspace(int64_t n_q, int64_t n_kv, int32_t n_heads,
                                         int32_t head_dim, int32_t q_tile, int32_t k_tile,

@@ -206,8 +206,8 @@ def zebra_tile_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         if not (sel.is_contiguous() and kbar.is_contiguous() and vbar.is_contiguous()):
             raise ValueError("sel, kbar and vbar must be contiguous")
     lib = library()
-    nbytes = 0 if sel is None else lib.zebra_tile_sparse_attn_workspace(
-        q.shape[1], k.shape[1], k.shape[0], HEAD_DIM, q_tile, k_tile, top_k)
+    nbytes = lib.zebra_tile_sparse_attn_workspace(q.shape[1], k.shape[1], k.shape[0], HEAD_DIM,
+                                                  q_tile, k_tile, top_k)
     workspace = _workspace(nbytes, q.device, workspace)
     _check("zebra_tile_sparse_attn", lib.zebra_tile_sparse_attn(
         _ptr(q), seq_of(q), _ptr(k), _ptr(v), seq_of(k), _ptr(kbar), _ptr(vbar), _ptr(sel),

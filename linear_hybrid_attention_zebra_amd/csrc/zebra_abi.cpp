@@ -183,11 +183,12 @@ zebra_status zebra_tile_sparse_attn(const void* q, zebra_seq qs, const void* k, 
   const bool dense = top_k == tk;
   if (!dense && (kbar == nullptr || vbar == nullptr || sel == nullptr))
     return ZEBRA_ERR_INVALID_ARG;
-  const size_t need = dense ? 0
-                            : zebra::sparse_workspace_bytes(qs.n_tokens, kvs.n_tokens,
-                                                            kvs.n_heads, q_tile, k_tile, top_k);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ZEBRA_ERR_WORKSPACE;
-  if (need > 0 && ((uintptr_t)workspace % 16) != 0) return ZEBRA_ERR_INVALID_ARG;
+  // the kernel addresses rows of one key tile with 32-bit byte offsets
+  if (kvs.stride_token > (int64_t)1 << 24) return ZEBRA_ERR_UNSUPPORTED;
+  const size_t need = zebra::sparse_workspace_bytes(qs.n_tokens, kvs.n_tokens, kvs.n_heads,
+                                                    q_tile, k_tile, top_k);
+  if (workspace == nullptr || workspace_bytes < need) return ZEBRA_ERR_WORKSPACE;
+  if (((uintptr_t)workspace % 16) != 0) return ZEBRA_ERR_INVALID_ARG;
   if (!dense && (((uintptr_t)kbar % 16) != 0 || ((uintptr_t)vbar % 16) != 0 ||
                  ((uintptr_t)sel % 4) != 0))
     return ZEBRA_ERR_INVALID_ARG;
@@ -200,11 +201,11 @@ zebra_status zebra_tile_sparse_attn(const void* q, zebra_seq qs, const void* k, 
     inputs.push_back(flat_range(kbar, (uint64_t)kvs.n_heads * tk * zebra::kHeadDim, 4));
     inputs.push_back(flat_range(vbar, (uint64_t)kvs.n_heads * tk * zebra::kHeadDim, 4));
     inputs.push_back(flat_range(sel, (uint64_t)kvs.n_heads * tq * top_k, 4));
-    const Range ws = flat_range(workspace, need, 1);
-    if (overlaps(ws, orng)) return ZEBRA_ERR_INVALID_ARG;
-    for (const Range& r : inputs)
-      if (overlaps(ws, r)) return ZEBRA_ERR_INVALID_ARG;
   }
+  const Range ws = flat_range(workspace, need, 1);
+  if (overlaps(ws, orng)) return ZEBRA_ERR_INVALID_ARG;
+  for (const Range& r : inputs)
+    if (overlaps(ws, r)) return ZEBRA_ERR_INVALID_ARG;
   for (const Range& r : inputs)
     if (overlaps(orng, r)) return ZEBRA_ERR_INVALID_ARG;
   return hip_status(zebra::launch_tile_sparse(

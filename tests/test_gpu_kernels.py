@@ -140,6 +140,37 @@ def test_dense_mode_parity(q_tile, k_tile, n_q, n_kv):
     assert_close(out, ref, "dense mode")
 
 
+@pytest.mark.parametrize("kind", ["mixed_q", "large_v", "dense_large_q"])
+def test_sparse_both_softmax_references(kind):
+    """Items whose logit bound is loose (large |q|) or whose values are huge take
+    the running-maximum path; the others the fixed-bound path, in one launch."""
+    print(f"[case] sparse reference paths {kind}", flush=True)
+    q, k, v = _clustered(21, 2, 700, 700, 64, 64, 3)
+    v_scale = 1.0
+    if kind == "mixed_q":
+        q = q.copy()
+        q[:, 128:320] *= 8.0  # query tiles 2..4: bound far above the fast-path limit
+        q = synth.bf16_round(q)
+    elif kind == "large_v":
+        v_scale = 2.0 ** 41
+        v = synth.bf16_round(v * v_scale)
+    else:
+        q = synth.bf16_round(q * 8.0)
+    qg, kg, vg = bf16_gpu(q), bf16_gpu(k), bf16_gpu(v)
+    if kind == "dense_large_q":
+        out = zb.zebra_tile_sparse_attn(qg, kg, vg, None, None, None, 64, 64, 11, 0.125,
+                                        out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        ref = np.stack([zo.dense_attention(q[h], k[h], v[h], 0.125) for h in range(2)])
+    else:
+        bufs = stage.SparseBuffers.allocate(2, 700, 700, 64, 64, 3, DEV, torch.float32)
+        stage.sparse_stage(qg, kg, vg, 64, 64, 3, 0.125, bufs)
+        torch.cuda.synchronize()
+        out = bufs.out
+        ref, _ = zo.tile_sparse_attention(q, k, v, 64, 64, 3, 0.125, sel=bufs.sel.cpu().numpy())
+    assert_close(to_f64(out) / v_scale, ref / v_scale, f"reference paths {kind}")
+
+
 def test_sparse_strided_layout():
     """Token-major [N][H][64] storage for q, k, v and the output."""
     q, k, v = _clustered(9, 3, 250, 250, 64, 64, 2)
