@@ -6,19 +6,22 @@
 //   S = sum_n phi(k_n) v_n^T,  z = sum_n phi(k_n),
 //   out_m = a (*) (phi(q_m)^T S) / (phi(q_m)^T z) + b.
 //
-// Three kernels, all streaming at HBM rate:
+// Three kernels, streaming at HBM rate:
 //  1. state: per (head, token chunk) partial S and z. K and V blocks of 64
-//     tokens go to LDS row-major; phi(K) is formed in float32 and split into
-//     bf16 hi + lo parts (phi = hi + lo to ~2^-17), so two bf16 MFMAs give a
-//     float32-grade product. The contraction runs over tokens, so both MFMA
-//     operands are read token-transposed with ds_read_b64_tr_b16. Each of the
-//     4 waves owns one 32x32 quarter of S.
+//     tokens go to LDS row-major (the next block's loads in flight while one
+//     is used); phi(K) is formed in float32 and split into bf16 hi + lo parts
+//     (phi = hi + lo to ~2^-17), so two bf16 MFMAs give a float32-grade
+//     product. The contraction runs over tokens, so both MFMA operands are
+//     read token-transposed with ds_read_b64_tr_b16. Each of the 4 waves owns
+//     one 32x32 quarter of S.
 //  2. reduce: partial states summed over chunks in a fixed order (float64),
-//     then the affine map folded into the state: a (*) (phi^T S)/(phi^T z) + b
-//     = phi^T (S diag(a) + z b^T) / (phi^T z). The folded state is stored as
-//     bf16 hi/lo MFMA A-operands.
-//  3. apply: O^T = S'^T phi(Q)^T with three bf16 MFMAs per product (hi.hi,
-//     hi.lo, lo.hi); the denominator phi(q).z is a float32 dot product.
+//     one thread per state element, into a float32 S and z per head.
+//  3. apply: each workgroup folds the affine map into the state,
+//     a (*) (phi^T S)/(phi^T z) + b = phi^T (S diag(a) + z b^T) / (phi^T z),
+//     and keeps the folded state as bf16 hi/lo MFMA A-operands in registers;
+//     then O^T = S'^T phi(Q)^T with three bf16 MFMAs per product (hi.hi,
+//     hi.lo, lo.hi) and the float32 denominator phi(q).z, 32 queries per wave
+//     and step, the next step's query loads in flight.
 // No atomics: the result is bitwise reproducible.
 #include <algorithm>
 
@@ -75,10 +78,13 @@ __global__ __launch_bounds__(256) void linear_state_kernel(const uint16_t* __res
                                                            int64_t nk, int64_t kst, int64_t ksh,
                                                            int64_t chunk_tok, int32_t nchunks,
                                                            float* __restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) uint8_t khi[kBlockTok * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t klo[kBlockTok * 128];
+  // phi(K) hi and lo tiles, then (after the last block) the z reduction buffer
+  __shared__ __attribute__((aligned(16))) uint8_t kt[2 * kBlockTok * 128];
   __shared__ __attribute__((aligned(16))) uint8_t vls[kBlockTok * 128];
-  __shared__ float zred[256][9];
+  uint8_t* khi = kt;
+  uint8_t* klo = kt + kBlockTok * 128;
+  float(*zred)[9] = (float(*)[9])kt;
+  static_assert(256 * 9 * sizeof(float) <= sizeof(kt), "z buffer fits");
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int chunk = blockIdx.x, h = blockIdx.y;
@@ -93,19 +99,33 @@ __global__ __launch_bounds__(256) void linear_state_kernel(const uint16_t* __res
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
   float z8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
+  // this thread's two 16-byte pieces of a 64-token block: row e/8, chunk e%8;
+  // the next block's loads are in flight while one block is used
+  u32x4 kn[2], vn[2];
+  auto load_block = [&](int64_t b0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + 256 * u;
+      const int64_t tok = b0 + (e >> 3);
+      kn[u] = u32x4{0u, 0u, 0u, 0u};
+      vn[u] = u32x4{0u, 0u, 0u, 0u};
+      if (tok < t1) {
+        kn[u] = *(const u32x4*)(kh + tok * kst + 8 * (e & 7));
+        vn[u] = *(const u32x4*)(vh + tok * kst + 8 * (e & 7));
+      }
+    }
+  };
+  load_block(t0);
   for (int64_t b0 = t0; b0 < t1; b0 += kBlockTok) {
-    __syncthreads();
+    const u32x4 kc[2] = {kn[0], kn[1]}, vc[2] = {vn[0], vn[1]};
+    load_block(b0 + kBlockTok);
+    __syncthreads();  // the previous block's LDS reads are done
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int e = tid + 256 * u;
       const int r = e >> 3, c = e & 7;
-      const int64_t tok = b0 + r;
-      u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-      const bool ok = tok < t1;
-      if (ok) {
-        kw = *(const u32x4*)(kh + tok * kst + 8 * c);
-        vw = *(const u32x4*)(vh + tok * kst + 8 * c);
-      }
+      const bool ok = b0 + r < t1;
+      const u32x4 kw = kc[u];
       float f[8];
       f[0] = phi(bf16lo(kw.x));
       f[1] = phi(bf16hi(kw.x));
@@ -125,7 +145,7 @@ __global__ __launch_bounds__(256) void linear_state_kernel(const uint16_t* __res
       split8(f, hi, lo);
       *(u32x4*)(khi + swz(r, c)) = hi;
       *(u32x4*)(klo + swz(r, c)) = lo;
-      *(u32x4*)(vls + swz(r, c)) = vw;
+      *(u32x4*)(vls + swz(r, c)) = vc[u];
     }
     __syncthreads();
     // S[c][e] += sum_n phi(K)[n][c] V[n][e]: A = phi(K)^T (channels x tokens),
@@ -156,6 +176,7 @@ __global__ __launch_bounds__(256) void linear_state_kernel(const uint16_t* __res
     out[c * kHeadDim + e] = acc[i];
   }
   // z: threads with the same tid%8 own the same 8 channels; fixed-order sum
+  __syncthreads();  // the K tiles are no longer read
 #pragma unroll
   for (int i = 0; i < 8; ++i) zred[tid][i] = z8[i];
   __syncthreads();
@@ -167,130 +188,169 @@ __global__ __launch_bounds__(256) void linear_state_kernel(const uint16_t* __res
   }
 }
 
-// Sums partials in chunk order, folds the affine map, writes the apply
-// kernel's operands: for e-block eb, k-step s, lane l, element j:
-// S'[16s + 8(l/32) + j][32eb + l%32], as bf16 hi and lo; then z (float32).
+// Sums the partial states in chunk order (float64): one thread per element of
+// [S | z], 8 chunks per round with their loads issued together.
 __global__ __launch_bounds__(256) void linear_reduce_kernel(const float* __restrict__ partial,
                                                             int32_t nchunks,
-                                                            const float* __restrict__ aff_a,
-                                                            const float* __restrict__ aff_b,
-                                                            uint16_t* __restrict__ sop,
-                                                            float* __restrict__ zout) {
-  __shared__ float st[kStateFloats];
-  const int h = blockIdx.x, tid = threadIdx.x;
-  const float* ph = partial + (int64_t)h * nchunks * kStateFloats;
-  for (int e = tid; e < kStateFloats; e += 256) {
-    double s = 0.0;
-    for (int c = 0; c < nchunks; ++c) s += (double)ph[(int64_t)c * kStateFloats + e];
-    st[e] = (float)s;
+                                                            float* __restrict__ state) {
+  const int h = blockIdx.y;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= kStateFloats) return;
+  const float* ph = partial + (int64_t)h * nchunks * kStateFloats + e;
+  double s = 0.0;
+  int c = 0;
+  for (; c + 8 <= nchunks; c += 8) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = ph[(int64_t)(c + i) * kStateFloats];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += (double)x[i];
   }
-  __syncthreads();
-  const float* z = st + kHeadDim * kHeadDim;
-  // element index: ((eb * 4 + s) * 64 + lane) * 8 + j, hi half then lo half
-  uint16_t* hi_out = sop + (int64_t)h * 2 * 4096;
-  uint16_t* lo_out = hi_out + 4096;
-  for (int idx = tid; idx < 4096; idx += 256) {
-    const int j = idx & 7, lane = (idx >> 3) & 63, s = (idx >> 9) & 3, eb = idx >> 11;
-    const int c = 16 * s + 8 * (lane >> 5) + j;
-    const int e = 32 * eb + (lane & 31);
-    const float a = aff_a ? aff_a[h * kHeadDim + e] : 1.f;
-    const float b = aff_b ? aff_b[h * kHeadDim + e] : 0.f;
-    const float val = a * st[c * kHeadDim + e] + z[c] * b;
-    const uint32_t w = pack_bf16x2(val, val - bf16lo(pack_bf16x2(val, 0.f)));
-    hi_out[idx] = (uint16_t)(w & 0xffffu);
-    lo_out[idx] = (uint16_t)(w >> 16);
-  }
-  if (tid < kHeadDim) zout[h * kHeadDim + tid] = z[tid];
+  for (; c < nchunks; ++c) s += (double)ph[(int64_t)c * kStateFloats];
+  state[(int64_t)h * kStateFloats + e] = (float)s;
 }
 
-__global__ __launch_bounds__(256) void linear_apply_kernel(
+// phi of 8 bf16 channels (one 16-byte piece) -> hi/lo operands, and the
+// partial denominator sum_j phi_j z_j
+__device__ __forceinline__ void phi_split(u32x4 w, const float* zr, bf16x8& hi8, bf16x8& lo8,
+                                          float& den) {
+  float f[8];
+  f[0] = phi(bf16lo(w.x));
+  f[1] = phi(bf16hi(w.x));
+  f[2] = phi(bf16lo(w.y));
+  f[3] = phi(bf16hi(w.y));
+  f[4] = phi(bf16lo(w.z));
+  f[5] = phi(bf16hi(w.z));
+  f[6] = phi(bf16lo(w.w));
+  f[7] = phi(bf16hi(w.w));
+#pragma unroll
+  for (int j = 0; j < 8; ++j) den = __builtin_fmaf(f[j], zr[j], den);
+  u32x4 hi, lo;
+  split8(f, hi, lo);
+  hi8 = as_bf16x8(hi);
+  lo8 = as_bf16x8(lo);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void linear_apply_kernel(
     const uint16_t* __restrict__ q, int64_t nq, int64_t qst, int64_t qsh,
-    const uint16_t* __restrict__ sop, const float* __restrict__ zin, int64_t tok_per_block,
-    void* __restrict__ o, int64_t ost, int64_t osh, int32_t o_f32) {
+    const float* __restrict__ state, const float* __restrict__ aff_a,
+    const float* __restrict__ aff_b, int64_t tok_per_block, void* __restrict__ o, int64_t ost,
+    int64_t osh, int32_t o_f32) {
+  // per wave: one 32-token x 128-byte tile, row-swizzled; queries come in and
+  // bf16 outputs go out through it so that global accesses are whole rows
+  __shared__ __attribute__((aligned(16))) uint8_t tile[4][32 * 128];
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int h = blockIdx.y;
   const int hh = lane >> 5, qi = lane & 31;
+  uint8_t* tw = tile[wave];
 
-  bf16x8 ahi[2][4], alo[2][4];
-  const uint16_t* sh = sop + (int64_t)h * 2 * 4096;
+  // A operands of O^T = S''^T phi(Q)^T, shared by the workgroup's waves in
+  // LDS: for part p (0 hi, 1 lo), e-block eb, k-step s and lane l, the bf16
+  // values S''[16s + 8(l/32) + j][32eb + l%32], j = 0..7
+  __shared__ u32x4 aops[2][2][4][kWave];
+  const float* st = state + (int64_t)h * kStateFloats;
+  const float* z = st + kHeadDim * kHeadDim;
+  {
+    const int eb = wave >> 1, s0 = 2 * (wave & 1);  // each wave builds two k-steps
+    const int e = 32 * eb + qi;
+    const float a = aff_a ? aff_a[h * kHeadDim + e] : 1.f;
+    const float b = aff_b ? aff_b[h * kHeadDim + e] : 0.f;
 #pragma unroll
-  for (int eb = 0; eb < 2; ++eb)
+    for (int s = s0; s < s0 + 2; ++s) {
+      float f[8];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int off = ((eb * 4 + s) * 64 + lane) * 8;
-      ahi[eb][s] = as_bf16x8(*(const u32x4*)(sh + off));
-      alo[eb][s] = as_bf16x8(*(const u32x4*)(sh + 4096 + off));
+      for (int j = 0; j < 8; ++j) {
+        const int c = 16 * s + 8 * hh + j;
+        f[j] = a * st[c * kHeadDim + e] + z[c] * b;
+      }
+      split8(f, aops[0][eb][s][lane], aops[1][eb][s][lane]);
     }
-  float zr[4][8];
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) zr[s][j] = zin[h * kHeadDim + 16 * s + 8 * hh + j];
+  }
+  __shared__ __attribute__((aligned(16))) float zs[kHeadDim];
+  if (tid < kHeadDim) zs[tid] = z[tid];
+  __syncthreads();
 
   const int64_t b0 = (int64_t)blockIdx.x * tok_per_block;
   const int64_t b1 = std::min(nq, b0 + tok_per_block);
+  const uint16_t* qh = q + (int64_t)h * qsh;
+  const int lrow = lane >> 3, lch = lane & 7;  // row-major view: 8 rows per access
+  // coalesced loads of a 32-token step: lane reads chunk lch of rows lrow + 8i;
+  // the next step's loads are in flight while one step is used
+  u32x4 qn[4];
+  auto load_q = [&](int64_t base) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t n = base + 8 * i + lrow;
+      qn[i] = u32x4{0u, 0u, 0u, 0u};
+      if (n < b1) qn[i] = *(const u32x4*)(qh + n * qst + 8 * lch);
+    }
+  };
+  load_q(b0 + 32 * wave);
   for (int64_t base = b0 + 32 * wave; base < b1; base += 128) {
+    // queries -> LDS (row-major), then the operand layout: row qi, chunk 2s + hh
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(u32x4*)(tw + swz(8 * i + lrow, lch)) = qn[i];
+    load_q(base + 128);
+    u32x4 qc[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qc[s] = *(const u32x4*)(tw + swz(qi, 2 * s + hh));
     const int64_t n = base + qi;
-    const bool ok = n < b1;
-    const uint16_t* qp = q + (int64_t)h * qsh + n * qst + 8 * hh;
     bf16x8 bhi[4], blo[4];
     float den = 0.f;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (ok) w = *(const u32x4*)(qp + 16 * s);
-      float f[8];
-      f[0] = phi(bf16lo(w.x));
-      f[1] = phi(bf16hi(w.x));
-      f[2] = phi(bf16lo(w.y));
-      f[3] = phi(bf16hi(w.y));
-      f[4] = phi(bf16lo(w.z));
-      f[5] = phi(bf16hi(w.z));
-      f[6] = phi(bf16lo(w.w));
-      f[7] = phi(bf16hi(w.w));
-#pragma unroll
-      for (int j = 0; j < 8; ++j) den = __builtin_fmaf(f[j], zr[s][j], den);
-      u32x4 hi, lo;
-      split8(f, hi, lo);
-      bhi[s] = as_bf16x8(hi);
-      blo[s] = as_bf16x8(lo);
+      const f32x4 z0 = *(const f32x4*)(zs + 16 * s + 8 * hh);
+      const f32x4 z1 = *(const f32x4*)(zs + 16 * s + 8 * hh + 4);
+      const float zr[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+      phi_split(qc[s], zr, bhi[s], blo[s], den);
     }
     den += __shfl_xor(den, 32, kWave);
     const float inv = 1.0f / den;
-    f32x16 acc[2];
+    // re-read the operands from LDS every step rather than keeping all 16 in
+    // registers (the compiler would otherwise hoist the loop-invariant reads)
+    asm volatile("" ::: "memory");
+    // one e-block at a time: acc[4g + r] = O^T[32eb + 8g + 4hh + r][n]
 #pragma unroll
     for (int eb = 0; eb < 2; ++eb) {
+      f32x16 acc;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[eb][i] = 0.f;
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        acc[eb] = mfma32(ahi[eb][s], bhi[s], acc[eb]);
-        acc[eb] = mfma32(ahi[eb][s], blo[s], acc[eb]);
-        acc[eb] = mfma32(alo[eb][s], bhi[s], acc[eb]);
+        const bf16x8 ahi = as_bf16x8(aops[0][eb][s][lane]);
+        const bf16x8 alo = as_bf16x8(aops[1][eb][s][lane]);
+        acc = mfma32(ahi, bhi[s], acc);
+        acc = mfma32(ahi, blo[s], acc);
+        acc = mfma32(alo, bhi[s], acc);
+      }
+      if (o_f32) {
+        if (n < b1) {
+          float* op = (float*)o + (int64_t)h * osh + n * ost + 32 * eb + 4 * hh;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            f32x4 w = {acc[4 * g] * inv, acc[4 * g + 1] * inv, acc[4 * g + 2] * inv,
+                       acc[4 * g + 3] * inv};
+            *(f32x4*)(op + 8 * g) = w;
+          }
+        }
+      } else {
+        // bf16 rows through the tile: 8 bytes of row qi at channel 32eb + 8g + 4hh
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2 w = {pack_bf16x2(acc[4 * g] * inv, acc[4 * g + 1] * inv),
+                     pack_bf16x2(acc[4 * g + 2] * inv, acc[4 * g + 3] * inv)};
+          *(u32x2*)(tw + swz(qi, 4 * eb + g) + 8 * hh) = w;
+        }
       }
     }
-    if (!ok) continue;
-    // acc[eb][4g + r] = O^T[32eb + 8g + 4hh + r][n]
-    if (o_f32) {
-      float* op = (float*)o + (int64_t)h * osh + n * ost + 4 * hh;
+    if (!o_f32) {
+      uint16_t* oh = (uint16_t*)o + (int64_t)h * osh;
 #pragma unroll
-      for (int eb = 0; eb < 2; ++eb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 w = {acc[eb][4 * g] * inv, acc[eb][4 * g + 1] * inv, acc[eb][4 * g + 2] * inv,
-                     acc[eb][4 * g + 3] * inv};
-          *(f32x4*)(op + 32 * eb + 8 * g) = w;
-        }
-    } else {
-      uint16_t* op = (uint16_t*)o + (int64_t)h * osh + n * ost + 4 * hh;
-#pragma unroll
-      for (int eb = 0; eb < 2; ++eb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          u32x2 w = {pack_bf16x2(acc[eb][4 * g] * inv, acc[eb][4 * g + 1] * inv),
-                     pack_bf16x2(acc[eb][4 * g + 2] * inv, acc[eb][4 * g + 3] * inv)};
-          *(u32x2*)(op + 32 * eb + 8 * g) = w;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int r = 8 * i + lrow;
+        const u32x4 w = *(const u32x4*)(tw + swz(r, lch));
+        if (base + r < b1) *(u32x4*)(oh + (base + r) * ost + 8 * lch) = w;
+      }
     }
   }
 }
@@ -311,9 +371,8 @@ size_t linear_workspace_bytes(int64_t n_kv, int32_t heads) {
   int64_t chunk_tok;
   state_chunking(n_kv, heads, nchunks, chunk_tok);
   const size_t partial = (size_t)heads * nchunks * kStateFloats * sizeof(float);
-  const size_t sop = (size_t)heads * 2 * 4096 * sizeof(uint16_t);
-  const size_t z = (size_t)heads * kHeadDim * sizeof(float);
-  return partial + sop + z;
+  const size_t state = (size_t)heads * kStateFloats * sizeof(float);
+  return partial + state;
 }
 
 hipError_t launch_linear(const uint16_t* q, int64_t nq, int64_t qst, int64_t qsh,
@@ -326,20 +385,21 @@ hipError_t launch_linear(const uint16_t* q, int64_t nq, int64_t qst, int64_t qsh
   int64_t chunk_tok;
   state_chunking(nk, heads, nchunks, chunk_tok);
   float* partial = (float*)ws;
-  uint16_t* sop = (uint16_t*)(partial + (size_t)heads * nchunks * kStateFloats);
-  float* z = (float*)(sop + (size_t)heads * 2 * 4096);
+  float* state = partial + (size_t)heads * nchunks * kStateFloats;
   hipLaunchKernelGGL(linear_state_kernel, dim3(nchunks, heads), dim3(256), 0, s, k, v, nk, kst,
                      ksh, chunk_tok, nchunks, partial);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(linear_reduce_kernel, dim3(heads), dim3(256), 0, s, partial, nchunks,
-                     aff_scale, aff_bias, sop, z);
+  hipLaunchKernelGGL(linear_reduce_kernel, dim3((kStateFloats + 255) / 256, heads), dim3(256), 0,
+                     s, partial, nchunks, state);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int64_t per_block = 512;
+  // about 2 workgroups of 4 waves per CU per head group; each wave loops over
+  // 32-query steps with the next step's loads in flight
+  const int64_t per_block = std::max<int64_t>(512, ((nq * heads + 4095) / 4096 + 127) / 128 * 128);
   const int64_t nblocks = (nq + per_block - 1) / per_block;
   hipLaunchKernelGGL(linear_apply_kernel, dim3((unsigned)nblocks, heads), dim3(256), 0, s, q, nq,
-                     qst, qsh, sop, z, per_block, o, ost, osh, o_f32 ? 1 : 0);
+                     qst, qsh, state, aff_scale, aff_bias, per_block, o, ost, osh, o_f32 ? 1 : 0);
   return hipGetLastError();
 }
 
