@@ -21,8 +21,10 @@ stage each) report the same fields for that stage.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -83,6 +85,26 @@ def sparse_flops(n_q, n_kv, q_tile, k_tile, top_k, sel):
     selected = 4.0 * d * float(np.sum(q_sizes[None, :] * kept_tokens))
     landmark = 4.0 * d * float(heads * np.sum(q_sizes) * (t_k - top_k))
     return selected, landmark
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per sparse launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, copy-scaled), or None when the summary does not
+    cover this workload or the attention kernel source has changed since."""
+    if workload != "stack24-512v":
+        return None
+    root = os.path.dirname(os.path.abspath(__file__))
+    summary = os.path.join(root, "profiles", "tile_sparse_kernel_stack24-512v_hbm_bytes.md")
+    source = os.path.join(root, "linear_hybrid_attention_zebra_amd", "csrc", "sparse_attn.hip")
+    try:
+        text = open(summary).read()
+        digest = hashlib.sha256(open(source, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    vals = dict(re.findall(r"^(\w+): (\S+)$", text, re.M))
+    if vals.get("source_sha256") != digest:
+        return None
+    return float(vals["fetch_bytes_per_launch"]) + float(vals["write_bytes_per_launch"])
 
 
 # ----------------------------------------------------------------------------
@@ -301,7 +323,8 @@ def main():
         achieved = res["selected_flops"] / sec / 1e12
         out["roofline"] = {"kernel": "tile_sparse_kernel", "bound": "mfma",
                            "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                           "frac": achieved / PEAK_BF16_TFLOPS,
+                           "traffic": recorded_traffic(w.name),
                            "achieved_with_landmarks": (res["selected_flops"]
                                                        + res["landmark_flops"]) / sec / 1e12,
                            "flops_per_launch": res["selected_flops"]}

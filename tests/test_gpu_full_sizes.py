@@ -1,0 +1,94 @@
+"""GPU parity at the benchmark workloads' full sizes, on sampled outputs.
+
+Each test runs one whole stage exactly as bench.py launches it (same buffers,
+tiles, top_k and scale) on the seeded full-size inputs, then checks a seeded
+sample of (head, query tile) rows against the CPU oracle one by one:
+  * the selection of each sampled row against the oracle's float64 pooled
+    scores of the whole head (bit-exact outside near ties);
+  * the attention output of each sampled query tile against the oracle run on
+    that row's GPU selection (max-abs 2e-2, rel-Frobenius 5e-3);
+  * linear stages: sampled query outputs against the oracle's state over all
+    keys with the GPU's fitted (a, b); the fit against the oracle on the GPU's
+    own (x, y); the dense calibration target on a sample of its queries.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.zebra_oracle as zo
+import linear_hybrid_attention_zebra_amd as zb
+from linear_hybrid_attention_zebra_amd import stage as stage_mod
+from linear_hybrid_attention_zebra_amd import synth
+from parity_util import assert_close, check_selection_row, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SCALE = 0.125
+ROWS = 6  # sampled (head, query tile) rows per sparse stage
+
+
+def _head(t, h):
+    return t[h].to("cpu", torch.float64).numpy()
+
+
+SPARSE_STAGES = [("sparse-16v", 0), ("stack24-512v", 9), ("sparse-1024v", 0)]
+
+
+@pytest.mark.parametrize("name,stage", SPARSE_STAGES, ids=[f"{n}:{s}" for n, s in SPARSE_STAGES])
+def test_full_size_sparse_stage_sampled(name, stage):
+    w = synth.WORKLOADS[name]
+    print(f"[case] full-size sparse {name} stage {stage}: N={w.n_tokens} H={w.heads} "
+          f"tiles {w.q_tile}x{w.k_tile} top_k={w.k}", flush=True)
+    q, k, v = synth.stage_inputs(w, stage, DEV)
+    bufs = stage_mod.SparseBuffers.allocate(w.heads, w.n_tokens, w.n_tokens, w.q_tile, w.k_tile,
+                                            w.k, DEV)
+    stage_mod.sparse_stage(q, k, v, w.q_tile, w.k_tile, w.k, SCALE, bufs)
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(w.heads, w.t_q, ROWS, 100 + stage)
+    swaps = 0
+    for h in sorted(set(rows[:, 0].tolist())):
+        qh, kh, vh = _head(q, h), _head(k, h), _head(v, h)
+        kbar = zo.pool_tiles(kh, w.k_tile)
+        for i in rows[rows[:, 0] == h][:, 1]:
+            s0, e0 = i * w.q_tile, min(w.n_tokens, (i + 1) * w.q_tile)
+            qbar_i = qh[s0:e0].mean(axis=0)
+            scores = zo.block_scores(qbar_i[None], kbar)[0]
+            gsel = bufs.sel[h, i].cpu().numpy()
+            swaps += check_selection_row(gsel, scores, w.k)
+            ref = zo.tile_sparse_attention_tile(qh[s0:e0], kh, vh, w.k_tile, gsel, SCALE)
+            assert_close(bufs.out[h, s0:e0], ref, f"{name} stage {stage} head {h} tile {i}")
+    print(f"[parity] near-tie swaps {swaps} of {len(rows)} sampled rows", flush=True)
+
+
+LINEAR_STAGES = [("linear-128v", 0), ("stack24-512v", 0)]
+
+
+@pytest.mark.parametrize("name,stage", LINEAR_STAGES, ids=[f"{n}:{s}" for n, s in LINEAR_STAGES])
+def test_full_size_linear_stage_sampled(name, stage):
+    w = synth.WORKLOADS[name]
+    n = w.n_tokens
+    print(f"[case] full-size linear {name} stage {stage}: N={n} H={w.heads}", flush=True)
+    q, k, v = synth.stage_inputs(w, stage, DEV)
+    idx = torch.from_numpy(synth.fit_sample_indices(n, w.fit_samples, w.stage_seed(stage))).to(DEV)
+    cal = stage_mod.calibrate_linear(q, k, v, idx, SCALE, w.k_tile)
+    out = zb.zebra_linear_attn(q, k, v, cal.aff_scale, cal.aff_bias)
+    torch.cuda.synchronize()
+    a, b = to_f64(cal.aff_scale), to_f64(cal.aff_bias)
+    x, y = to_f64(cal.x), to_f64(cal.y)
+    rng = np.random.default_rng(200 + stage)
+    for h in rng.choice(w.heads, size=2, replace=False):
+        qh, kh, vh = _head(q, h), _head(k, h), _head(v, h)
+        # the fit on the GPU's own (x, y)
+        a_ref, b_ref, _ = zo.fit_affine(x[h], y[h])
+        np.testing.assert_allclose(a[h], a_ref, rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(b[h], b_ref, rtol=1e-5, atol=1e-7)
+        # the linear output at sampled queries, with the GPU's (a, b)
+        tok = np.sort(rng.choice(n, size=512, replace=False))
+        ref, _, _ = zo.linear_attention(qh[tok], kh, vh, a[h], b[h])
+        assert_close(out[h, torch.from_numpy(tok).to(DEV)], ref, f"{name} linear head {h}")
+        # the unfitted linear output and the dense target at a few fit samples
+        pick = np.sort(rng.choice(idx.numel(), size=64, replace=False))
+        qs = qh[idx.cpu().numpy()[pick]]
+        assert_close(x[h, pick], zo.linear_attention(qs, kh, vh)[0], f"{name} x head {h}")
+        assert_close(y[h, pick], zo.dense_attention(qs, kh, vh, SCALE), f"{name} y head {h}")
