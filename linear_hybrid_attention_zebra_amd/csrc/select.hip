@@ -7,254 +7,328 @@
 // (s_ij descending, j ascending) and emits them in ascending order.
 //
 // Two kernels:
-//  1. score_kernel: a K=64 float32 GEMM, 64x64 output tile per workgroup,
-//     operands staged in LDS, sequential FMA over the 64 channels (the same
-//     summation order for every element).
-//  2. select_kernel: one workgroup per (head, query tile). The row's scores
-//     sit in registers (contiguous index range per thread). The k-th largest
-//     value tau is found exactly: min/max, a 2048-bin histogram on the value
-//     range (a monotone binning, so equal scores share a bin), the bin where
-//     the count from the top crosses k, then an exact rank among that bin's
-//     members. Kept tiles are {s > tau} plus the lowest-indexed ties at tau,
-//     written in index order through a block-wide scan. No sort, no float
-//     atomics; the result does not depend on scheduling.
+//  1. score_kernel: a K=64 float32 GEMM, 128x128 output tile per workgroup
+//     and 8x8 per thread, operands staged transposed in LDS, sequential FMA
+//     over the 64 channels (the same summation order for every element).
+//  2. select_kernel: one wave per (head, query tile), no workgroup barriers.
+//     The k-th largest value tau is found exactly: min/max, a 2048-bin
+//     histogram on the value range (a monotone binning, so equal scores share
+//     a bin), the bin where the count from the top crosses k, then an exact
+//     rank among that bin's members (bisection on order-preserving keys when
+//     the bin is crowded). Kept tiles are {s > tau} plus the lowest-indexed
+//     ties at tau, written in index order through wave prefix sums. No sort,
+//     no float atomics; the result does not depend on scheduling.
 #include "common.h"
 
 namespace zebra {
 
 namespace {
 
-constexpr int kScoreTile = 64;
+constexpr int kScoreTile = 128;  // output tile edge of score_kernel
 
+// One 128x128 tile of s = qbar kbar^T per workgroup; thread (ty, tx) owns rows
+// 8ty .. 8ty+7 and columns 4tx .. 4tx+3, 64+4tx .. 64+4tx+3. Both operand
+// tiles sit transposed in LDS ([channel][row]), so each channel step is four
+// 16-byte reads and 64 FMAs per thread; every output element is the same
+// sequential FMA chain over the 64 channels.
 __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qbar,
                                                     const float* __restrict__ kbar, int32_t tq,
                                                     int32_t tk, float* __restrict__ scores) {
-  __shared__ float qs[kScoreTile][kHeadDim + 1];
-  __shared__ float ks[kScoreTile][kHeadDim + 1];
+  constexpr int T = kScoreTile, P = T + 4;  // padded rows of the transposed tiles
+  __shared__ __attribute__((aligned(16))) float qs[kHeadDim][P];
+  __shared__ __attribute__((aligned(16))) float ks[kHeadDim][P];
   const int h = blockIdx.z;
-  const int i0 = blockIdx.y * kScoreTile;
-  const int j0 = blockIdx.x * kScoreTile;
+  const int i0 = blockIdx.y * T;
+  const int j0 = blockIdx.x * T;
+  const int tid = threadIdx.x;
   const float* qh = qbar + (int64_t)h * tq * kHeadDim;
   const float* kh = kbar + (int64_t)h * tk * kHeadDim;
-  for (int e = threadIdx.x; e < kScoreTile * kHeadDim; e += 256) {
-    const int r = e / kHeadDim, c = e % kHeadDim;
-    qs[r][c] = (i0 + r < tq) ? qh[(int64_t)(i0 + r) * kHeadDim + c] : 0.f;
-    ks[r][c] = (j0 + r < tk) ? kh[(int64_t)(j0 + r) * kHeadDim + c] : 0.f;
+  // 128 rows x 16 float4 per operand: 8 float4 of each per thread
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int e = tid + 256 * u;
+    const int r = e >> 4, c4 = e & 15;
+    f32x4 qv = {0.f, 0.f, 0.f, 0.f}, kv = {0.f, 0.f, 0.f, 0.f};
+    if (i0 + r < tq) qv = *(const f32x4*)(qh + (int64_t)(i0 + r) * kHeadDim + 4 * c4);
+    if (j0 + r < tk) kv = *(const f32x4*)(kh + (int64_t)(j0 + r) * kHeadDim + 4 * c4);
+    qs[4 * c4][r] = qv.x;
+    qs[4 * c4 + 1][r] = qv.y;
+    qs[4 * c4 + 2][r] = qv.z;
+    qs[4 * c4 + 3][r] = qv.w;
+    ks[4 * c4][r] = kv.x;
+    ks[4 * c4 + 1][r] = kv.y;
+    ks[4 * c4 + 2][r] = kv.z;
+    ks[4 * c4 + 3][r] = kv.w;
   }
   __syncthreads();
-  const int tx = threadIdx.x % 16;  // columns tx + 16 b
-  const int ty = threadIdx.x / 16;  // rows 4 ty + a
-  float acc[4][4];
+  const int tx = tid & 15, ty = tid >> 4;
+  float acc[8][8];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
+    for (int b = 0; b < 8; ++b) acc[a][b] = 0.f;
+#pragma unroll 4
   for (int c = 0; c < kHeadDim; ++c) {
-    float qv[4], kv[4];
+    const f32x4 q0 = *(const f32x4*)&qs[c][8 * ty];
+    const f32x4 q1 = *(const f32x4*)&qs[c][8 * ty + 4];
+    const f32x4 k0 = *(const f32x4*)&ks[c][4 * tx];
+    const f32x4 k1 = *(const f32x4*)&ks[c][64 + 4 * tx];
+    const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    const float kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
 #pragma unroll
-    for (int a = 0; a < 4; ++a) qv[a] = qs[4 * ty + a][c];
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) kv[b] = ks[tx + 16 * b][c];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_fmaf(qv[a], kv[b], acc[a][b]);
+      for (int b = 0; b < 8; ++b) acc[a][b] = __builtin_fmaf(qv[a], kv[b], acc[a][b]);
   }
   float* out = scores + (int64_t)h * tq * tk;
+  const bool vec = (tk & 3) == 0;
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int i = i0 + 4 * ty + a;
+  for (int a = 0; a < 8; ++a) {
+    const int i = i0 + 8 * ty + a;
     if (i >= tq) continue;
+    float* orow = out + (int64_t)i * tk;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int j = j0 + tx + 16 * b;
-      if (j < tk) out[(int64_t)i * tk + j] = acc[a][b];
+    for (int half = 0; half < 2; ++half) {
+      const int j = j0 + 64 * half + 4 * tx;
+      const float* src = &acc[a][4 * half];
+      if (vec && j + 3 < tk) {
+        *(f32x4*)(orow + j) = f32x4{src[0], src[1], src[2], src[3]};
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          if (j + b < tk) orow[j + b] = src[b];
+      }
     }
   }
 }
 
 constexpr int kBins = 2048;
+constexpr int kRowsPerGroup = 4;  // one wave per row
+constexpr int kMaxCand = 256;     // members of the threshold bin ranked exactly
 
-// Inclusive prefix sum over the block (NT threads), integer.
-template <int NT>
-__device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, uint32_t* wave_tot) {
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+__device__ __forceinline__ float wave_min(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Inclusive prefix sum over the wave's 64 lanes.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
     const uint32_t u = __shfl_up(v, o, kWave);
     if (lane >= o) v += u;
   }
-  if (lane == kWave - 1) wave_tot[wave] = v;
-  __syncthreads();
-  uint32_t before = 0;
-  for (int w = 0; w < wave; ++w) before += wave_tot[w];
-  __syncthreads();
-  return v + before;
+  return v;
 }
 
-template <int NT>
-__device__ __forceinline__ float block_reduce_max(float v, float* tmp) {
-  v = wave_max(v);
-  if (threadIdx.x % kWave == 0) tmp[threadIdx.x / kWave] = v;
-  __syncthreads();
-  float r = tmp[0];
-  for (int w = 1; w < NT / kWave; ++w) r = fmaxf(r, tmp[w]);
-  __syncthreads();
-  return r;
-}
-
-template <int NT>
-__device__ __forceinline__ uint32_t block_reduce_sum(uint32_t v, uint32_t* tmp) {
-  v = (uint32_t)wave_sum_int((int)v);
-  if (threadIdx.x % kWave == 0) tmp[threadIdx.x / kWave] = v;
-  __syncthreads();
-  uint32_t r = 0;
-  for (int w = 0; w < NT / kWave; ++w) r += tmp[w];
-  __syncthreads();
-  return r;
-}
-
-template <int NT, int MAXL>
-__global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ scores, int32_t tk,
-                                                    int32_t top_k, int32_t* __restrict__ sel) {
-  __shared__ uint32_t hist[kBins];
-  __shared__ float cand[NT];
-  __shared__ uint32_t red_u[NT / kWave];
-  __shared__ float red_f[NT / kWave];
-  __shared__ uint32_t s_bin, s_above, s_ncand;
-  __shared__ float s_tau;
-
-  const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  const float* srow = scores + row * tk;
-  const int L = (tk + NT - 1) / NT;
-  const int beg = tid * L;
-
-  float v[MAXL];
+// Row elements in chunks of 256: lane l holds elements 256c + 4l .. +3 (index
+// order = chunk, lane, element), 16-byte loads when the row allows them.
+struct RowReader {
+  const float* row;
+  int32_t n;
+  bool vec;
+  __device__ __forceinline__ void load(int c, int lane, float (&x)[4]) const {
+    const int i0 = 256 * c + 4 * lane;
+    if (vec && i0 + 3 < n) {
+      const f32x4 w = *(const f32x4*)(row + i0);
+      x[0] = w.x;
+      x[1] = w.y;
+      x[2] = w.z;
+      x[3] = w.w;
+    } else {
 #pragma unroll
-  for (int i = 0; i < MAXL; ++i) {
-    const int idx = beg + i;
-    v[i] = (i < L && idx < tk) ? srow[idx] : 0.f;
+      for (int u = 0; u < 4; ++u) x[u] = i0 + u < n ? row[i0 + u] : 0.f;
+    }
   }
-  auto valid = [&](int i) { return i < L && beg + i < tk; };
+};
+
+// One wave per (head, query tile) row; no workgroup barriers. Passes over the
+// row (re-read from L2): value range; a 2048-bin monotone histogram in LDS;
+// the bin where the count from the top reaches top_k; the exact threshold tau
+// among that bin's members (or by bisection on order-preserving keys when the
+// bin holds more than kMaxCand values, e.g. many equal scores); then an
+// ordered compaction of {s > tau} plus the lowest-indexed ties at tau.
+__global__ __launch_bounds__(kRowsPerGroup * kWave) void select_kernel(
+    const float* __restrict__ scores, int64_t n_rows, int32_t tk, int32_t top_k,
+    int32_t* __restrict__ sel) {
+  __shared__ uint32_t hist_all[kRowsPerGroup][kBins];
+  __shared__ float cand_all[kRowsPerGroup][kMaxCand];
+  __shared__ uint32_t ncand_all[kRowsPerGroup];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerGroup + wave;
+  if (row >= n_rows) return;  // whole wave; no barriers follow
+  uint32_t* hist = hist_all[wave];
+  float* cand = cand_all[wave];
+  const RowReader rd{scores + row * tk, tk, (tk & 3) == 0};
+  const int nchunks = (tk + 255) / 256;
+  auto valid = [&](int c, int u) { return 256 * c + 4 * lane + u < tk; };
 
   // 1. value range
-  float lmax = -INFINITY, lneg = -INFINITY;  // lneg = max of -v = -min
+  float lmax = -INFINITY, lmin = INFINITY;
+  #pragma unroll 4
+  for (int c = 0; c < nchunks; ++c) {
+    float x[4];
+    rd.load(c, lane, x);
 #pragma unroll
-  for (int i = 0; i < MAXL; ++i)
-    if (valid(i)) {
-      lmax = fmaxf(lmax, v[i]);
-      lneg = fmaxf(lneg, -v[i]);
-    }
-  const float vmax = block_reduce_max<NT>(lmax, red_f);
-  const float vmin = -block_reduce_max<NT>(lneg, red_f);
-
-  // 2. histogram over [vmin, vmax]; bin() is monotone non-decreasing in v
-  for (int b = tid; b < kBins; b += NT) hist[b] = 0;
-  if (tid == 0) {
-    s_bin = 0;
-    s_tau = vmax;
+    for (int u = 0; u < 4; ++u)
+      if (valid(c, u)) {
+        lmax = fmaxf(lmax, x[u]);
+        lmin = fminf(lmin, x[u]);
+      }
   }
-  __syncthreads();
+  const float vmax = wave_max(lmax), vmin = wave_min(lmin);
+
+  // 2. histogram; bin() is monotone non-decreasing in the value
+  for (int b = lane; b < kBins; b += kWave) hist[b] = 0u;
   const float inv = (vmax > vmin) ? (float)kBins / (vmax - vmin) : 0.f;
   auto bin_of = [&](float x) { return min(kBins - 1, (int)((x - vmin) * inv)); };
+  #pragma unroll 4
+  for (int c = 0; c < nchunks; ++c) {
+    float x[4];
+    rd.load(c, lane, x);
 #pragma unroll
-  for (int i = 0; i < MAXL; ++i)
-    if (valid(i)) atomicAdd(&hist[bin_of(v[i])], 1u);
-  __syncthreads();
-
-  // 3. the bin in which the count from the top reaches top_k
-  constexpr int BPT = kBins / NT;
-  uint32_t mine = 0;
-#pragma unroll
-  for (int b = 0; b < BPT; ++b) mine += hist[tid * BPT + b];
-  const uint32_t incl = block_inclusive_scan<NT>(mine, red_u);
-  if (tid == NT - 1) s_above = incl;  // total count
-  __syncthreads();
-  const uint32_t all = s_above;
-  __syncthreads();
-  uint32_t above = all - incl;  // count in bins owned by higher threads
-  for (int b = BPT - 1; b >= 0; --b) {
-    const uint32_t hb = hist[tid * BPT + b];
-    if (above < (uint32_t)top_k && (uint32_t)top_k <= above + hb) {
-      s_bin = tid * BPT + b;
-      s_above = above;
-    }
-    above += hb;
+    for (int u = 0; u < 4; ++u)
+      if (valid(c, u)) atomicAdd(&hist[bin_of(x[u])], 1u);
   }
-  __syncthreads();
-  const int bstar = (int)s_bin;
-  const uint32_t need_in_bin = (uint32_t)top_k - s_above;  // 1 .. hist[bstar]
+
+  // 3. the bin where the count from the top reaches top_k: lane l owns bins
+  // 32(63-l) .. 32(63-l)+31, so lane order is descending value order
+  constexpr int BPL = kBins / kWave;
+  const int b0 = BPL * (kWave - 1 - lane);
+  uint32_t mine = 0;
+#pragma unroll 8
+  for (int b = 0; b < BPL; ++b) mine += hist[b0 + b];
+  const uint32_t incl = wave_incl_scan(mine, lane);  // count in bins >= b0
+  uint32_t above = incl - mine;                      // count in bins above this lane's
+  int bstar = -1;
+  uint32_t above_star = 0;
+  if (above < (uint32_t)top_k && (uint32_t)top_k <= incl) {
+    for (int b = BPL - 1; b >= 0; --b) {
+      const uint32_t hb = hist[b0 + b];
+      if (above < (uint32_t)top_k && (uint32_t)top_k <= above + hb) {
+        bstar = b0 + b;
+        above_star = above;
+        break;
+      }
+      above += hb;
+    }
+  }
+  // exactly one lane found it; broadcast
+  const uint64_t who = __ballot(bstar >= 0);
+  const int src = __ffsll((unsigned long long)who) - 1;
+  bstar = __shfl(bstar, src, kWave);
+  above_star = __shfl(above_star, src, kWave);
+  const uint32_t need_in_bin = (uint32_t)top_k - above_star;  // 1 .. hist[bstar]
   const uint32_t n_in_bin = hist[bstar];
 
-  // 4. tau = the need_in_bin-th largest value among the bin's members
-  if (n_in_bin <= (uint32_t)NT) {
-    if (tid == 0) s_ncand = 0;
-    __syncthreads();
+  // 4. tau = the need_in_bin-th largest value of the bin
+  float tau;
+  if (n_in_bin <= (uint32_t)kMaxCand) {
+    if (lane == 0) ncand_all[wave] = 0u;
+#pragma unroll 4
+    for (int c = 0; c < nchunks; ++c) {
+      float x[4];
+      rd.load(c, lane, x);
 #pragma unroll
-    for (int i = 0; i < MAXL; ++i)
-      if (valid(i) && bin_of(v[i]) == bstar) {
-        const uint32_t slot = atomicAdd(&s_ncand, 1u);
-        if (slot < (uint32_t)NT) cand[slot] = v[i];
-      }
-    __syncthreads();
-    if (tid < (int)n_in_bin) {
-      const float c = cand[tid];
-      uint32_t gt = 0, ge = 0;
-      for (uint32_t u = 0; u < n_in_bin; ++u) {
-        gt += cand[u] > c;
-        ge += cand[u] >= c;
-      }
-      if (gt < need_in_bin && need_in_bin <= ge) s_tau = c;  // every writer stores the same value
+      for (int u = 0; u < 4; ++u)
+        if (valid(c, u) && bin_of(x[u]) == bstar) {
+          const uint32_t slot = atomicAdd(&ncand_all[wave], 1u);
+          cand[slot] = x[u];
+        }
     }
-    __syncthreads();
+    float t = -INFINITY;
+    bool found = false;
+    for (uint32_t i = lane; i < n_in_bin; i += kWave) {
+      const float ci = cand[i];
+      uint32_t gt = 0, ge = 0;
+      for (uint32_t j = 0; j < n_in_bin; ++j) {
+        gt += cand[j] > ci;
+        ge += cand[j] >= ci;
+      }
+      if (gt < need_in_bin && need_in_bin <= ge) {
+        t = ci;  // every lane that finds it holds the same value
+        found = true;
+      }
+    }
+    const uint64_t w2 = __ballot(found);
+    tau = __shfl(t, __ffsll((unsigned long long)w2) - 1, kWave);
   } else {
-    // Rare: a bin holds more than NT scores (e.g. many equal values). Find tau
-    // by bisection on order-preserving keys over the whole row.
+    // many equal or nearly equal scores: bisection on order-preserving keys
     uint32_t lo_key = 0;
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t trial = lo_key | (1u << bit);
       uint32_t cnt = 0;
+      for (int c = 0; c < nchunks; ++c) {
+        float x[4];
+        rd.load(c, lane, x);
 #pragma unroll
-      for (int i = 0; i < MAXL; ++i)
-        if (valid(i)) cnt += float_key(v[i]) >= trial;
-      if (block_reduce_sum<NT>(cnt, red_u) >= (uint32_t)top_k) lo_key = trial;
+        for (int u = 0; u < 4; ++u)
+          if (valid(c, u)) cnt += float_key(x[u]) >= trial;
+      }
+      if ((uint32_t)wave_sum_int((int)cnt) >= (uint32_t)top_k) lo_key = trial;
     }
-    if (tid == 0) {
-      const uint32_t u = (lo_key & 0x80000000u) ? (lo_key & 0x7fffffffu) : ~lo_key;
-      s_tau = __uint_as_float(u);
-    }
-    __syncthreads();
+    const uint32_t u = (lo_key & 0x80000000u) ? (lo_key & 0x7fffffffu) : ~lo_key;
+    tau = __uint_as_float(u);
   }
-  const float tau = s_tau;
 
-  // 5. ordered compaction: {s > tau} and the first (top_k - #{s > tau}) ties
-  uint32_t gt = 0, eq = 0;
+  // 5. ordered compaction: {s > tau}, then ties at tau in index order while
+  // fewer than top_k are kept. Every score in a bin above bstar exceeds tau
+  // (the binning is monotone), so n_gt needs a pass only after bisection.
+  uint32_t n_gt = 0;
+  if (n_in_bin <= (uint32_t)kMaxCand) {
+    uint32_t m = 0;
+    for (uint32_t i = lane; i < n_in_bin; i += kWave) m += cand[i] > tau;
+    n_gt = above_star + (uint32_t)wave_sum_int((int)m);
+  } else {
+    for (int c = 0; c < nchunks; ++c) {
+      float x[4];
+      rd.load(c, lane, x);
 #pragma unroll
-  for (int i = 0; i < MAXL; ++i)
-    if (valid(i)) {
-      gt += v[i] > tau;
-      eq += v[i] == tau;
+      for (int u = 0; u < 4; ++u) n_gt += valid(c, u) && x[u] > tau;
     }
-  const uint32_t packed = (gt << 16) | eq;
-  const uint32_t incl2 = block_inclusive_scan<NT>(packed, red_u);
-  if (tid == NT - 1) s_above = incl2 >> 16;  // total strictly above tau
-  __syncthreads();
-  const uint32_t need_eq = s_above < (uint32_t)top_k ? (uint32_t)top_k - s_above : 0u;
-  const uint32_t excl = incl2 - packed;
-  uint32_t g = excl >> 16, e = excl & 0xffffu;
+    n_gt = (uint32_t)wave_sum_int((int)n_gt);
+  }
+  const uint32_t need_eq = n_gt < (uint32_t)top_k ? (uint32_t)top_k - n_gt : 0u;
   int32_t* out = sel + row * top_k;
+  uint32_t base = 0, ties = 0;  // kept so far, ties seen so far (uniform)
+  #pragma unroll 4
+  for (int c = 0; c < nchunks; ++c) {
+    float x[4];
+    rd.load(c, lane, x);
+    uint32_t g = 0, e = 0;
 #pragma unroll
-  for (int i = 0; i < MAXL; ++i) {
-    if (!valid(i)) continue;
-    if (v[i] > tau) {
-      const uint32_t pos = g + min(e, need_eq);
-      if (pos < (uint32_t)top_k) out[pos] = beg + i;
-      ++g;
-    } else if (v[i] == tau) {
-      if (e < need_eq && g + e < (uint32_t)top_k) out[g + e] = beg + i;
-      ++e;
+    for (int u = 0; u < 4; ++u)
+      if (valid(c, u)) {
+        g += x[u] > tau;
+        e += x[u] == tau;
+      }
+    const uint32_t packed = (g << 16) | e;
+    const uint32_t inc = wave_incl_scan(packed, lane);
+    const uint32_t exc = inc - packed;
+    uint32_t eg = exc >> 16, ee = exc & 0xffffu;  // before this lane, in this chunk
+    const uint32_t tot = __shfl(inc, kWave - 1, kWave);
+    // kept before this lane's first element: strictly-greater ones plus the
+    // ties still within the budget
+    const uint32_t ties_before = ties + ee;
+    uint32_t pos = base + eg + min(ties_before, need_eq) - min(ties, need_eq);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (!valid(c, u)) continue;
+      const int32_t idx = 256 * c + 4 * lane + u;
+      if (x[u] > tau) {
+        if (pos < (uint32_t)top_k) out[pos] = idx;
+        ++pos;
+      } else if (x[u] == tau) {
+        if (ties + ee < need_eq) {
+          if (pos < (uint32_t)top_k) out[pos] = idx;
+          ++pos;
+        }
+        ++ee;
+      }
     }
+    const uint32_t tg = tot >> 16, te = tot & 0xffffu;
+    base += tg + min(ties + te, need_eq) - min(ties, need_eq);
+    ties += te;
   }
 }
 
@@ -268,17 +342,9 @@ hipError_t launch_select(const float* qbar, const float* kbar, int32_t heads, in
   hipLaunchKernelGGL(score_kernel, sgrid, dim3(256), 0, s, qbar, kbar, tq, tk, scores);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const unsigned rows = (unsigned)((int64_t)heads * tq);
-  if (tk <= 256 * 4) {
-    hipLaunchKernelGGL((select_kernel<256, 4>), dim3(rows), dim3(256), 0, s, scores, tk, top_k,
-                       sel);
-  } else if (tk <= 1024 * 8) {
-    hipLaunchKernelGGL((select_kernel<1024, 8>), dim3(rows), dim3(1024), 0, s, scores, tk,
-                       top_k, sel);
-  } else {
-    hipLaunchKernelGGL((select_kernel<1024, 32>), dim3(rows), dim3(1024), 0, s, scores, tk,
-                       top_k, sel);
-  }
+  const int64_t rows = (int64_t)heads * tq;
+  hipLaunchKernelGGL(select_kernel, dim3((unsigned)((rows + kRowsPerGroup - 1) / kRowsPerGroup)),
+                     dim3(kRowsPerGroup * kWave), 0, s, scores, rows, tk, top_k, sel);
   return hipGetLastError();
 }
 
