@@ -165,8 +165,7 @@ __global__ __launch_bounds__(kRowsPerGroup * kWave) void select_kernel(
 
   // 1. value range
   float lmax = -INFINITY, lmin = INFINITY;
-  #pragma unroll 4
-  for (int c = 0; c < nchunks; ++c) {
+    for (int c = 0; c < nchunks; ++c) {
     float x[4];
     rd.load(c, lane, x);
 #pragma unroll
@@ -182,8 +181,7 @@ __global__ __launch_bounds__(kRowsPerGroup * kWave) void select_kernel(
   for (int b = lane; b < kBins; b += kWave) hist[b] = 0u;
   const float inv = (vmax > vmin) ? (float)kBins / (vmax - vmin) : 0.f;
   auto bin_of = [&](float x) { return min(kBins - 1, (int)((x - vmin) * inv)); };
-  #pragma unroll 4
-  for (int c = 0; c < nchunks; ++c) {
+    for (int c = 0; c < nchunks; ++c) {
     float x[4];
     rd.load(c, lane, x);
 #pragma unroll
@@ -225,7 +223,6 @@ __global__ __launch_bounds__(kRowsPerGroup * kWave) void select_kernel(
   float tau;
   if (n_in_bin <= (uint32_t)kMaxCand) {
     if (lane == 0) ncand_all[wave] = 0u;
-#pragma unroll 4
     for (int c = 0; c < nchunks; ++c) {
       float x[4];
       rd.load(c, lane, x);
@@ -291,8 +288,7 @@ __global__ __launch_bounds__(kRowsPerGroup * kWave) void select_kernel(
   const uint32_t need_eq = n_gt < (uint32_t)top_k ? (uint32_t)top_k - n_gt : 0u;
   int32_t* out = sel + row * top_k;
   uint32_t base = 0, ties = 0;  // kept so far, ties seen so far (uniform)
-  #pragma unroll 4
-  for (int c = 0; c < nchunks; ++c) {
+    for (int c = 0; c < nchunks; ++c) {
     float x[4];
     rd.load(c, lane, x);
     uint32_t g = 0, e = 0;
