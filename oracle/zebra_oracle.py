@@ -50,6 +50,7 @@ __all__ = [
     "select_tiles", "attention_columns", "tile_sparse_attention_tile",
     "tile_sparse_attention", "dense_attention", "elu_plus_one",
     "linear_attention", "fit_affine", "affine_apply", "mean_attention_sparsity",
+    "block_attention_mass", "retained_mass", "top_mass",
 ]
 
 
@@ -287,3 +288,46 @@ def mean_attention_sparsity(linear_frac: float, keep_frac: float, k_tile: int) -
     """
     dense_frac = keep_frac + (1.0 - keep_frac) / k_tile
     return linear_frac + (1.0 - linear_frac) * (1.0 - dense_frac)
+
+
+# ----------------------------------------------------------------------------
+# selection-quality diagnostic
+# ----------------------------------------------------------------------------
+
+def block_attention_mass(q, k, q_tile: int, k_tile: int, scale: float,
+                         row_block: int = 1024) -> np.ndarray:
+    """Attention mass of every (query tile, key tile) block under dense softmax, one head.
+
+    The pages measure how much attention mass the highest-mass 20% of 64x64
+    token blocks retain ([paper page] Figure 2 caption, panel (b); Figure 8
+    caption). For query tile i and key tile j (reading R1 tiles):
+        M[i][j] = (1 / |Q_i|) sum_{q in Q_i} sum_{k in K_j} softmax_q(scale q . k),
+    so every row of M sums to one. [Nq][d], [Nk][d] -> [Tq][Tk].
+    """
+    q, k = _f64(q), _f64(k)
+    qb = tile_bounds(q.shape[0], q_tile)
+    kb = tile_bounds(k.shape[0], k_tile)
+    mass = np.zeros((len(qb), len(kb)), dtype=np.float64)
+    # per-query block sums, then the mean over each query tile
+    col = np.zeros((q.shape[0], len(kb)), dtype=np.float64)
+    for s0 in range(0, q.shape[0], row_block):
+        e0 = min(q.shape[0], s0 + row_block)
+        p = _softmax_rows(scale * (q[s0:e0] @ k.T))
+        for j, (a, b) in enumerate(kb):
+            col[s0:e0, j] = p[:, a:b].sum(axis=1)
+    for i, (a, b) in enumerate(qb):
+        mass[i] = col[a:b].sum(axis=0) / (b - a)
+    return mass
+
+
+def retained_mass(mass, sel) -> np.ndarray:
+    """Mass each query tile keeps on its selected key tiles: sum_{j in sel_i} M[i][j]."""
+    mass = _f64(mass)
+    sel = np.asarray(sel, dtype=np.int64)
+    return np.take_along_axis(mass, sel, axis=1).sum(axis=1)
+
+
+def top_mass(mass, top_k: int) -> np.ndarray:
+    """Mass of the top_k highest-mass key tiles of each query tile (the pages' oracle selection)."""
+    mass = _f64(mass)
+    return -np.sort(-mass, axis=1)[:, :top_k].sum(axis=1)

@@ -330,6 +330,54 @@ def pin_mean_sparsity_pages():
         assert abs(100.0 * s - p["about_percent"]) <= 1.0, f"{p}: {100 * s:.2f}%"
 
 
+# ----------------------------------------------------------------------------
+# selection-quality diagnostic
+# ----------------------------------------------------------------------------
+
+def pin_block_mass_tile_one_is_softmax():
+    """With 1-token tiles, M is the attention matrix itself (torch softmax)."""
+    q, k, _ = _qkv(41, 1, 7, 9, 8)
+    m = zo.block_attention_mass(q[0], k[0], 1, 1, 0.3)
+    ref = torch.softmax(0.3 * torch.from_numpy(q[0]) @ torch.from_numpy(k[0]).T, dim=1).numpy()
+    _close(m, ref, 1e-13, "block mass with 1-token tiles")
+
+
+def pin_block_mass_rows_sum_to_one_and_by_hand():
+    """Rows sum to one; a 2x2-tile case summed by hand from torch's softmax."""
+    q, k, _ = _qkv(42, 1, 5, 7, 4)
+    m = zo.block_attention_mass(q[0], k[0], 3, 4, 0.5)
+    _close(m.sum(axis=1), np.ones(m.shape[0]), 1e-13, "block mass row sums")
+    p = torch.softmax(0.5 * torch.from_numpy(q[0]) @ torch.from_numpy(k[0]).T, dim=1).numpy()
+    hand = np.array([[p[0:3, 0:4].sum() / 3, p[0:3, 4:7].sum() / 3],
+                     [p[3:5, 0:4].sum() / 2, p[3:5, 4:7].sum() / 2]])
+    _close(m, hand, 1e-13, "block mass by hand")
+
+
+def pin_block_mass_constant_keys():
+    """Equal keys: softmax is uniform, so a tile's mass is its share of the tokens."""
+    rng = np.random.default_rng(43)
+    q = rng.standard_normal((6, 4))
+    k = np.tile(rng.standard_normal((1, 4)), (10, 1))
+    m = zo.block_attention_mass(q, k, 4, 4, 1.0)
+    _close(m, np.tile([[0.4, 0.4, 0.2]], (2, 1)), 1e-13, "constant keys")
+
+
+def pin_retained_and_top_mass():
+    """Keeping every tile retains all mass; the top-k by mass bounds any k-subset."""
+    q, k, _ = _qkv(44, 1, 40, 60, 8)
+    m = zo.block_attention_mass(q[0], k[0], 8, 6, 0.4)
+    t_k = m.shape[1]
+    _close(zo.retained_mass(m, np.tile(np.arange(t_k), (m.shape[0], 1))), np.ones(m.shape[0]),
+           1e-13, "keep-all retains everything")
+    best = zo.top_mass(m, 3)
+    for combo in itertools.combinations(range(t_k), 3):
+        sel = np.tile(np.array(combo), (m.shape[0], 1))
+        assert np.all(zo.retained_mass(m, sel) <= best + 1e-15)
+    brute = np.array([max(m[i, list(c)].sum() for c in itertools.combinations(range(t_k), 3))
+                      for i in range(m.shape[0])])
+    _close(best, brute, 1e-15, "top-3 mass by brute force")
+
+
 ALL_PINS = [
     pin_pool_exact_rational, pin_select_brute_force, pin_select_tiles_orientation,
     pin_dense_vs_sdpa, pin_dense_closed_forms, pin_keep_all_equals_dense,
@@ -337,5 +385,7 @@ ALL_PINS = [
     pin_convexity_and_constant_values, pin_permutation_within_tile,
     pin_tiny_workload_hot_tile, pin_elu_plus_one_vs_torch, pin_linear_brute_force,
     pin_linear_closed_forms, pin_fit_vs_lstsq, pin_fit_exact_and_degenerate,
-    pin_mean_sparsity_pages,
+    pin_mean_sparsity_pages, pin_block_mass_tile_one_is_softmax,
+    pin_block_mass_rows_sum_to_one_and_by_hand, pin_block_mass_constant_keys,
+    pin_retained_and_top_mass,
 ]

@@ -108,6 +108,29 @@ def _fit_bias_sign(x, y, degenerate_rel=1e-30):
     return a, b + 2 * a * xbar, n
 
 
+def _mass_with(divide_by_k_tile=False, no_mean=False, skip_last_tile=False):
+    def mass(q, k, q_tile, k_tile, scale, row_block=1024):
+        q, k = np.asarray(q, np.float64), np.asarray(k, np.float64)
+        qb, kb = zo.tile_bounds(q.shape[0], q_tile), zo.tile_bounds(k.shape[0], k_tile)
+        lg = scale * (q @ k.T)
+        p = np.exp(lg - lg.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        out = np.zeros((len(qb), len(kb)))
+        for i, (a, b) in enumerate(qb):
+            for j, (c, d) in enumerate(kb):
+                if skip_last_tile and j == len(kb) - 1:
+                    continue
+                tot = p[a:b, c:d].sum()
+                out[i, j] = tot if no_mean else tot / ((d - c) if divide_by_k_tile else (b - a))
+        return out
+    return mass
+
+
+def _top_mass_lowest(mass, top_k):
+    m = np.asarray(mass, np.float64)
+    return np.sort(m, axis=1)[:, :top_k].sum(axis=1)
+
+
 MUTATIONS = {
     "pool divides by the full tile size": ("pool_tiles", _pool_full_tile_divisor),
     "ties go to the highest index": ("select_top_tiles", _select_ties_high),
@@ -123,6 +146,12 @@ MUTATIONS = {
     "linear normaliser dropped": ("linear_attention", _linear_no_normaliser),
     "fit through the origin": ("fit_affine", _fit_uncentred),
     "fit bias sign": ("fit_affine", _fit_bias_sign),
+    "block mass averaged over key tokens": ("block_attention_mass",
+                                            _mass_with(divide_by_k_tile=True)),
+    "block mass not averaged over queries": ("block_attention_mass", _mass_with(no_mean=True)),
+    "block mass drops the last key tile": ("block_attention_mass",
+                                           _mass_with(skip_last_tile=True)),
+    "top mass takes the lowest blocks": ("top_mass", _top_mass_lowest),
 }
 
 
