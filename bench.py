@@ -48,6 +48,10 @@ def parse():
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB three times (the "
                         "reference kernel that scales the HBM byte counters) and exit")
+    p.add_argument("--selection-quality", action="store_true",
+                   help="only measure how much dense attention mass the pooled-score selection "
+                        "keeps, against the top-k blocks by mass, on the workload's first sparse "
+                        "stage (at most 65,536 tokens) and exit")
     return p.parse_args()
 
 
@@ -211,6 +215,43 @@ def run_gpu(args, w, torch, zb, stage_mod, synth):
     return res, inputs
 
 
+def selection_quality(args, w, torch, zb, synth):
+    """Block attention mass of the first sparse stage (dense softmax), the mass
+    the pooled-score selection retains, and the mass of the top-k blocks by mass."""
+    if w.kind == "linear" or w.n_tokens > 65536:
+        print(f"--selection-quality needs a sparse workload of at most 65,536 tokens "
+              f"({w.name} has {w.n_tokens})", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda", 0)
+    s = next(i for i in range(w.n_stages) if w.stage_kind(i) == "sparse")
+    q, k, _ = synth.stage_inputs(w, s, dev)
+    qbar = zb.zebra_pool_landmarks(q, w.q_tile)
+    kbar = zb.zebra_pool_landmarks(k, w.k_tile)
+    sel = zb.zebra_select_tiles(qbar, kbar, w.k)
+    mass = zb.zebra_block_mass(q, k, w.q_tile, w.k_tile, SCALE)  # warm-up, then timed
+    ms = []
+    for _ in range(max(1, args.steps)):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        zb.zebra_block_mass(q, k, w.q_tile, w.k_tile, SCALE, out=mass)
+        b.record()
+        ms.append((a, b))
+    torch.cuda.synchronize()
+    m = mass.cpu().numpy().astype(np.float64)  # [H][Tq][Tk]
+    sel_np = sel.cpu().numpy().astype(np.int64)
+    kept = np.take_along_axis(m, sel_np, axis=2).sum(axis=2)
+    best = -np.partition(-m, w.k - 1, axis=2)[:, :, :w.k].sum(axis=2)
+    out = {"workload": w.name, "stage": s, "tokens": w.n_tokens, "heads": w.heads,
+           "q_tile": w.q_tile, "k_tile": w.k_tile, "top_k": w.k,
+           "keep_fraction": w.k / m.shape[2],
+           "retained_mass_mean": float(kept.mean()), "retained_mass_min": float(kept.min()),
+           "top_mass_mean": float(best.mean()), "top_mass_min": float(best.min()),
+           "retained_over_top_mean": float((kept / best).mean()),
+           "row_sum_max_dev": float(np.abs(m.sum(axis=2) - 1.0).max()),
+           "block_mass_ms": float(np.median([x.elapsed_time(y) for x, y in ms]))}
+    print(json.dumps({"selection_quality": out}), flush=True)
+
+
 # ----------------------------------------------------------------------------
 # CPU oracle baseline on a bounded sample of the same workload
 # ----------------------------------------------------------------------------
@@ -290,6 +331,9 @@ def main():
         sys.exit(1)
     zb.library()  # fails loudly if libzebra.so is missing
     w = synth.WORKLOADS[args.workload]
+    if args.selection_quality:
+        selection_quality(args, w, torch, zb, synth)
+        return
     res, inputs = run_gpu(args, w, torch, zb, stage_mod, synth)
     print(f"[bench] gpu done: {json.dumps(res)}", file=sys.stderr, flush=True)
 

@@ -174,6 +174,29 @@ zebra_status zebra_fit_affine(const float* x, const float* y, int32_t m, int32_t
                               int32_t head_dim, float* scale_out, float* bias_out,
                               int32_t* n_degenerate_out, void* stream);
 
+/*
+ * Selection-quality diagnostic: attention mass of every (query tile, key
+ * tile) block under dense softmax. Zebra3D paper page, Figure 2 caption,
+ * panel (b), and Figure 8 caption: the attention mass retained by the
+ * highest-mass 20% of 64x64 token blocks. For query tile i and key tile j:
+ *   mass[h][i][j] = (1/|Q_i|) sum_{q in Q_i} sum_{k in K_j} softmax_q(scale q . k),
+ * so each row sums to one. Comparing sum_{j in sel_i} mass[h][i][j] with the
+ * sum of the top_k largest entries of row i measures how much of the attention
+ * mass the pooled-score selection keeps. Not on the forward path.
+ *
+ * q (qs) and k (ks) bf16 with the same n_heads; the sequences may differ in
+ * length. q_tile 32, 64 or 128; k_tile 32 or 64; t_k = ceil(Nk / k_tile) at
+ * most 32768. scale > 0.
+ * mass_out float32 [H][t_q][t_k], contiguous. Row statistics (maximum and
+ * sum per query) and masses are float32 from bf16 MFMA scores.
+ * workspace at least zebra_block_mass_workspace(Nq, H) bytes, 16-byte aligned
+ * (the per-query row statistics).
+ */
+size_t zebra_block_mass_workspace(int64_t n_q, int32_t n_heads);
+zebra_status zebra_block_mass(const void* q, zebra_seq qs, const void* k, zebra_seq ks,
+                              int32_t q_tile, int32_t k_tile, float scale, float* mass_out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static strings; never NULL. */
 const char* zebra_status_string(zebra_status status);
 const char* zebra_version(void);

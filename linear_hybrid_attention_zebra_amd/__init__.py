@@ -29,7 +29,7 @@ ENTRY_POINTS = (
     "zebra_pool_landmarks", "zebra_select_tiles_workspace", "zebra_select_tiles",
     "zebra_tile_sparse_attn_workspace", "zebra_tile_sparse_attn",
     "zebra_linear_attn_workspace", "zebra_linear_attn", "zebra_fit_affine",
-    "zebra_status_string", "zebra_version",
+    "zebra_block_mass_workspace", "zebra_block_mass", "zebra_status_string", "zebra_version",
 )
 
 
@@ -71,6 +71,9 @@ def _declare(lib):
         "zebra_linear_attn": (c_i32, [c_p, ZebraSeq, c_p, c_p, ZebraSeq, c_p, c_p, c_p, ZebraSeq,
                                       c_i32, c_p, c_sz, c_p]),
         "zebra_fit_affine": (c_i32, [c_p, c_p, c_i32, c_i32, c_i32, c_p, c_p, c_p, c_p]),
+        "zebra_block_mass_workspace": (c_sz, [c_i64, c_i32]),
+        "zebra_block_mass": (c_i32, [c_p, ZebraSeq, c_p, ZebraSeq, c_i32, c_i32, c_f, c_p, c_p,
+                                     c_sz, c_p]),
         "zebra_status_string": (ctypes.c_char_p, [c_i32]),
         "zebra_version": (ctypes.c_char_p, []),
     }
@@ -263,3 +266,25 @@ def zebra_fit_affine(x: torch.Tensor, y: torch.Tensor, scale_out: Optional[torch
         _ptr(x), _ptr(y), m, h, x.shape[2], _ptr(scale_out), _ptr(bias_out), _ptr(n_degenerate),
         _stream(x.device)))
     return scale_out, bias_out, n_degenerate
+
+
+def zebra_block_mass(q: torch.Tensor, k: torch.Tensor, q_tile: int, k_tile: int, scale: float,
+                     out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Dense-softmax attention mass of every (query tile, key tile) block: float32 [H][Tq][Tk]."""
+    _need(q, torch.bfloat16, "q")
+    _need(k, torch.bfloat16, "k")
+    h = q.shape[0]
+    if out is None:
+        out = torch.empty((h, ceil_div(q.shape[1], q_tile), ceil_div(k.shape[1], k_tile)),
+                          dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out")
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    lib = library()
+    nbytes = lib.zebra_block_mass_workspace(q.shape[1], h)
+    workspace = _workspace(nbytes, q.device, workspace)
+    _check("zebra_block_mass", lib.zebra_block_mass(
+        _ptr(q), seq_of(q), _ptr(k), seq_of(k), q_tile, k_tile, scale, _ptr(out),
+        _ptr(workspace), nbytes, _stream(q.device)))
+    return out

@@ -84,6 +84,11 @@ hipError_t launch_linear(const uint16_t* q, int64_t nq, int64_t qst, int64_t qsh
                          int64_t ksh, int32_t heads, const float* aff_scale,
                          const float* aff_bias, void* o, int64_t ost, int64_t osh, bool o_f32,
                          void* ws, hipStream_t s);
+size_t mass_workspace_bytes(int64_t n_q, int32_t heads);
+hipError_t launch_block_mass(const uint16_t* q, int64_t nq, int64_t qst, int64_t qsh,
+                             const uint16_t* k, int64_t nk, int64_t kst, int64_t ksh,
+                             int32_t heads, int32_t q_tile, int32_t k_tile, float scale,
+                             float* mass, void* ws, hipStream_t s);
 hipError_t launch_fit(const float* x, const float* y, int32_t m, int32_t heads, float* a,
                       float* b, int32_t* n_deg, hipStream_t s);
 }  // namespace zebra

@@ -216,6 +216,42 @@ zebra_status zebra_tile_sparse_attn(const void* q, zebra_seq qs, const void* k, 
       (hipStream_t)stream));
 }
 
+size_t zebra_block_mass_workspace(int64_t n_q, int32_t n_heads) {
+  if (n_q < 0 || n_heads < 0) return 0;
+  return zebra::mass_workspace_bytes(n_q, n_heads);
+}
+
+zebra_status zebra_block_mass(const void* q, zebra_seq qs, const void* k, zebra_seq ks,
+                              int32_t q_tile, int32_t k_tile, float scale, float* mass_out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  zebra_status st;
+  if ((st = check_seq(q, qs, false)) != ZEBRA_OK) return st;
+  if ((st = check_seq(k, ks, false)) != ZEBRA_OK) return st;
+  if (qs.n_heads != ks.n_heads) return ZEBRA_ERR_INVALID_ARG;
+  if (q_tile != 32 && q_tile != 64 && q_tile != 128) return ZEBRA_ERR_UNSUPPORTED;
+  if (k_tile != 32 && k_tile != 64) return ZEBRA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || scale > 1e30f) return ZEBRA_ERR_INVALID_ARG;
+  if (seq_empty(qs)) return ZEBRA_OK;
+  if (ks.n_tokens == 0) return ZEBRA_ERR_INVALID_ARG;
+  const int64_t tk = ceil_div(ks.n_tokens, k_tile);
+  if (tk > kMaxKeyTiles) return ZEBRA_ERR_UNSUPPORTED;
+  const int64_t tq = ceil_div(qs.n_tokens, q_tile);
+  if (tq > (int64_t)INT32_MAX) return ZEBRA_ERR_UNSUPPORTED;
+  if (mass_out == nullptr || ((uintptr_t)mass_out % 4) != 0) return ZEBRA_ERR_INVALID_ARG;
+  const size_t need = zebra::mass_workspace_bytes(qs.n_tokens, qs.n_heads);
+  if (workspace == nullptr || workspace_bytes < need) return ZEBRA_ERR_WORKSPACE;
+  if (((uintptr_t)workspace % 16) != 0) return ZEBRA_ERR_INVALID_ARG;
+  const Range out = flat_range(mass_out, (uint64_t)qs.n_heads * tq * tk, 4);
+  const Range ws = flat_range(workspace, need, 1);
+  for (const Range& r : {seq_range(q, qs, 2), seq_range(k, ks, 2)})
+    if (overlaps(out, r) || overlaps(ws, r)) return ZEBRA_ERR_INVALID_ARG;
+  if (overlaps(out, ws)) return ZEBRA_ERR_INVALID_ARG;
+  return hip_status(zebra::launch_block_mass(
+      (const uint16_t*)q, qs.n_tokens, qs.stride_token, qs.stride_head, (const uint16_t*)k,
+      ks.n_tokens, ks.stride_token, ks.stride_head, qs.n_heads, q_tile, k_tile, scale,
+      mass_out, workspace, (hipStream_t)stream));
+}
+
 size_t zebra_linear_attn_workspace(int64_t n_kv, int32_t n_heads, int32_t head_dim) {
   if (n_kv < 0 || n_heads <= 0 || head_dim != zebra::kHeadDim) return 0;
   return zebra::linear_workspace_bytes(n_kv, n_heads);

@@ -31,7 +31,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     for name in names:
         assert hasattr(lib, name), f"{name} declared in zebra.h but not exported"
     assert set(names) == set(zb.ENTRY_POINTS)
@@ -121,6 +121,26 @@ def test_linear_validation(lib):
     assert call(kvs=seq(0)) == zb.ZEBRA_ERR_INVALID_ARG
     assert call(a=P(1 << 28)) == zb.ZEBRA_ERR_INVALID_ARG  # affine scale inside the output
     assert call(kvs=seq(300, h=3)) == zb.ZEBRA_ERR_INVALID_ARG  # head count mismatch
+
+
+def test_block_mass_validation(lib):
+    f = lib.zebra_block_mass
+    s = seq(256)
+    ws = lib.zebra_block_mass_workspace(256, 2)
+    assert ws == 256 * 2 * 8
+
+    def call(q_tile=64, k_tile=64, scale=0.125, out=P(1 << 28), ws_p=P(1 << 30), ws_b=ws, ks=s):
+        return f(P(1 << 16), s, P(1 << 20), ks, q_tile, k_tile, scale, out, ws_p, ws_b, None)
+
+    assert call(q_tile=16) == zb.ZEBRA_ERR_UNSUPPORTED
+    assert call(k_tile=128) == zb.ZEBRA_ERR_UNSUPPORTED
+    assert call(scale=-1.0) == zb.ZEBRA_ERR_INVALID_ARG
+    assert call(out=None) == zb.ZEBRA_ERR_INVALID_ARG
+    assert call(out=P(1 << 20)) == zb.ZEBRA_ERR_INVALID_ARG  # mass written over k
+    assert call(ws_p=None) == zb.ZEBRA_ERR_WORKSPACE
+    assert call(ws_b=ws - 8) == zb.ZEBRA_ERR_WORKSPACE
+    assert call(ks=seq(0)) == zb.ZEBRA_ERR_INVALID_ARG
+    assert call(ks=seq(256, h=3)) == zb.ZEBRA_ERR_INVALID_ARG  # head count mismatch
 
 
 def test_fit_validation(lib):

@@ -92,3 +92,19 @@ def test_full_size_linear_stage_sampled(name, stage):
         qs = qh[idx.cpu().numpy()[pick]]
         assert_close(x[h, pick], zo.linear_attention(qs, kh, vh)[0], f"{name} x head {h}")
         assert_close(y[h, pick], zo.dense_attention(qs, kh, vh, SCALE), f"{name} y head {h}")
+
+
+def test_full_size_block_mass_sampled():
+    w = synth.WORKLOADS["sparse-16v"]
+    print(f"[case] full-size block mass {w.name}: N={w.n_tokens} H={w.heads}", flush=True)
+    q, k, _ = synth.stage_inputs(w, 0, DEV)
+    mass = zb.zebra_block_mass(q, k, w.q_tile, w.k_tile, SCALE)
+    torch.cuda.synchronize()
+    g = to_f64(mass)
+    np.testing.assert_allclose(g.sum(axis=2), 1.0, atol=1e-4)
+    rows = synth.sample_rows(w.heads, w.t_q, 4, 300)
+    for h, i in rows:
+        qh, kh = _head(q, h), _head(k, h)
+        s0, e0 = i * w.q_tile, min(w.n_tokens, (i + 1) * w.q_tile)
+        ref = zo.block_attention_mass(qh[s0:e0], kh, w.q_tile, w.k_tile, SCALE)[0]
+        np.testing.assert_allclose(g[h, i], ref, rtol=1e-3, atol=1e-6)

@@ -288,3 +288,73 @@ def test_calibration_pipeline_small():
         ra, rb, _ = zo.fit_affine(to_f64(cal.x[h]), to_f64(cal.y[h]))
         np.testing.assert_allclose(to_f64(cal.aff_scale[h]), ra, rtol=1e-4, atol=1e-6)
         np.testing.assert_allclose(to_f64(cal.aff_bias[h]), rb, rtol=1e-4, atol=1e-7)
+
+
+# ----------------------------------------------------------------------------
+# block attention mass (selection-quality diagnostic)
+# ----------------------------------------------------------------------------
+
+# float32 scores and exponentials against float64: per-element relative error
+# of a few 1e-6 per term; the sums over up to 10^4 terms stay well inside these.
+MASS_RTOL = 1e-3
+MASS_ATOL = 1e-6
+
+
+@pytest.mark.parametrize("heads,n_q,n_kv,q_tile,k_tile,n_hot", [
+    (2, 300, 300, 64, 64, 2), (1, 130, 700, 128, 64, 3), (3, 97, 65, 32, 32, 1),
+    (2, 1, 40, 64, 64, 1), (1, 2000, 1500, 64, 32, 4),
+])
+def test_block_mass_parity(heads, n_q, n_kv, q_tile, k_tile, n_hot):
+    print(f"[case] block mass H={heads} Nq={n_q} Nk={n_kv} tiles {q_tile}x{k_tile}", flush=True)
+    q, k, _ = _clustered(n_q + n_kv, heads, n_q, n_kv, q_tile, k_tile, n_hot)
+    got = zb.zebra_block_mass(bf16_gpu(q), bf16_gpu(k), q_tile, k_tile, 0.125)
+    torch.cuda.synchronize()
+    g = to_f64(got)
+    for h in range(heads):
+        ref = zo.block_attention_mass(q[h], k[h], q_tile, k_tile, 0.125)
+        np.testing.assert_allclose(g[h], ref, rtol=MASS_RTOL, atol=MASS_ATOL)
+    np.testing.assert_allclose(g.sum(axis=2), 1.0, atol=1e-4)
+
+
+def test_block_mass_large_scores_and_strided_layout():
+    # scores far beyond float32's exp range: the running maximum must absorb them
+    rng = np.random.default_rng(7)
+    heads, n = 2, 700
+    q = synth.bf16_round(rng.standard_normal((heads, n, 64)).astype(np.float32) * 12)
+    k = synth.bf16_round(rng.standard_normal((heads, n, 64)).astype(np.float32) * 12)
+    qg = bf16_gpu(q).permute(1, 0, 2).contiguous().permute(1, 0, 2)  # token-major
+    got = zb.zebra_block_mass(qg, bf16_gpu(k), 64, 64, 0.125)
+    torch.cuda.synchronize()
+    for h in range(heads):
+        ref = zo.block_attention_mass(q[h], k[h], 64, 64, 0.125)
+        np.testing.assert_allclose(to_f64(got[h]), ref, rtol=MASS_RTOL, atol=MASS_ATOL)
+
+
+def test_block_mass_is_deterministic():
+    q, k, _ = _clustered(11, 2, 600, 900, 64, 64, 2)
+    qg, kg = bf16_gpu(q), bf16_gpu(k)
+    a = zb.zebra_block_mass(qg, kg, 64, 64, 0.125)
+    b = zb.zebra_block_mass(qg, kg, 64, 64, 0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_block_mass_retained_by_gpu_selection():
+    # the mass the GPU's own selection keeps, from the GPU's masses, matches the
+    # oracle's, and never exceeds the oracle's top-k mass
+    heads, n, tile, top_k = 2, 1024, 64, 4
+    q, k, _ = _clustered(5, heads, n, n, tile, tile, 2)
+    qg, kg = bf16_gpu(q), bf16_gpu(k)
+    sel = zb.zebra_select_tiles(zb.zebra_pool_landmarks(qg, tile),
+                                zb.zebra_pool_landmarks(kg, tile), top_k)
+    mass = zb.zebra_block_mass(qg, kg, tile, tile, 0.125)
+    torch.cuda.synchronize()
+    for h in range(heads):
+        ref = zo.block_attention_mass(q[h], k[h], tile, tile, 0.125)
+        kept = zo.retained_mass(to_f64(mass[h]), sel[h].cpu().numpy())
+        kept_ref = zo.retained_mass(ref, sel[h].cpu().numpy())
+        np.testing.assert_allclose(kept, kept_ref, rtol=MASS_RTOL, atol=1e-5)
+        best = zo.top_mass(ref, top_k)
+        assert np.all(kept_ref <= best + 1e-12)
+        print(f"[parity] head {h}: retained {kept_ref.mean():.4f} of top {best.mean():.4f}",
+              flush=True)
