@@ -7,14 +7,25 @@
 // each omitted tile j. With sel == NULL every tile is kept: exact dense
 // attention.
 //
-// Work decomposition. One workgroup per (head, query tile) item, head-major,
-// so the workgroups running together share one head's keys and values. One
-// wave owns 32 queries. An item is a list of column blocks of KT columns:
-// its kept key tiles (ascending),
-// then the landmark rows of ALL key tiles, KT at a time, with the kept ones
-// masked out by a per-item bitmap in LDS. Landmark rows are few and shared by
-// every item of a head, so they stay in L2; masking costs less than gathering
-// per-item omitted lists.
+// Work decomposition. One workgroup per item, head-major; one wave owns 32
+// queries. An item is a list of column blocks of KT columns: its kept key
+// tiles (ascending), then the landmark rows of the key tiles it covers, KT at
+// a time, with the kept ones masked out by a per-item bitmap in LDS.
+// Landmark rows are few and shared by every item of a head, so they stay in
+// L2; masking costs less than gathering per-item omitted lists.
+//
+// Short key ranges (and dense attention): an item is one (head, query tile)
+// over every key tile, and writes the normalised output.
+//
+// Long key ranges (split keys): the key tiles are cut into chunks of CT tiles
+// and an item is one (head, key chunk, query tile), ordered chunk-major within
+// a head. Query tiles keep different random subsets of key tiles, so over the
+// whole range the workgroups running together share almost no K/V blocks and
+// every kept block is a fresh fetch from HBM. Within one chunk they share the
+// chunk's few megabytes of K/V, which then stay in L2. Each item writes its
+// unnormalised output and (reference, row sum) in float32; a combine kernel
+// merges the chunks of each query in chunk order:
+//   O = sum_c 2^(r_c - R) O_c / sum_c 2^(r_c - R) l_c,   R = max_c r_c.
 //
 // Per block the wave computes the transposed score block S^T = K Q^T with
 // bf16 MFMA 32x32x16 (each lane then holds ONE query's scores over 32 keys),
@@ -76,10 +87,15 @@ struct SparseParams {
   int64_t nq, qst, qsh;
   int64_t nk, kst, ksh;
   int64_t ost, osh;
-  int64_t n_items;         // heads * tq
+  int64_t n_items;         // heads * n_chunks * tq
   int32_t tq, tk, top_k;
   float scale_log2;        // softmax scale * log2(e), > 0
   int32_t o_f32;
+  // split keys (n_chunks > 1): chunk c covers key tiles [c CT, (c + 1) CT)
+  int32_t n_chunks, chunk_tiles;
+  const int32_t* coff;     // [H][tq][n_chunks + 1]: first kept entry of each chunk
+  float* part_o;           // [H][nq][n_chunks][64] unnormalised outputs
+  float2* part_ml;         // [H][nq][n_chunks] (reference, row sum), p = 2^(c s - reference)
 };
 
 // Byte offset of 16-byte chunk `chunk` of 128-byte row `row` in a tile. The
@@ -210,12 +226,13 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
   const int qi = lane & 31;  // query within the wave / column of S^T
   const int hh = lane >> 5;  // lane half
   const bool dense = sel == nullptr;
-  const int n_kept = dense ? p.tk : p.top_k;
-  const int n_lb = dense ? 0 : (p.tk + KT - 1) / KT;  // landmark blocks
-  const int n_total = n_kept + n_lb;
+  const int n_lb_all = dense ? 0 : (p.tk + KT - 1) / KT;  // landmark blocks of a head
   const int tail_rows = (int)(p.nk - (int64_t)(p.tk - 1) * KT);  // rows of tile tk-1
-  const int last_lrows = p.tk - (n_lb - 1) * KT;  // landmark rows in the last block
+  const int last_lrows = p.tk - (n_lb_all - 1) * KT;  // landmark rows in the last block
   const float c = p.scale_log2;
+  const int n_ch = p.n_chunks;
+  const int lb_per_chunk = p.chunk_tiles / KT;
+  const int64_t items_per_head = (int64_t)n_ch * p.tq;
 
   // ---- direct-to-LDS staging. 1 KB block u of a tile holds rows 8u..8u+7;
   // lane i writes physical chunk i%8 of row r = 8u + i/8, i.e. logical chunk
@@ -232,9 +249,22 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
   }
 
   for (int64_t item = blockIdx.x; item < p.n_items; item += gridDim.x) {
-    const int h = (int)(item / p.tq);
-    const int qtile = (int)(item - (int64_t)h * p.tq);
-    const int32_t* sel_row = dense ? nullptr : sel + item * p.top_k;
+    const int h = (int)(item / items_per_head);
+    const int64_t rem = item - (int64_t)h * items_per_head;
+    const int ch = (int)(rem / p.tq);
+    const int qtile = (int)(rem - (int64_t)ch * p.tq);
+    const int64_t row = (int64_t)h * p.tq + qtile;  // (head, query tile)
+    // the item's kept entries [kept0, kept0 + n_kept) and landmark blocks [lb0, lb0 + n_lb)
+    int kept0 = 0, n_kept = dense ? p.tk : p.top_k, lb0 = 0, n_lb = n_lb_all;
+    if (n_ch > 1) {
+      const int32_t* co = p.coff + row * (n_ch + 1) + ch;
+      kept0 = __builtin_amdgcn_readfirstlane(co[0]);
+      n_kept = max(__builtin_amdgcn_readfirstlane(co[1]) - kept0, 0);
+      lb0 = ch * lb_per_chunk;
+      n_lb = min(lb_per_chunk, n_lb_all - lb0);
+    }
+    const int n_total = n_kept + n_lb;
+    const int32_t* sel_row = dense ? nullptr : sel + row * p.top_k + kept0;
     const uint8_t* kh = (const uint8_t*)(p.k + (int64_t)h * p.ksh);
     const uint8_t* vh = (const uint8_t*)(p.v + (int64_t)h * p.ksh);
     const uint8_t* klm =
@@ -245,8 +275,8 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
     lds_barrier();  // every wave is done with the previous item's LDS
     if (tid == 0) slow_item = 0;
     if (!dense) {
-      const int words = NB * n_lb;  // every word a landmark block reads
-      for (int e = tid; e < words; e += NT) kept_bits[e] = 0u;
+      const int words = NB * n_lb;  // every word the item's landmark blocks read
+      for (int e = tid; e < words; e += NT) kept_bits[NB * lb0 + e] = 0u;
       const int nw = min(kWin, n_kept);
       for (int e = tid; e < nw; e += NT) win[e] = (uint16_t)min(max(sel_row[e], 0), p.tk - 1);
     }
@@ -267,7 +297,8 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
     }
     float k2 = p.range[((int64_t)h * kRangeParts + lane) * 2];
     float vmax = p.range[((int64_t)h * kRangeParts + lane) * 2 + 1];
-    const int last_kept = dense ? p.tk - 1 : min(max(sel_row[n_kept - 1], 0), p.tk - 1);
+    const int last_kept =
+        dense ? p.tk - 1 : (n_kept > 0 ? min(max(sel_row[n_kept - 1], 0), p.tk - 1) : -1);
     __syncthreads();  // also completes every vector load above
     if (!dense)
       for (int e = tid; e < n_kept; e += NT) {
@@ -323,9 +354,9 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
 #pragma unroll
         for (int v = 0; v < NU; ++v) off[v] = off_kv[v];
       } else {
-        const int b = t - n_kept;
+        const int b = lb0 + t - n_kept;
         base = tl + (int64_t)b * KT * 128;
-        rows = b == n_lb - 1 ? last_lrows : KT;
+        rows = b == n_lb_all - 1 ? last_lrows : KT;
         row_bytes = 128;
 #pragma unroll
         for (int v = 0; v < NU; ++v) off[v] = off_lm[v];
@@ -343,11 +374,11 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
     // excluded columns of block t (bit set = excluded), or 0
     auto block_mask = [&](int t) -> uint64_t {
       if (t < n_kept) return t == n_kept - 1 && last_rows < KT ? ~0ull << last_rows : 0ull;
-      const int b = t - n_kept;
+      const int b = lb0 + t - n_kept;
       const uint32_t lo = __builtin_amdgcn_readfirstlane(kept_bits[NB * b]);
       const uint32_t hi = KT == 64 ? __builtin_amdgcn_readfirstlane(kept_bits[2 * b + 1]) : 0u;
       uint64_t m = ((uint64_t)hi << 32) | lo;
-      if (b == n_lb - 1 && last_lrows < KT) m |= ~0ull << last_lrows;
+      if (b == n_lb_all - 1 && last_lrows < KT) m |= ~0ull << last_lrows;
       return m;
     };
 
@@ -557,7 +588,22 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
     // ---- epilogue: O / l, lane (qi, hh) holds channels 32db + 8g + 4hh + r
     const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
                                                       __float_as_uint(l_run), false, false);
-    const float inv = 1.0f / (__uint_as_float(lsw[0]) + __uint_as_float(lsw[1]));
+    const float l_sum = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
+    if (n_ch > 1) {  // split keys: unnormalised partial and (reference, row sum)
+      if (qvalid) {
+        const int64_t prow = ((int64_t)h * p.nq + qrow) * n_ch + ch;
+        float* op = p.part_o + prow * kHeadDim + 4 * hh;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *(f32x4*)(op + 32 * db + 8 * g) = f32x4{oacc[db][4 * g], oacc[db][4 * g + 1],
+                                                    oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+        if (hh == 0) p.part_ml[prow] = float2{fast ? m_q - kPShift : mc_run, l_sum};
+      }
+      continue;
+    }
+    const float inv = 1.0f / l_sum;
     if (qvalid) {
       if (p.o_f32) {
         float* op = (float*)p.o + (int64_t)h * p.osh + qrow * p.ost + 4 * hh;
@@ -595,27 +641,135 @@ __global__ void pack_landmarks_kernel(const float* __restrict__ kbar,
   }
 }
 
+// Split keys: coff[row][c] = first entry of the (ascending) kept list of row
+// whose tile index is at least c * chunk_tiles, c = 0..n_chunks. Lower bound
+// by bisection; any contents of sel give an index in [0, top_k].
+__global__ __launch_bounds__(256) void chunk_offsets_kernel(const int32_t* __restrict__ sel,
+                                                            int64_t rows, int32_t top_k,
+                                                            int32_t n_chunks, int32_t chunk_tiles,
+                                                            int32_t* __restrict__ coff) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= rows * (n_chunks + 1)) return;
+  const int64_t row = e / (n_chunks + 1);
+  const int ch = (int)(e - row * (n_chunks + 1));
+  const int32_t* s = sel + row * top_k;
+  const int64_t target = (int64_t)ch * chunk_tiles;
+  int lo = 0, hi = top_k;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (s[mid] < target) lo = mid + 1;
+    else hi = mid;
+  }
+  coff[e] = lo;
+}
+
+// Split keys: merge the chunk partials of each query in chunk order. 16 lanes
+// per query, 4 channels each.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o,
+                                                      const float2* __restrict__ part_ml,
+                                                      int32_t n_chunks, int64_t nq, int64_t rows,
+                                                      void* o, int64_t ost, int64_t osh,
+                                                      int32_t o_f32) {
+  const int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // (head, query)
+  if (r >= rows) return;
+  const int sub = threadIdx.x & 15;
+  const float2* ml = part_ml + r * n_chunks;
+  float ref = -INFINITY;
+  for (int ch = 0; ch < n_chunks; ++ch) ref = fmaxf(ref, ml[ch].x);
+  const float* po = part_o + r * n_chunks * kHeadDim + 4 * sub;
+  float l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    const float2 m = ml[ch];
+    const float w = __builtin_amdgcn_exp2f(m.x - ref);
+    const f32x4 x = *(const f32x4*)(po + (int64_t)ch * kHeadDim);
+    l = __builtin_fmaf(m.y, w, l);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(x[i], w, acc[i]);
+  }
+  const float inv = 1.0f / l;
+  const int64_t h = r / nq, q = r - h * nq;
+  if (o_f32) {
+    float* op = (float*)o + h * osh + q * ost + 4 * sub;
+    *(f32x4*)op = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+  } else {
+    uint16_t* op = (uint16_t*)o + h * osh + q * ost + 4 * sub;
+    *(u32x2*)op = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv),
+                        pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  }
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Keys per chunk of the split-key decomposition: K and V of one chunk of one
+// head take kChunkKeys * 256 bytes.
+constexpr int64_t kChunkKeys = 32768;
+// Partial outputs take at most this much workspace; longer ranges use fewer,
+// larger chunks.
+constexpr double kMaxPartialBytes = 64.0 * (1ull << 30);
+
+struct SplitPlan {
+  int32_t n_chunks = 1, chunk_tiles = 0;
+  size_t coff = 0, part_o = 0, part_ml = 0;  // workspace bytes of each
+};
+
+// Split only where the K/V traffic bounds the stage: 128-query tiles fetch half
+// the bytes per flop and run compute-bound, and there the partials cost more
+// than the L2 reuse saves.
+SplitPlan split_plan(int64_t nq, int64_t tk, int32_t heads, int32_t q_tile, int32_t k_tile,
+                     int32_t top_k) {
+  SplitPlan sp;
+  if (top_k >= tk || q_tile > 64) return sp;
+  int64_t ct = kChunkKeys / k_tile;
+  const double per_chunk = (double)heads * nq * (kHeadDim + 2) * sizeof(float);
+  const int64_t max_chunks = (int64_t)(kMaxPartialBytes / per_chunk);
+  if (max_chunks < 2 || tk < 2 * ct) return sp;
+  int64_t nc = (tk + ct - 1) / ct;
+  if (nc > max_chunks) {  // widen the chunks to a multiple of k_tile landmark rows
+    ct = ((tk + max_chunks - 1) / max_chunks + k_tile - 1) / k_tile * k_tile;
+    nc = (tk + ct - 1) / ct;
+  }
+  if (nc < 2) return sp;
+  const int64_t tq = (nq + q_tile - 1) / q_tile;
+  sp.n_chunks = (int32_t)nc;
+  sp.chunk_tiles = (int32_t)ct;
+  sp.coff = align256((size_t)heads * tq * (nc + 1) * sizeof(int32_t));
+  sp.part_o = align256((size_t)heads * nq * nc * kHeadDim * sizeof(float));
+  sp.part_ml = align256((size_t)heads * nq * nc * sizeof(float2));
+  return sp;
+}
 
 template <int QT, int KT>
 hipError_t launch_kernel(const SparseParams& p, const int32_t* sel, hipStream_t s) {
-  // one workgroup per item (the item loop also serves a smaller grid)
-  hipLaunchKernelGGL((tile_sparse_kernel<QT, KT>), dim3((unsigned)p.n_items), dim3(QT * 2), 0, s,
-                     p, sel);
+  // one workgroup per item (the item loop serves the rest when the grid is capped)
+  const int64_t grid = std::min<int64_t>(p.n_items, (int64_t)1 << 24);
+  hipLaunchKernelGGL((tile_sparse_kernel<QT, KT>), dim3((unsigned)grid), dim3(QT * 2), 0, s, p,
+                     sel);
   return hipGetLastError();
+}
+
+hipError_t launch_tiles(const SparseParams& p, const int32_t* sel, int32_t q_tile,
+                        int32_t k_tile, hipStream_t s) {
+  if (k_tile == 64) {
+    if (q_tile == 32) return launch_kernel<32, 64>(p, sel, s);
+    if (q_tile == 64) return launch_kernel<64, 64>(p, sel, s);
+    return launch_kernel<128, 64>(p, sel, s);
+  }
+  if (q_tile == 32) return launch_kernel<32, 32>(p, sel, s);
+  if (q_tile == 64) return launch_kernel<64, 32>(p, sel, s);
+  return launch_kernel<128, 32>(p, sel, s);
 }
 
 }  // namespace
 
 size_t sparse_workspace_bytes(int64_t n_q, int64_t n_kv, int32_t heads, int32_t q_tile,
                               int32_t k_tile, int32_t top_k) {
-  (void)n_q;
-  (void)q_tile;
   const int64_t tk = (n_kv + k_tile - 1) / k_tile;
   const size_t range = align256((size_t)heads * kRangeParts * 2 * sizeof(float));
   if (top_k >= tk) return range;
   const size_t lm = align256((size_t)heads * tk * kHeadDim * sizeof(uint16_t));
-  return 2 * lm + range;
+  const SplitPlan sp = split_plan(n_q, tk, heads, q_tile, k_tile, top_k);
+  return 2 * lm + range + sp.coff + sp.part_o + sp.part_ml;
 }
 
 hipError_t launch_tile_sparse(const uint16_t* q, int64_t nq, int64_t qst, int64_t qsh,
@@ -640,6 +794,11 @@ hipError_t launch_tile_sparse(const uint16_t* q, int64_t nq, int64_t qst, int64_
   p.tq = (int32_t)((nq + q_tile - 1) / q_tile);
   p.tk = (int32_t)((nk + k_tile - 1) / k_tile);
   p.n_items = (int64_t)heads * p.tq;
+  p.n_chunks = 1;
+  p.chunk_tiles = 0;
+  p.coff = nullptr;
+  p.part_o = nullptr;
+  p.part_ml = nullptr;
   p.top_k = top_k;
   p.scale_log2 = scale * kLog2e;
   p.o_f32 = o_f32 ? 1 : 0;
@@ -670,14 +829,27 @@ hipError_t launch_tile_sparse(const uint16_t* q, int64_t nq, int64_t qst, int64_
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   p.range = range;
-  if (k_tile == 64) {
-    if (q_tile == 32) return launch_kernel<32, 64>(p, sel, s);
-    if (q_tile == 64) return launch_kernel<64, 64>(p, sel, s);
-    return launch_kernel<128, 64>(p, sel, s);
-  }
-  if (q_tile == 32) return launch_kernel<32, 32>(p, sel, s);
-  if (q_tile == 64) return launch_kernel<64, 32>(p, sel, s);
-  return launch_kernel<128, 32>(p, sel, s);
+  const SplitPlan sp = sparse ? split_plan(nq, p.tk, heads, q_tile, k_tile, top_k) : SplitPlan{};
+  if (sp.n_chunks == 1) return launch_tiles(p, sel, q_tile, k_tile, s);
+
+  uint8_t* w = wsb + align256((size_t)heads * kRangeParts * 2 * sizeof(float));
+  p.n_chunks = sp.n_chunks;
+  p.chunk_tiles = sp.chunk_tiles;
+  p.coff = (const int32_t*)w;
+  p.part_o = (float*)(w + sp.coff);
+  p.part_ml = (float2*)(w + sp.coff + sp.part_o);
+  p.n_items = (int64_t)heads * sp.n_chunks * p.tq;
+  const int64_t rows = (int64_t)heads * p.tq;
+  const int64_t n_off = rows * (sp.n_chunks + 1);
+  hipLaunchKernelGGL(chunk_offsets_kernel, dim3((unsigned)((n_off + 255) / 256)), dim3(256), 0, s,
+                     sel, rows, top_k, sp.n_chunks, sp.chunk_tiles, (int32_t*)w);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if ((err = launch_tiles(p, sel, q_tile, k_tile, s)) != hipSuccess) return err;
+  const int64_t qrows = (int64_t)heads * nq;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((qrows + 15) / 16)), dim3(256), 0, s,
+                     (const float*)p.part_o, (const float2*)p.part_ml, sp.n_chunks, nq, qrows, o,
+                     ost, osh, p.o_f32);
+  return hipGetLastError();
 }
 
 }  // namespace zebra

@@ -126,6 +126,51 @@ def test_sparse_stage_parity(case, out_dtype):
     print(f"[parity] near-tie swaps {swaps}", flush=True)
 
 
+# With query tiles of at most 64, key ranges of at least 1,024 tiles of 64
+# (2,048 of 32) run as split keys: items per (head, key chunk of 512 tiles of
+# 64 / 1,024 of 32, query tile), merged by a combine kernel.
+SPLIT_CASES = [
+    # (q_tile, k_tile, n_q, n_kv, top_k, n_hot, heads)
+    (64, 64, 300, 65536 + 333, 1, 1, 2),     # 3 chunks, ragged tail; most chunks keep nothing
+    (64, 64, 300, 65536 + 333, 206, 3, 2),   # 20% kept
+    (64, 64, 130, 65536, 1023, 2, 1),        # 2 whole chunks; all but one tile kept
+    (64, 32, 257, 70000, 440, 2, 1),         # 32-key tiles: 3 chunks of 1,024 tiles
+    (128, 64, 257, 70000, 220, 2, 1),        # 128-query tiles: one pass, no split
+    (32, 64, 100, 98304, 300, 2, 2),         # 32-query tiles
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[str(c) for c in SPLIT_CASES])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_split_keys_parity(case, out_dtype):
+    test_sparse_stage_parity(case, out_dtype)
+
+
+def test_split_keys_both_softmax_references():
+    """Split keys with some query tiles on the running-maximum path."""
+    n_q, n_kv = 300, 65536 + 100
+    print(f"[case] split keys reference paths Nq={n_q} Nk={n_kv}", flush=True)
+    q, k, v = _clustered(23, 2, n_q, n_kv, 64, 64, 3)
+    q = q.copy()
+    q[:, 64:192] *= 8.0  # query tiles 1 and 2: bound far above the fast-path limit
+    q = synth.bf16_round(q)
+    bufs = stage.SparseBuffers.allocate(2, n_q, n_kv, 64, 64, 100, DEV, torch.float32)
+    stage.sparse_stage(bf16_gpu(q), bf16_gpu(k), bf16_gpu(v), 64, 64, 100, 0.125, bufs)
+    torch.cuda.synchronize()
+    ref, _ = zo.tile_sparse_attention(q, k, v, 64, 64, 100, 0.125, sel=bufs.sel.cpu().numpy())
+    assert_close(bufs.out, ref, "split keys reference paths")
+
+
+def test_split_keys_is_deterministic():
+    q, k, v = _clustered(12, 1, 200, 70000, 64, 64, 3)
+    outs = []
+    for _ in range(2):
+        bufs = stage.sparse_stage(bf16_gpu(q), bf16_gpu(k), bf16_gpu(v), 64, 64, 220, 0.125)
+        outs.append(bufs.out.clone())
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+
+
 @pytest.mark.parametrize("q_tile,k_tile,n_q,n_kv", [(64, 64, 300, 300), (128, 64, 130, 700),
                                                     (32, 32, 100, 65)])
 def test_dense_mode_parity(q_tile, k_tile, n_q, n_kv):
