@@ -34,6 +34,16 @@ Readings taken where the pages are silent (each is listed again where used):
   R5 the fit target is dense softmax attention of the same stage at sampled
      queries; a channel whose inputs do not vary gets scale 0 and bias mean(y).
 
+Operator variants of the pages' ablations ([paper page] Table 3(a) and (b);
+appendix Tables 15-17: block or tile sparse, each with and without landmark),
+off by default:
+  V1 without landmarks: omitted tiles are dropped; softmax runs over the
+     tokens of the kept tiles only.
+  V2 landmark log count: a landmark stands for the n_j valid tokens of its
+     tile, so its logit gains ln(n_j) (the short last tile counts its valid
+     tokens).
+  V3 uncentered fit: the map through the origin, a = sum x y / sum x^2, b = 0.
+
 Parity status: every function on the attention path is pinned by
 ``tests/oracle_pins.py`` against closed forms, library routines or brute
 force. ``mean_attention_sparsity`` is bookkeeping, not part of the path; the
@@ -49,8 +59,9 @@ __all__ = [
     "tile_bounds", "pool_tiles", "block_scores", "select_top_tiles",
     "select_tiles", "attention_columns", "tile_sparse_attention_tile",
     "tile_sparse_attention", "dense_attention", "elu_plus_one",
-    "linear_attention", "fit_affine", "affine_apply", "mean_attention_sparsity",
-    "block_attention_mass", "retained_mass", "top_mass",
+    "linear_attention", "fit_affine", "fit_scale_only", "affine_apply",
+    "mean_attention_sparsity", "block_attention_mass",
+    "retained_mass", "top_mass",
 ]
 
 
@@ -122,14 +133,19 @@ def select_tiles(qbar, kbar, top_k: int) -> np.ndarray:
 # tile-sparse softmax attention with mean-key/value landmarks
 # ----------------------------------------------------------------------------
 
-def attention_columns(k, v, k_tile: int, kept):
-    """Keys and values one query tile attends to (readings R1, R3).
+def attention_columns(k, v, k_tile: int, kept, landmarks: bool = True,
+                      landmark_log_count: bool = False):
+    """Keys, values and additive logits of the columns one query tile attends to
+    (readings R1, R3).
 
     Every token of every kept tile, then one landmark (kbar_j, vbar_j) for
     every omitted tile j. Kept tiles keep full softmax interactions and
     omitted tiles become mean-key/value landmarks ([paper page] Figure 1
     caption); the [synopsis] ("Interpretation") calls the kept part exact
-    softmax over selected tiles.
+    softmax over selected tiles. The additive logit is zero for every column,
+    except that under variant V2 a landmark gets ln(n_j), n_j the valid tokens
+    of its tile. With landmarks=False (variant V1) the omitted tiles
+    contribute nothing. Returns ([C][d] keys, [C][d] values, [C] logits).
     """
     k = _f64(k)
     v = _f64(v)
@@ -140,18 +156,22 @@ def attention_columns(k, v, k_tile: int, kept):
         raise ValueError("kept tiles must be distinct")
     kbar = pool_tiles(k, k_tile)
     vbar = pool_tiles(v, k_tile)
-    keys, vals = [], []
+    keys, vals, bias = [], [], []
     for j in sorted(kept):
         s, e = bounds[j]
         keys.append(k[s:e])
         vals.append(v[s:e])
+        bias.append(np.zeros(e - s))
     for j in range(len(bounds)):
-        if j not in kept_set:
+        if landmarks and j not in kept_set:
+            s, e = bounds[j]
             keys.append(kbar[j:j + 1])
             vals.append(vbar[j:j + 1])
+            bias.append(np.full(1, np.log(e - s) if landmark_log_count else 0.0))
     if not keys:
-        return np.zeros((0, k.shape[1])), np.zeros((0, v.shape[1]))
-    return np.concatenate(keys, axis=0), np.concatenate(vals, axis=0)
+        return np.zeros((0, k.shape[1])), np.zeros((0, v.shape[1])), np.zeros(0)
+    return (np.concatenate(keys, axis=0), np.concatenate(vals, axis=0),
+            np.concatenate(bias))
 
 
 def _softmax_rows(logits: np.ndarray) -> np.ndarray:
@@ -160,20 +180,26 @@ def _softmax_rows(logits: np.ndarray) -> np.ndarray:
     return w / w.sum(axis=1, keepdims=True)
 
 
-def tile_sparse_attention_tile(q_rows, k, v, k_tile: int, kept, scale: float) -> np.ndarray:
-    """Output of the queries of one query tile: softmax(scale q C_k^T) C_v."""
+def tile_sparse_attention_tile(q_rows, k, v, k_tile: int, kept, scale: float,
+                               landmarks: bool = True,
+                               landmark_log_count: bool = False) -> np.ndarray:
+    """Output of the queries of one query tile: softmax(scale q C_k^T + bias) C_v.
+
+    bias is zero except under variant V2 (attention_columns).
+    """
     q_rows = _f64(q_rows)
-    ck, cv = attention_columns(k, v, k_tile, kept)
-    return _softmax_rows(scale * (q_rows @ ck.T)) @ cv
+    ck, cv, bias = attention_columns(k, v, k_tile, kept, landmarks, landmark_log_count)
+    return _softmax_rows(scale * (q_rows @ ck.T) + bias[None, :]) @ cv
 
 
 def tile_sparse_attention(q, k, v, q_tile: int, k_tile: int, top_k: int, scale: float,
-                          sel=None):
+                          sel=None, landmarks: bool = True, landmark_log_count: bool = False):
     """Tile-sparse stage over all heads: [H][Nq][d], [H][Nk][d] x2 -> ([H][Nq][d], sel).
 
     ``sel`` ([H][Tq][top_k]) replaces the oracle's own selection when given,
     which lets the attention step be checked on another implementation's
-    choice of tiles.
+    choice of tiles. ``landmarks`` and ``landmark_log_count`` select the
+    variants V1 and V2.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     heads, n_q, _ = q.shape
@@ -187,7 +213,8 @@ def tile_sparse_attention(q, k, v, q_tile: int, k_tile: int, top_k: int, scale: 
         sels.append(sel_h)
         for i, (s, e) in enumerate(tile_bounds(n_q, q_tile)):
             out[h, s:e] = tile_sparse_attention_tile(q[h, s:e], k[h], v[h], k_tile,
-                                                     sel_h[i], scale)
+                                                     sel_h[i], scale, landmarks,
+                                                     landmark_log_count)
     return out, np.stack(sels) if sels else np.zeros((0, 0, top_k), dtype=np.int64)
 
 
@@ -271,6 +298,26 @@ def fit_affine(x, y, degenerate_rel: float = 1e-30):
     a = np.where(ok, sxy / np.where(ok, sxx, 1.0), 0.0)
     b = ybar - a * xbar
     return a, b, int((~ok).sum())
+
+
+def fit_scale_only(x, y, degenerate_rel: float = 1e-30):
+    """Variant V3, the uncentered fit: per channel min over a of sum_i (a x_ic - y_ic)^2.
+
+    [paper page] Table 3(a) lists "Linear, uncentered fit" between no fit and
+    the centred fit; read here as the least-squares map through the origin:
+        a = sum x y / sum x^2,  b = 0.
+    A channel with sum x^2 <= degenerate_rel * M gets a = 0. Returns
+    (a, b, n_degenerate) like fit_affine.
+    """
+    x, y = _f64(x), _f64(y)
+    m = x.shape[0]
+    if m == 0:
+        raise ValueError("fit needs at least one sample")
+    sxx = (x * x).sum(axis=0)
+    sxy = (x * y).sum(axis=0)
+    ok = sxx > degenerate_rel * m
+    a = np.where(ok, sxy / np.where(ok, sxx, 1.0), 0.0)
+    return a, np.zeros_like(a), int((~ok).sum())
 
 
 # ----------------------------------------------------------------------------

@@ -378,6 +378,86 @@ def pin_retained_and_top_mass():
     _close(best, brute, 1e-15, "top-3 mass by brute force")
 
 
+# ----------------------------------------------------------------------------
+# operator variants (the pages' ablation rows)
+# ----------------------------------------------------------------------------
+
+def pin_no_landmarks_is_attention_over_kept_tokens():
+    """Without landmarks a query tile attends to exactly its kept tiles' tokens:
+    torch's scaled-dot-product attention over those tokens alone."""
+    q, k, v = _qkv(45, 1, 9, 23, 8)
+    bounds = [(0, 5), (5, 10), (10, 15), (15, 20), (20, 23)]  # tiles of 5, last of 3
+    for kept in ([1], [0, 4], [2, 3, 4], [0, 1, 2, 3, 4]):
+        idx = np.concatenate([np.arange(*bounds[j]) for j in kept])
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[0])[None], torch.from_numpy(k[0][idx])[None],
+            torch.from_numpy(v[0][idx])[None], scale=0.4)[0].numpy()
+        got = zo.tile_sparse_attention_tile(q[0], k[0], v[0], 5, kept, 0.4, landmarks=False)
+        _close(got, ref, 1e-13, f"no landmarks kept={kept}")
+    out, _ = zo.tile_sparse_attention(q, k, v, 3, 5, 5, 0.4, landmarks=False)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), scale=0.4).numpy()
+    _close(out, ref, 1e-13, "no landmarks, every tile kept")
+
+
+def pin_log_count_constant_tiles_is_dense():
+    """Key tiles of one repeated key/value, ragged last tile: a landmark weighted by
+    its tile's token count stands in exactly for the tile, so every selection gives
+    dense attention (torch's scaled-dot-product attention)."""
+    rng = np.random.default_rng(46)
+    bk, nk, d, sc = 4, 14, 6, 0.6  # tiles of 4, 4, 4, 2 tokens
+    t_k = -(-nk // bk)
+    k = np.repeat(rng.standard_normal((t_k, d)), bk, axis=0)[:nk]
+    v = np.repeat(rng.standard_normal((t_k, 3)), bk, axis=0)[:nk]
+    q = rng.standard_normal((5, d))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        scale=sc)[0].numpy()
+    for kept in ([0, 2], [3], [1], [0, 1, 2, 3]):
+        got = zo.tile_sparse_attention_tile(q, k, v, bk, kept, sc, landmark_log_count=True)
+        _close(got, ref, 1e-12, f"log-count landmarks, constant tiles, kept={kept}")
+    # and without the count the omitted tiles are under-weighted: the plain reading differs
+    plain = zo.tile_sparse_attention_tile(q, k, v, bk, [3], sc)
+    assert np.max(np.abs(plain - ref)) > 1e-3, "plain landmarks should not equal dense here"
+
+
+def pin_log_count_unit_tiles_by_hand():
+    """A landmark of a 1-token tile counts once: one query by hand over two
+    kept tokens and one omitted 3-token tile with weight 3 e^l."""
+    rng = np.random.default_rng(47)
+    q = rng.standard_normal((1, 4))
+    k = rng.standard_normal((5, 4))
+    v = rng.standard_normal((5, 2))
+    sc = 0.7
+    # tiles of 2 tokens: {0,1} kept, {2,3} omitted (n = 2), {4} omitted (n = 1)
+    cols = [(k[0], v[0], 1.0), (k[1], v[1], 1.0), (0.5 * (k[2] + k[3]), 0.5 * (v[2] + v[3]), 2.0),
+            (k[4], v[4], 1.0)]
+    w = [n * math.exp(sc * math.fsum(float(a) * float(b) for a, b in zip(q[0], ck)))
+         for ck, _, n in cols]
+    expect = sum(wi * cv for wi, (_, cv, _) in zip(w, cols)) / sum(w)
+    got = zo.tile_sparse_attention_tile(q, k, v, 2, [0], sc, landmark_log_count=True)
+    _close(got[0], expect, 1e-13, "log-count landmark by hand")
+
+
+def pin_scale_only_fit_vs_lstsq():
+    """The uncentered fit equals numpy's least squares on the single column x; it
+    recovers y = alpha x exactly; a zero channel gets a = 0."""
+    rng = np.random.default_rng(48)
+    x = rng.standard_normal((40, 5))
+    y = 0.7 * x + rng.standard_normal((40, 5)) * 0.3 + 0.2
+    a, b, n_deg = zo.fit_scale_only(x, y)
+    assert n_deg == 0 and np.all(b == 0.0)
+    for c in range(5):
+        sol = np.linalg.lstsq(x[:, c:c + 1], y[:, c], rcond=None)[0]
+        _close([a[c]], sol, 1e-12, f"scale-only fit vs lstsq c={c}")
+    a, b, _ = zo.fit_scale_only(x, -2.25 * x)
+    _close(a, [-2.25] * 5, 1e-12, "recover scale through the origin")
+    xz = x.copy()
+    xz[:, 2] = 0.0
+    a, b, n_deg = zo.fit_scale_only(xz, y)
+    assert n_deg == 1 and a[2] == 0.0, "degenerate channel"
+
+
 ALL_PINS = [
     pin_pool_exact_rational, pin_select_brute_force, pin_select_tiles_orientation,
     pin_dense_vs_sdpa, pin_dense_closed_forms, pin_keep_all_equals_dense,
@@ -387,5 +467,7 @@ ALL_PINS = [
     pin_linear_closed_forms, pin_fit_vs_lstsq, pin_fit_exact_and_degenerate,
     pin_mean_sparsity_pages, pin_block_mass_tile_one_is_softmax,
     pin_block_mass_rows_sum_to_one_and_by_hand, pin_block_mass_constant_keys,
-    pin_retained_and_top_mass,
+    pin_retained_and_top_mass, pin_no_landmarks_is_attention_over_kept_tokens,
+    pin_log_count_constant_tiles_is_dense, pin_log_count_unit_tiles_by_hand,
+    pin_scale_only_fit_vs_lstsq,
 ]

@@ -36,31 +36,36 @@ def _scores_transposed(qbar, kbar):
     return np.asarray(kbar, np.float64) @ np.asarray(qbar, np.float64).T
 
 
-def _columns_with(kept_bias=False, landmarks_for_all=False, drop_landmarks=False):
-    def cols(k, v, k_tile, kept):
+def _columns_with(kept_bias=False, landmarks_for_all=False, drop_landmarks=False,
+                  ignore_switch=False, count_base2=False, count_full_tiles=False):
+    def cols(k, v, k_tile, kept, landmarks=True, landmark_log_count=False):
         k = np.asarray(k, np.float64)
         v = np.asarray(v, np.float64)
         bounds = zo.tile_bounds(k.shape[0], k_tile)
         kbar, vbar = zo.pool_tiles(k, k_tile), zo.pool_tiles(v, k_tile)
-        keys, vals = [], []
+        keys, vals, bias = [], [], []
         for j in sorted(int(t) for t in kept):
             s, e = bounds[j]
             keys.append(k[s:e])
             vals.append(v[s:e])
+            bias.append(np.zeros(e - s))
         for j in range(len(bounds)):
-            if drop_landmarks:
+            if drop_landmarks or not (landmarks or ignore_switch):
                 continue
             if landmarks_for_all or j not in set(int(t) for t in kept):
                 n = bounds[j][1] - bounds[j][0]
                 rep = n if kept_bias else 1  # a landmark counted n_j times
                 keys.append(np.repeat(kbar[j:j + 1], rep, axis=0))
                 vals.append(np.repeat(vbar[j:j + 1], rep, axis=0))
-        return np.concatenate(keys), np.concatenate(vals)
+                cnt = k_tile if count_full_tiles else n
+                lg = (np.log2(cnt) if count_base2 else np.log(cnt)) if landmark_log_count else 0.0
+                bias.append(np.full(rep, lg))
+        return np.concatenate(keys), np.concatenate(vals), np.concatenate(bias)
     return cols
 
 
-def _sparse_tile_no_scale(q_rows, k, v, k_tile, kept, scale):
-    return _orig["tile_sparse_attention_tile"](q_rows, k, v, k_tile, kept, 1.0)
+def _sparse_tile_no_scale(q_rows, k, v, k_tile, kept, scale, *variant):
+    return _orig["tile_sparse_attention_tile"](q_rows, k, v, k_tile, kept, 1.0, *variant)
 
 
 def _dense_wrong_axis(q, k, v, scale, row_block=1024):
@@ -126,6 +131,17 @@ def _mass_with(divide_by_k_tile=False, no_mean=False, skip_last_tile=False):
     return mass
 
 
+def _scale_fit_centred(x, y, degenerate_rel=1e-30):
+    x, y = np.asarray(x, np.float64), np.asarray(y, np.float64)
+    dx, dy = x - x.mean(axis=0), y - y.mean(axis=0)
+    return (dx * dy).sum(axis=0) / (dx * dx).sum(axis=0), np.zeros(x.shape[1]), 0
+
+
+def _scale_fit_keeps_intercept(x, y, degenerate_rel=1e-30):
+    a, b, n = _orig["fit_affine"](x, y, degenerate_rel)
+    return a, b, n
+
+
 def _top_mass_lowest(mass, top_k):
     m = np.asarray(mass, np.float64)
     return np.sort(m, axis=1)[:, :top_k].sum(axis=1)
@@ -152,6 +168,12 @@ MUTATIONS = {
     "block mass drops the last key tile": ("block_attention_mass",
                                            _mass_with(skip_last_tile=True)),
     "top mass takes the lowest blocks": ("top_mass", _top_mass_lowest),
+    "landmark switch ignored": ("attention_columns", _columns_with(ignore_switch=True)),
+    "landmark count in base 2": ("attention_columns", _columns_with(count_base2=True)),
+    "landmark count ignores the short last tile": ("attention_columns",
+                                                   _columns_with(count_full_tiles=True)),
+    "uncentered fit centred": ("fit_scale_only", _scale_fit_centred),
+    "uncentered fit keeps an intercept": ("fit_scale_only", _scale_fit_keeps_intercept),
 }
 
 
