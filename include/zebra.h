@@ -143,6 +143,28 @@ zebra_status zebra_tile_sparse_attn(const void* q, zebra_seq qs, const void* k, 
                                     size_t workspace_bytes, void* stream);
 
 /*
+ * Variants of the sparse operator from the pages' ablations (Zebra3D paper
+ * page, Table 3(b); appendix Tables 15-17 compare block/tile sparse attention
+ * with and without landmarks). flags = 0 is zebra_tile_sparse_attn.
+ *   ZEBRA_SPARSE_NO_LANDMARKS       omitted tiles are dropped: softmax over the
+ *                                   kept tiles' tokens only; kbar and vbar are
+ *                                   not read and may be NULL.
+ *   ZEBRA_SPARSE_LANDMARK_LOG_COUNT a landmark stands for the n_j valid tokens
+ *                                   of its tile: its logit gains ln(n_j).
+ * The two flags are exclusive (ZEBRA_ERR_INVALID_ARG). Everything else,
+ * including the workspace size, is as for zebra_tile_sparse_attn. With
+ * top_k == t_k (dense attention) the flags have no effect.
+ */
+#define ZEBRA_SPARSE_NO_LANDMARKS 1u
+#define ZEBRA_SPARSE_LANDMARK_LOG_COUNT 2u
+zebra_status zebra_tile_sparse_attn_ex(const void* q, zebra_seq qs, const void* k, const void* v,
+                                       zebra_seq kvs, const float* kbar, const float* vbar,
+                                       const int32_t* sel, int32_t q_tile, int32_t k_tile,
+                                       int32_t top_k, float scale, void* o, zebra_seq os,
+                                       zebra_dtype o_dtype, uint32_t flags, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/*
  * Linear attention plus affine map. Tolerant stages run linear(-centered)
  * attention (Zebra3D paper page, Abstract; Table 3(a) "Linear-centered +
  * fit"). With phi(x) = elu(x) + 1 per channel:
@@ -178,6 +200,18 @@ zebra_status zebra_linear_attn(const void* q, zebra_seq qs, const void* k, const
 zebra_status zebra_fit_affine(const float* x, const float* y, int32_t m, int32_t n_heads,
                               int32_t head_dim, float* scale_out, float* bias_out,
                               int32_t* n_degenerate_out, void* stream);
+
+/*
+ * Uncentered fit, the variant the Zebra3D paper page's Table 3(a) lists as
+ * "Linear, uncentered fit": per (head h, channel c) the least-squares map
+ * through the origin, min sum (a x - y)^2:
+ *   a = sum x y / sum x^2,  b = 0.
+ * A channel with sum x^2 <= 1e-30 * m gets a = 0. Arguments, layouts and
+ * errors as zebra_fit_affine (bias_out is written with zeros).
+ */
+zebra_status zebra_fit_scale_only(const float* x, const float* y, int32_t m, int32_t n_heads,
+                                  int32_t head_dim, float* scale_out, float* bias_out,
+                                  int32_t* n_degenerate_out, void* stream);
 
 /*
  * Selection-quality diagnostic: attention mass of every (query tile, key

@@ -24,11 +24,12 @@ HEAD_DIM = 64
 
 ZEBRA_OK, ZEBRA_ERR_INVALID_ARG, ZEBRA_ERR_UNSUPPORTED, ZEBRA_ERR_WORKSPACE, ZEBRA_ERR_HIP = range(5)
 ZEBRA_BF16, ZEBRA_F32 = 0, 1
+ZEBRA_SPARSE_NO_LANDMARKS, ZEBRA_SPARSE_LANDMARK_LOG_COUNT = 1, 2
 
 ENTRY_POINTS = (
     "zebra_pool_landmarks", "zebra_select_tiles_workspace", "zebra_select_tiles",
-    "zebra_tile_sparse_attn_workspace", "zebra_tile_sparse_attn",
-    "zebra_linear_attn_workspace", "zebra_linear_attn", "zebra_fit_affine",
+    "zebra_tile_sparse_attn_workspace", "zebra_tile_sparse_attn", "zebra_tile_sparse_attn_ex",
+    "zebra_linear_attn_workspace", "zebra_linear_attn", "zebra_fit_affine", "zebra_fit_scale_only",
     "zebra_block_mass_workspace", "zebra_block_mass", "zebra_status_string", "zebra_version",
 )
 
@@ -67,10 +68,14 @@ def _declare(lib):
         "zebra_tile_sparse_attn": (c_i32, [c_p, ZebraSeq, c_p, c_p, ZebraSeq, c_p, c_p, c_p,
                                            c_i32, c_i32, c_i32, c_f, c_p, ZebraSeq, c_i32, c_p,
                                            c_sz, c_p]),
+        "zebra_tile_sparse_attn_ex": (c_i32, [c_p, ZebraSeq, c_p, c_p, ZebraSeq, c_p, c_p, c_p,
+                                              c_i32, c_i32, c_i32, c_f, c_p, ZebraSeq, c_i32,
+                                              ctypes.c_uint32, c_p, c_sz, c_p]),
         "zebra_linear_attn_workspace": (c_sz, [c_i64, c_i32, c_i32]),
         "zebra_linear_attn": (c_i32, [c_p, ZebraSeq, c_p, c_p, ZebraSeq, c_p, c_p, c_p, ZebraSeq,
                                       c_i32, c_p, c_sz, c_p]),
         "zebra_fit_affine": (c_i32, [c_p, c_p, c_i32, c_i32, c_i32, c_p, c_p, c_p, c_p]),
+        "zebra_fit_scale_only": (c_i32, [c_p, c_p, c_i32, c_i32, c_i32, c_p, c_p, c_p, c_p]),
         "zebra_block_mass_workspace": (c_sz, [c_i64, c_i32]),
         "zebra_block_mass": (c_i32, [c_p, ZebraSeq, c_p, ZebraSeq, c_i32, c_i32, c_f, c_p, c_p,
                                      c_sz, c_p]),
@@ -194,6 +199,18 @@ def zebra_tile_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                            out_dtype=torch.bfloat16,
                            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Tile-sparse softmax attention with mean-key/value landmarks (sel=None: dense)."""
+    return zebra_tile_sparse_attn_ex(q, k, v, kbar, vbar, sel, q_tile, k_tile, top_k, scale, 0,
+                                     out, out_dtype, workspace)
+
+
+def zebra_tile_sparse_attn_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                              kbar: Optional[torch.Tensor], vbar: Optional[torch.Tensor],
+                              sel: Optional[torch.Tensor], q_tile: int, k_tile: int, top_k: int,
+                              scale: float, flags: int, out: Optional[torch.Tensor] = None,
+                              out_dtype=torch.bfloat16,
+                              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Sparse-operator variants: flags ZEBRA_SPARSE_NO_LANDMARKS (kbar, vbar may be
+    None) or ZEBRA_SPARSE_LANDMARK_LOG_COUNT; 0 is zebra_tile_sparse_attn."""
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, torch.bfloat16, name)
     if k.shape != v.shape or k.stride() != v.stride():
@@ -204,18 +221,21 @@ def zebra_tile_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise ValueError("out must be bfloat16 or float32")
     if sel is not None:
         _need(sel, torch.int32, "sel")
-        _need(kbar, torch.float32, "kbar")
-        _need(vbar, torch.float32, "vbar")
-        if not (sel.is_contiguous() and kbar.is_contiguous() and vbar.is_contiguous()):
-            raise ValueError("sel, kbar and vbar must be contiguous")
+        if not sel.is_contiguous():
+            raise ValueError("sel must be contiguous")
+        for t, name in ((kbar, "kbar"), (vbar, "vbar")):
+            if t is not None or not flags & ZEBRA_SPARSE_NO_LANDMARKS:
+                _need(t, torch.float32, name)
+                if not t.is_contiguous():
+                    raise ValueError(f"{name} must be contiguous")
     lib = library()
     nbytes = lib.zebra_tile_sparse_attn_workspace(q.shape[1], k.shape[1], k.shape[0], HEAD_DIM,
                                                   q_tile, k_tile, top_k)
     workspace = _workspace(nbytes, q.device, workspace)
-    _check("zebra_tile_sparse_attn", lib.zebra_tile_sparse_attn(
+    _check("zebra_tile_sparse_attn_ex", lib.zebra_tile_sparse_attn_ex(
         _ptr(q), seq_of(q), _ptr(k), _ptr(v), seq_of(k), _ptr(kbar), _ptr(vbar), _ptr(sel),
         q_tile, k_tile, top_k, scale, _ptr(out), seq_of(out),
-        ZEBRA_F32 if out.dtype == torch.float32 else ZEBRA_BF16, _ptr(workspace), nbytes,
+        ZEBRA_F32 if out.dtype == torch.float32 else ZEBRA_BF16, flags, _ptr(workspace), nbytes,
         _stream(q.device)))
     return out
 
@@ -251,6 +271,18 @@ def zebra_fit_affine(x: torch.Tensor, y: torch.Tensor, scale_out: Optional[torch
                      bias_out: Optional[torch.Tensor] = None,
                      n_degenerate: Optional[torch.Tensor] = None):
     """Closed-form least-squares a, b per (head, channel) from x, y float32 [H][M][64]."""
+    return _fit("zebra_fit_affine", x, y, scale_out, bias_out, n_degenerate)
+
+
+def zebra_fit_scale_only(x: torch.Tensor, y: torch.Tensor,
+                         scale_out: Optional[torch.Tensor] = None,
+                         bias_out: Optional[torch.Tensor] = None,
+                         n_degenerate: Optional[torch.Tensor] = None):
+    """Uncentered fit: a = sum x y / sum x^2, b = 0 per (head, channel)."""
+    return _fit("zebra_fit_scale_only", x, y, scale_out, bias_out, n_degenerate)
+
+
+def _fit(entry, x, y, scale_out, bias_out, n_degenerate):
     _need(x, torch.float32, "x")
     _need(y, torch.float32, "y")
     if x.shape != y.shape or not (x.is_contiguous() and y.is_contiguous()):
@@ -262,7 +294,7 @@ def zebra_fit_affine(x: torch.Tensor, y: torch.Tensor, scale_out: Optional[torch
         bias_out = torch.empty((h, HEAD_DIM), dtype=torch.float32, device=x.device)
     if n_degenerate is None:
         n_degenerate = torch.empty(1, dtype=torch.int32, device=x.device)
-    _check("zebra_fit_affine", library().zebra_fit_affine(
+    _check(entry, getattr(library(), entry)(
         _ptr(x), _ptr(y), m, h, x.shape[2], _ptr(scale_out), _ptr(bias_out), _ptr(n_degenerate),
         _stream(x.device)))
     return scale_out, bias_out, n_degenerate

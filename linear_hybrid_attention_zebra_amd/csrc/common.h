@@ -72,12 +72,15 @@ hipError_t launch_select(const float* qbar, const float* kbar, int32_t heads, in
                          hipStream_t s);
 size_t sparse_workspace_bytes(int64_t n_q, int64_t n_kv, int32_t heads, int32_t q_tile,
                               int32_t k_tile, int32_t top_k);
+// launch_tile_sparse flags (the same bits as the ABI's ZEBRA_SPARSE_*)
+constexpr uint32_t kSparseNoLandmarks = 1u;
+constexpr uint32_t kSparseLandmarkLogCount = 2u;
 hipError_t launch_tile_sparse(const uint16_t* q, int64_t nq, int64_t qst, int64_t qsh,
                               const uint16_t* k, const uint16_t* v, int64_t nk, int64_t kst,
                               int64_t ksh, int32_t heads, const float* kbar, const float* vbar,
                               const int32_t* sel, int32_t q_tile, int32_t k_tile,
                               int32_t top_k, float scale, void* o, int64_t ost, int64_t osh,
-                              bool o_f32, void* ws, hipStream_t s);
+                              bool o_f32, uint32_t flags, void* ws, hipStream_t s);
 size_t linear_workspace_bytes(int64_t n_kv, int32_t heads);
 hipError_t launch_linear(const uint16_t* q, int64_t nq, int64_t qst, int64_t qsh,
                          const uint16_t* k, const uint16_t* v, int64_t nk, int64_t kst,
@@ -90,5 +93,5 @@ hipError_t launch_block_mass(const uint16_t* q, int64_t nq, int64_t qst, int64_t
                              int32_t heads, int32_t q_tile, int32_t k_tile, float scale,
                              float* mass, void* ws, hipStream_t s);
 hipError_t launch_fit(const float* x, const float* y, int32_t m, int32_t heads, float* a,
-                      float* b, int32_t* n_deg, hipStream_t s);
+                      float* b, int32_t* n_deg, bool centred, hipStream_t s);
 }  // namespace zebra

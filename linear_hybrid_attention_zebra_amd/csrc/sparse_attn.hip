@@ -48,6 +48,12 @@
 // with lazy rescaling (the maximum moves only when a block's maximum exceeds
 // it by more than 8 in log2 units).
 //
+// Variants (the pages' sparse-attention ablations): without landmarks the
+// item walks its kept tiles only; with the landmark log count a landmark
+// stands for the n_j valid tokens of its tile, i.e. its probability gains a
+// factor n_j (2^log2(n_j) in the exponent). The fast path then lowers every
+// probability by KT so that the landmarks' stay below 2^60.
+//
 // Pipeline. K and V blocks go global -> LDS directly
 // (global_load_lds_dwordx4) into two-stage rings, the K ring one block ahead
 // of the V ring: step t issues K(t+2) and V(t+1), then computes QK(t+1),
@@ -91,6 +97,10 @@ struct SparseParams {
   int32_t tq, tk, top_k;
   float scale_log2;        // softmax scale * log2(e), > 0
   int32_t o_f32;
+  int32_t landmarks;       // 0: omitted tiles are dropped (no landmark columns)
+  int32_t log_count;       // landmark logits gain log2(n_j) (log2 units)
+  float lm_log2_kt;        // log2(KT)
+  float lm_tail_corr;      // (log2(n of tile tk-1) - log2(KT)) / c, score units
   // split keys (n_chunks > 1): chunk c covers key tiles [c CT, (c + 1) CT)
   int32_t n_chunks, chunk_tiles;
   const int32_t* coff;     // [H][tq][n_chunks + 1]: first kept entry of each chunk
@@ -226,10 +236,12 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
   const int qi = lane & 31;  // query within the wave / column of S^T
   const int hh = lane >> 5;  // lane half
   const bool dense = sel == nullptr;
-  const int n_lb_all = dense ? 0 : (p.tk + KT - 1) / KT;  // landmark blocks of a head
+  const int n_lb_all = dense || !p.landmarks ? 0 : (p.tk + KT - 1) / KT;  // landmark blocks
   const int tail_rows = (int)(p.nk - (int64_t)(p.tk - 1) * KT);  // rows of tile tk-1
   const int last_lrows = p.tk - (n_lb_all - 1) * KT;  // landmark rows in the last block
   const float c = p.scale_log2;
+  const bool log_count = p.log_count != 0;
+  const float lm_shift = log_count ? p.lm_log2_kt : 0.f;  // landmark columns, log2 units
   const int n_ch = p.n_chunks;
   const int lb_per_chunk = p.chunk_tiles / KT;
   const int64_t items_per_head = (int64_t)n_ch * p.tq;
@@ -261,22 +273,25 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
       kept0 = __builtin_amdgcn_readfirstlane(co[0]);
       n_kept = max(__builtin_amdgcn_readfirstlane(co[1]) - kept0, 0);
       lb0 = ch * lb_per_chunk;
-      n_lb = min(lb_per_chunk, n_lb_all - lb0);
+      n_lb = n_lb_all > 0 ? min(lb_per_chunk, n_lb_all - lb0) : 0;
     }
     const int n_total = n_kept + n_lb;
     const int32_t* sel_row = dense ? nullptr : sel + row * p.top_k + kept0;
     const uint8_t* kh = (const uint8_t*)(p.k + (int64_t)h * p.ksh);
     const uint8_t* vh = (const uint8_t*)(p.v + (int64_t)h * p.ksh);
+    const bool has_lm = n_lb_all > 0;
     const uint8_t* klm =
-        dense ? nullptr : (const uint8_t*)(p.kbar_b + (int64_t)h * p.tk * kHeadDim);
+        has_lm ? (const uint8_t*)(p.kbar_b + (int64_t)h * p.tk * kHeadDim) : nullptr;
     const uint8_t* vlm =
-        dense ? nullptr : (const uint8_t*)(p.vbar_b + (int64_t)h * p.tk * kHeadDim);
+        has_lm ? (const uint8_t*)(p.vbar_b + (int64_t)h * p.tk * kHeadDim) : nullptr;
 
     lds_barrier();  // every wave is done with the previous item's LDS
     if (tid == 0) slow_item = 0;
-    if (!dense) {
+    if (n_lb > 0) {
       const int words = NB * n_lb;  // every word the item's landmark blocks read
       for (int e = tid; e < words; e += NT) kept_bits[NB * lb0 + e] = 0u;
+    }
+    if (!dense) {
       const int nw = min(kWin, n_kept);
       for (int e = tid; e < nw; e += NT) win[e] = (uint16_t)min(max(sel_row[e], 0), p.tk - 1);
     }
@@ -300,7 +315,7 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
     const int last_kept =
         dense ? p.tk - 1 : (n_kept > 0 ? min(max(sel_row[n_kept - 1], 0), p.tk - 1) : -1);
     __syncthreads();  // also completes every vector load above
-    if (!dense)
+    if (n_lb > 0)
       for (int e = tid; e < n_kept; e += NT) {
         const int j = min(max(sel_row[e], 0), p.tk - 1);
         atomicOr(&kept_bits[j >> 5], 1u << (j & 31));
@@ -428,7 +443,7 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
     const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
     float l_run = 0.f;
     float mc_run = -INFINITY;  // fallback: running maximum in log2 units
-    const float nm_fast = kPShift - m_q;
+    const float nm_fast = kPShift - m_q - lm_shift;
     // lane holds keys 32b + 8g + 4hh + r in register 4g + r of score block b.
     // colmask is uniform: per register, the excluded lanes form a 64-bit lane
     // mask built with scalar ops, applied by one v_cndmask.
@@ -487,6 +502,22 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
       return -mc_run;
     };
 
+    // variant V2: the landmark of the short last key tile counts its tail_rows
+    // tokens, not KT: add corr to the score of column col (uniform) of the block,
+    // with the same uniform lane masks as apply_mask
+    auto add_col = [&](f32x16 (&sacc)[NB], int col, float corr) {
+      const uint64_t m0 = 1ull << col, m1 = m0 >> 4;  // lane halves 0 and 1
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int bit = 32 * b + 8 * (i >> 2) + (i & 3);
+          const uint64_t lanes = (((m0 >> bit) & 1ull) ? 0x00000000ffffffffull : 0ull) |
+                                 (((m1 >> bit) & 1ull) ? 0xffffffff00000000ull : 0ull);
+          if (__builtin_amdgcn_inverse_ballot_w64(lanes)) sacc[b][i] += corr;
+        }
+    };
+
     f32x16 sa0[NB], sa1[NB];
     auto sbuf = [&](auto par) -> f32x16(&)[NB] {
       if constexpr (decltype(par)::value == 0) return sa0;
@@ -503,14 +534,18 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
       // QK(t+1), softmax(t), PV(t) as one basic block: the scheduler can then
       // interleave the score MFMAs of the next block with this block's
       // softmax arithmetic (the groups below ask for that order).
-      auto body = [&](auto par, auto masked_c, uint64_t cmask) {
+      auto body = [&](auto par, auto masked_c, uint64_t cmask, float nm_add, int tail_col) {
         constexpr bool kMasked = decltype(masked_c)::value;
         using Q = std::integral_constant<int, 1 - decltype(par)::value>;
         f32x16(&cur)[NB] = sbuf(par);
+        if constexpr (kMasked) {
+          if (tail_col >= 0) add_col(cur, tail_col, p.lm_tail_corr);
+        }
         qk(Q{}, sbuf(Q{}));  // QK(t+1); past the end it reads a repeated block
         if constexpr (kMasked) apply_mask(cur, cmask);
         float nm = nm_fast;
         if constexpr (!kFast) nm = online_ref(cur);
+        if constexpr (kMasked) nm += nm_add;  // landmark blocks: log2(KT) under V2
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           bf16x8 lo8, hi8;
@@ -555,10 +590,15 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
         issue(tvn, vh, vlm, vbuf(Q{}));
         if (t == -1) qk(Q{}, sbuf(Q{}));
         if (t < 0) return;
-        if constexpr (decltype(masked_c)::value)
-          body(par, masked_c, block_mask(t));
-        else
-          body(par, masked_c, 0ull);
+        if constexpr (decltype(masked_c)::value) {
+          const bool lm = t >= n_kept;
+          const int tcol = lm && log_count && lb0 + t - n_kept == n_lb_all - 1 && tail_rows < KT
+                               ? last_lrows - 1
+                               : -1;
+          body(par, masked_c, block_mask(t), lm ? lm_shift : 0.f, tcol);
+        } else {
+          body(par, masked_c, 0ull, 0.f, -1);
+        }
       };
       using Plain = std::false_type;
       using Masked = std::true_type;
@@ -580,10 +620,12 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
       if (t < n_total) step(t, P0{}, Masked{});
       wait_vmcnt<0>();  // no direct-to-LDS load may outlive the item
     };
-    if (fast)
-      run(std::true_type{});
-    else
-      run(std::false_type{});
+    if (n_total > 0) {  // an item may have no columns: split keys without landmarks
+      if (fast)
+        run(std::true_type{});
+      else
+        run(std::false_type{});
+    }
 
     // ---- epilogue: O / l, lane (qi, hh) holds channels 32db + 8g + 4hh + r
     const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
@@ -599,7 +641,7 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
           for (int g = 0; g < 4; ++g)
             *(f32x4*)(op + 32 * db + 8 * g) = f32x4{oacc[db][4 * g], oacc[db][4 * g + 1],
                                                     oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
-        if (hh == 0) p.part_ml[prow] = float2{fast ? m_q - kPShift : mc_run, l_sum};
+        if (hh == 0) p.part_ml[prow] = float2{fast ? -nm_fast : mc_run, l_sum};
       }
       continue;
     }
@@ -674,20 +716,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if (r >= rows) return;
   const int sub = threadIdx.x & 15;
   const float2* ml = part_ml + r * n_chunks;
-  float ref = -INFINITY;
-  for (int ch = 0; ch < n_chunks; ++ch) ref = fmaxf(ref, ml[ch].x);
+  float ref = -INFINITY;  // over the chunks with columns (l > 0)
+  for (int ch = 0; ch < n_chunks; ++ch)
+    if (ml[ch].y > 0.f) ref = fmaxf(ref, ml[ch].x);
   const float* po = part_o + r * n_chunks * kHeadDim + 4 * sub;
   float l = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int ch = 0; ch < n_chunks; ++ch) {
     const float2 m = ml[ch];
-    const float w = __builtin_amdgcn_exp2f(m.x - ref);
+    const float w = m.y > 0.f ? __builtin_amdgcn_exp2f(m.x - ref) : 0.f;
     const f32x4 x = *(const f32x4*)(po + (int64_t)ch * kHeadDim);
     l = __builtin_fmaf(m.y, w, l);
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(x[i], w, acc[i]);
   }
-  const float inv = 1.0f / l;
+  const float inv = l > 0.f ? 1.0f / l : 0.f;  // l == 0 only without any column
   const int64_t h = r / nq, q = r - h * nq;
   if (o_f32) {
     float* op = (float*)o + h * osh + q * ost + 4 * sub;
@@ -777,7 +820,7 @@ hipError_t launch_tile_sparse(const uint16_t* q, int64_t nq, int64_t qst, int64_
                               int64_t ksh, int32_t heads, const float* kbar, const float* vbar,
                               const int32_t* sel, int32_t q_tile, int32_t k_tile,
                               int32_t top_k, float scale, void* o, int64_t ost, int64_t osh,
-                              bool o_f32, void* ws, hipStream_t s) {
+                              bool o_f32, uint32_t flags, void* ws, hipStream_t s) {
   SparseParams p;
   p.q = q;
   p.k = k;
@@ -804,13 +847,25 @@ hipError_t launch_tile_sparse(const uint16_t* q, int64_t nq, int64_t qst, int64_
   p.o_f32 = o_f32 ? 1 : 0;
   p.kbar_b = nullptr;
   p.vbar_b = nullptr;
+  p.landmarks = (flags & kSparseNoLandmarks) ? 0 : 1;
+  p.log_count = (flags & kSparseLandmarkLogCount) ? 1 : 0;
+  p.lm_log2_kt = __builtin_log2f((float)k_tile);
+  {
+    const int64_t tail = nk - (int64_t)(p.tk - 1) * k_tile;  // tokens of the last key tile
+    p.lm_tail_corr = tail > 0 ? (__builtin_log2f((float)tail) - p.lm_log2_kt) / (scale * kLog2e)
+                              : 0.f;
+  }
   if (p.tq == 0 || heads == 0) return hipSuccess;
   const bool sparse = sel != nullptr && top_k < p.tk;
   uint8_t* wsb = (uint8_t*)ws;
   if (sparse) {
     const size_t lm = align256((size_t)heads * p.tk * kHeadDim * sizeof(uint16_t));
-    uint16_t* kb = (uint16_t*)wsb;
-    uint16_t* vb = (uint16_t*)(wsb + lm);
+    wsb += 2 * lm;
+  }
+  if (sparse && p.landmarks) {
+    const size_t lm = align256((size_t)heads * p.tk * kHeadDim * sizeof(uint16_t));
+    uint16_t* kb = (uint16_t*)ws;
+    uint16_t* vb = (uint16_t*)((uint8_t*)ws + lm);
     const int64_t pairs = (int64_t)heads * p.tk * (kHeadDim / 2);
     const int blocks = (int)std::min<int64_t>((pairs + 255) / 256, 8192);
     hipLaunchKernelGGL(pack_landmarks_kernel, dim3(blocks), dim3(256), 0, s, kbar, vbar, pairs,
@@ -819,10 +874,8 @@ hipError_t launch_tile_sparse(const uint16_t* q, int64_t nq, int64_t qst, int64_
     if (err != hipSuccess) return err;
     p.kbar_b = kb;
     p.vbar_b = vb;
-    wsb += 2 * lm;
-  } else {
-    sel = nullptr;  // every tile kept: dense attention, no landmarks
   }
+  if (!sparse) sel = nullptr;  // every tile kept: dense attention, no landmarks
   float* range = (float*)wsb;
   hipLaunchKernelGGL(range_kernel, dim3(kRangeParts, heads), dim3(256), 0, s, k, v, nk, kst, ksh,
                      p.kbar_b, p.vbar_b, p.tk, range);

@@ -79,6 +79,9 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
 
+static_assert(zebra::kSparseNoLandmarks == ZEBRA_SPARSE_NO_LANDMARKS, "flag bits");
+static_assert(zebra::kSparseLandmarkLogCount == ZEBRA_SPARSE_LANDMARK_LOG_COUNT, "flag bits");
+
 extern "C" {
 
 const char* zebra_status_string(zebra_status status) {
@@ -162,7 +165,20 @@ zebra_status zebra_tile_sparse_attn(const void* q, zebra_seq qs, const void* k, 
                                     int32_t top_k, float scale, void* o, zebra_seq os,
                                     zebra_dtype o_dtype, void* workspace,
                                     size_t workspace_bytes, void* stream) {
+  return zebra_tile_sparse_attn_ex(q, qs, k, v, kvs, kbar, vbar, sel, q_tile, k_tile, top_k,
+                                   scale, o, os, o_dtype, 0u, workspace, workspace_bytes, stream);
+}
+
+zebra_status zebra_tile_sparse_attn_ex(const void* q, zebra_seq qs, const void* k, const void* v,
+                                       zebra_seq kvs, const float* kbar, const float* vbar,
+                                       const int32_t* sel, int32_t q_tile, int32_t k_tile,
+                                       int32_t top_k, float scale, void* o, zebra_seq os,
+                                       zebra_dtype o_dtype, uint32_t flags, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
   zebra_status st;
+  const uint32_t known = ZEBRA_SPARSE_NO_LANDMARKS | ZEBRA_SPARSE_LANDMARK_LOG_COUNT;
+  if ((flags & ~known) != 0u || flags == known) return ZEBRA_ERR_INVALID_ARG;
+  const bool landmarks = (flags & ZEBRA_SPARSE_NO_LANDMARKS) == 0u;
   if ((st = check_seq(q, qs, false)) != ZEBRA_OK) return st;
   if ((st = check_seq(k, kvs, false)) != ZEBRA_OK) return st;
   if ((st = check_seq(v, kvs, false)) != ZEBRA_OK) return st;
@@ -181,27 +197,28 @@ zebra_status zebra_tile_sparse_attn(const void* q, zebra_seq qs, const void* k, 
   if (tq * qs.n_heads > (int64_t)UINT32_MAX) return ZEBRA_ERR_UNSUPPORTED;
   if (top_k < 1 || top_k > tk) return ZEBRA_ERR_INVALID_ARG;
   const bool dense = top_k == tk;
-  if (!dense && (kbar == nullptr || vbar == nullptr || sel == nullptr))
-    return ZEBRA_ERR_INVALID_ARG;
+  const bool use_lm = !dense && landmarks;  // kbar and vbar are read
+  if (!dense && sel == nullptr) return ZEBRA_ERR_INVALID_ARG;
+  if (use_lm && (kbar == nullptr || vbar == nullptr)) return ZEBRA_ERR_INVALID_ARG;
   // the kernel addresses rows of one key tile with 32-bit byte offsets
   if (kvs.stride_token > (int64_t)1 << 24) return ZEBRA_ERR_UNSUPPORTED;
   const size_t need = zebra::sparse_workspace_bytes(qs.n_tokens, kvs.n_tokens, kvs.n_heads,
                                                     q_tile, k_tile, top_k);
   if (workspace == nullptr || workspace_bytes < need) return ZEBRA_ERR_WORKSPACE;
   if (((uintptr_t)workspace % 16) != 0) return ZEBRA_ERR_INVALID_ARG;
-  if (!dense && (((uintptr_t)kbar % 16) != 0 || ((uintptr_t)vbar % 16) != 0 ||
-                 ((uintptr_t)sel % 4) != 0))
+  if (use_lm && (((uintptr_t)kbar % 16) != 0 || ((uintptr_t)vbar % 16) != 0))
     return ZEBRA_ERR_INVALID_ARG;
+  if (!dense && ((uintptr_t)sel % 4) != 0) return ZEBRA_ERR_INVALID_ARG;
   const size_t oel = o_dtype == ZEBRA_F32 ? 4 : 2;
   if (o_dtype == ZEBRA_F32 && (os.stride_token % 8 != 0 || os.stride_head % 8 != 0))
     return ZEBRA_ERR_UNSUPPORTED;
   const Range orng = seq_range(o, os, oel);
   std::vector<Range> inputs = {seq_range(q, qs, 2), seq_range(k, kvs, 2), seq_range(v, kvs, 2)};
-  if (!dense) {
+  if (use_lm) {
     inputs.push_back(flat_range(kbar, (uint64_t)kvs.n_heads * tk * zebra::kHeadDim, 4));
     inputs.push_back(flat_range(vbar, (uint64_t)kvs.n_heads * tk * zebra::kHeadDim, 4));
-    inputs.push_back(flat_range(sel, (uint64_t)kvs.n_heads * tq * top_k, 4));
   }
+  if (!dense) inputs.push_back(flat_range(sel, (uint64_t)kvs.n_heads * tq * top_k, 4));
   const Range ws = flat_range(workspace, need, 1);
   if (overlaps(ws, orng)) return ZEBRA_ERR_INVALID_ARG;
   for (const Range& r : inputs)
@@ -211,9 +228,9 @@ zebra_status zebra_tile_sparse_attn(const void* q, zebra_seq qs, const void* k, 
   return hip_status(zebra::launch_tile_sparse(
       (const uint16_t*)q, qs.n_tokens, qs.stride_token, qs.stride_head, (const uint16_t*)k,
       (const uint16_t*)v, kvs.n_tokens, kvs.stride_token, kvs.stride_head, qs.n_heads,
-      dense ? nullptr : kbar, dense ? nullptr : vbar, dense ? nullptr : sel, q_tile, k_tile,
-      top_k, scale, o, os.stride_token, os.stride_head, o_dtype == ZEBRA_F32, workspace,
-      (hipStream_t)stream));
+      use_lm ? kbar : nullptr, use_lm ? vbar : nullptr, dense ? nullptr : sel, q_tile, k_tile,
+      top_k, scale, o, os.stride_token, os.stride_head, o_dtype == ZEBRA_F32,
+      dense ? 0u : flags, workspace, (hipStream_t)stream));
 }
 
 size_t zebra_block_mass_workspace(int64_t n_q, int32_t n_heads) {
@@ -294,9 +311,11 @@ zebra_status zebra_linear_attn(const void* q, zebra_seq qs, const void* k, const
       (hipStream_t)stream));
 }
 
-zebra_status zebra_fit_affine(const float* x, const float* y, int32_t m, int32_t n_heads,
-                              int32_t head_dim, float* scale_out, float* bias_out,
-                              int32_t* n_degenerate_out, void* stream) {
+namespace {
+
+zebra_status fit_common(const float* x, const float* y, int32_t m, int32_t n_heads,
+                        int32_t head_dim, float* scale_out, float* bias_out,
+                        int32_t* n_degenerate_out, bool centred, void* stream) {
   if (m < 1 || n_heads < 0) return ZEBRA_ERR_INVALID_ARG;
   if (head_dim != zebra::kHeadDim) return ZEBRA_ERR_UNSUPPORTED;
   if (x == nullptr || y == nullptr || scale_out == nullptr || bias_out == nullptr)
@@ -313,7 +332,23 @@ zebra_status zebra_fit_affine(const float* x, const float* y, int32_t m, int32_t
     if (overlaps(o, xr) || overlaps(o, yr)) return ZEBRA_ERR_INVALID_ARG;
   if (overlaps(ar, br) || overlaps(ar, dr) || overlaps(br, dr)) return ZEBRA_ERR_INVALID_ARG;
   return hip_status(zebra::launch_fit(x, y, m, n_heads, scale_out, bias_out, n_degenerate_out,
-                                      (hipStream_t)stream));
+                                      centred, (hipStream_t)stream));
+}
+
+}  // namespace
+
+zebra_status zebra_fit_affine(const float* x, const float* y, int32_t m, int32_t n_heads,
+                              int32_t head_dim, float* scale_out, float* bias_out,
+                              int32_t* n_degenerate_out, void* stream) {
+  return fit_common(x, y, m, n_heads, head_dim, scale_out, bias_out, n_degenerate_out, true,
+                    stream);
+}
+
+zebra_status zebra_fit_scale_only(const float* x, const float* y, int32_t m, int32_t n_heads,
+                                  int32_t head_dim, float* scale_out, float* bias_out,
+                                  int32_t* n_degenerate_out, void* stream) {
+  return fit_common(x, y, m, n_heads, head_dim, scale_out, bias_out, n_degenerate_out, false,
+                    stream);
 }
 
 }  // extern "C"

@@ -16,7 +16,7 @@ from typing import Optional
 import torch
 
 from . import (ceil_div, zebra_fit_affine, zebra_linear_attn, zebra_pool_landmarks,
-               zebra_select_tiles, zebra_tile_sparse_attn)
+               zebra_select_tiles, zebra_tile_sparse_attn, zebra_tile_sparse_attn_ex)
 
 
 @dataclasses.dataclass
@@ -52,8 +52,12 @@ class SparseBuffers:
 
 
 def sparse_stage(q, k, v, q_tile: int, k_tile: int, top_k: int, scale: float,
-                 bufs: Optional[SparseBuffers] = None) -> SparseBuffers:
-    """One tile-sparse stage; returns the buffers (out, sel, means) it filled."""
+                 bufs: Optional[SparseBuffers] = None, flags: int = 0) -> SparseBuffers:
+    """One tile-sparse stage; returns the buffers (out, sel, means) it filled.
+
+    flags selects an operator variant (ZEBRA_SPARSE_NO_LANDMARKS or
+    ZEBRA_SPARSE_LANDMARK_LOG_COUNT); 0 is the method's operator.
+    """
     if bufs is None:
         bufs = SparseBuffers.allocate(q.shape[0], q.shape[1], k.shape[1], q_tile, k_tile, top_k,
                                       q.device)
@@ -61,8 +65,8 @@ def sparse_stage(q, k, v, q_tile: int, k_tile: int, top_k: int, scale: float,
     zebra_pool_landmarks(k, k_tile, out=bufs.kbar)
     zebra_pool_landmarks(v, k_tile, out=bufs.vbar)
     zebra_select_tiles(bufs.qbar, bufs.kbar, top_k, out=bufs.sel, workspace=bufs.select_ws)
-    zebra_tile_sparse_attn(q, k, v, bufs.kbar, bufs.vbar, bufs.sel, q_tile, k_tile, top_k, scale,
-                           out=bufs.out, workspace=bufs.attn_ws)
+    zebra_tile_sparse_attn_ex(q, k, v, bufs.kbar, bufs.vbar, bufs.sel, q_tile, k_tile, top_k,
+                              scale, flags, out=bufs.out, workspace=bufs.attn_ws)
     return bufs
 
 

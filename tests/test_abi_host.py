@@ -31,7 +31,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     for name in names:
         assert hasattr(lib, name), f"{name} declared in zebra.h but not exported"
     assert set(names) == set(zb.ENTRY_POINTS)
@@ -106,6 +106,40 @@ def test_sparse_validation(lib):
     assert call(dtype=7) == zb.ZEBRA_ERR_INVALID_ARG
 
 
+def test_sparse_variant_flags_validation(lib):
+    f = lib.zebra_tile_sparse_attn_ex
+    s = seq(256)
+    ws = lib.zebra_tile_sparse_attn_workspace(256, 256, 2, 64, 64, 64, 2)
+
+    def call(flags, kbar=P(1 << 22), vbar=P(1 << 23), sel=P(1 << 24), ws_b=ws):
+        return f(P(1 << 16), s, P(1 << 18), P(1 << 20), s, kbar, vbar, sel, 64, 64, 2, 0.125,
+                 P(1 << 28), s, 0, flags, P(1 << 30), ws_b, None)
+
+    assert call(4) == zb.ZEBRA_ERR_INVALID_ARG  # unknown flag bit
+    assert call(zb.ZEBRA_SPARSE_NO_LANDMARKS | zb.ZEBRA_SPARSE_LANDMARK_LOG_COUNT) == \
+        zb.ZEBRA_ERR_INVALID_ARG  # a count needs landmarks
+    assert call(zb.ZEBRA_SPARSE_LANDMARK_LOG_COUNT, kbar=None) == zb.ZEBRA_ERR_INVALID_ARG
+    assert call(zb.ZEBRA_SPARSE_NO_LANDMARKS, sel=None) == zb.ZEBRA_ERR_INVALID_ARG
+    # without landmarks kbar/vbar are not read: the next check reached is the workspace
+    assert call(zb.ZEBRA_SPARSE_NO_LANDMARKS, kbar=None, vbar=None, ws_b=ws - 1) == \
+        zb.ZEBRA_ERR_WORKSPACE
+    assert call(0, ws_b=ws - 1) == zb.ZEBRA_ERR_WORKSPACE
+
+
+def test_split_key_workspace_sizes(lib):
+    """Long key ranges with q_tile <= 64 add float32 partials (264 B per query and
+    chunk of 32,768 keys) to the workspace; 128-query tiles and dense calls do not."""
+    n = 65536 * 2 + 100  # 3 chunks of 512 tiles of 64
+    base = lib.zebra_tile_sparse_attn_workspace(300, n, 2, 64, 128, 64, 100)
+    split = lib.zebra_tile_sparse_attn_workspace(300, n, 2, 64, 64, 64, 100)
+    assert split - base >= 2 * 300 * 3 * 264
+    assert lib.zebra_tile_sparse_attn_workspace(300, 60000, 2, 64, 64, 64, 100) == \
+        lib.zebra_tile_sparse_attn_workspace(300, 60000, 2, 64, 128, 64, 100)
+    t_k = -(-n // 64)
+    dense = lib.zebra_tile_sparse_attn_workspace(300, n, 2, 64, 64, 64, t_k)
+    assert 0 < dense < base
+
+
 def test_linear_validation(lib):
     f = lib.zebra_linear_attn
     s = seq(300)
@@ -153,6 +187,16 @@ def test_fit_validation(lib):
         zb.ZEBRA_ERR_INVALID_ARG
     assert f(P(1 << 16), P(1 << 20), 10, 2, 64, P(1 << 16), P(1 << 25), None, None) == \
         zb.ZEBRA_ERR_INVALID_ARG  # scale written over x
+
+
+def test_scale_only_fit_validation(lib):
+    f = lib.zebra_fit_scale_only
+    assert f(P(1 << 16), P(1 << 20), 0, 2, 64, P(1 << 24), P(1 << 25), None, None) == \
+        zb.ZEBRA_ERR_INVALID_ARG
+    assert f(P(1 << 16), P(1 << 20), 10, 2, 48, P(1 << 24), P(1 << 25), None, None) == \
+        zb.ZEBRA_ERR_UNSUPPORTED
+    assert f(P(1 << 16), P(1 << 20), 10, 2, 64, P(1 << 24), P(1 << 24), None, None) == \
+        zb.ZEBRA_ERR_INVALID_ARG  # scale and bias outputs overlap
 
 
 def test_binding_refuses_cpu_tensors():

@@ -264,6 +264,91 @@ def test_constant_tiles_closed_form_on_gpu():
 
 
 # ----------------------------------------------------------------------------
+# operator variants: no landmarks, landmark log count
+# ----------------------------------------------------------------------------
+
+VARIANT_CASES = [
+    # (q_tile, k_tile, n_q, n_kv, top_k, n_hot, heads); every case has a short last key tile
+    (64, 64, 300, 300, 2, 2, 2),
+    (128, 32, 257, 300, 4, 2, 1),
+    (32, 64, 100, 450, 1, 1, 2),
+    (64, 64, 300, 65536 + 333, 1, 1, 2),    # split keys: most chunks keep nothing
+    (64, 64, 300, 65536 + 333, 206, 3, 1),  # split keys, 20% kept
+]
+VARIANTS = {"no_landmarks": (1, dict(landmarks=False)),
+            "log_count": (2, dict(landmark_log_count=True))}
+
+
+@pytest.mark.parametrize("variant", sorted(VARIANTS))
+@pytest.mark.parametrize("case", VARIANT_CASES, ids=[str(c) for c in VARIANT_CASES])
+def test_sparse_variant_parity(case, variant):
+    q_tile, k_tile, n_q, n_kv, top_k, n_hot, heads = case
+    flags, kw = VARIANTS[variant]
+    print(f"[case] sparse variant {variant} {case}", flush=True)
+    q, k, v = _clustered(sum(case) + flags, heads, n_q, n_kv, q_tile, k_tile, n_hot)
+    bufs = stage.SparseBuffers.allocate(heads, n_q, n_kv, q_tile, k_tile, top_k, DEV,
+                                        torch.float32)
+    stage.sparse_stage(bf16_gpu(q), bf16_gpu(k), bf16_gpu(v), q_tile, k_tile, top_k, 0.125, bufs,
+                       flags=flags)
+    torch.cuda.synchronize()
+    ref, _ = zo.tile_sparse_attention(q, k, v, q_tile, k_tile, top_k, 0.125,
+                                      sel=bufs.sel.cpu().numpy(), **kw)
+    assert_close(bufs.out, ref, f"sparse {variant} {case}")
+
+
+@pytest.mark.parametrize("variant", sorted(VARIANTS))
+def test_sparse_variant_running_max_path(variant):
+    """Query tiles with a loose logit bound take the running-maximum path."""
+    flags, kw = VARIANTS[variant]
+    q, k, v = _clustered(31, 2, 700, 700, 64, 64, 3)
+    q = q.copy()
+    q[:, 128:320] *= 8.0
+    q = synth.bf16_round(q)
+    bufs = stage.SparseBuffers.allocate(2, 700, 700, 64, 64, 3, DEV, torch.float32)
+    stage.sparse_stage(bf16_gpu(q), bf16_gpu(k), bf16_gpu(v), 64, 64, 3, 0.125, bufs, flags=flags)
+    torch.cuda.synchronize()
+    ref, _ = zo.tile_sparse_attention(q, k, v, 64, 64, 3, 0.125, sel=bufs.sel.cpu().numpy(), **kw)
+    assert_close(bufs.out, ref, f"{variant} running-maximum path")
+
+
+@pytest.mark.parametrize("n_kv", [64 * 5 + 20, 65536 + 100])
+def test_log_count_constant_tiles_is_dense_on_gpu(n_kv):
+    """Key tiles of one repeated key/value (short last tile): a landmark that counts
+    its tile's tokens stands in exactly for the tile, so the output is dense
+    attention whatever is kept."""
+    rng = np.random.default_rng(5)
+    bk = 64
+    t_k = -(-n_kv // bk)
+    kap = synth.bf16_round(rng.standard_normal((t_k, 64)).astype(np.float32))
+    nu = synth.bf16_round(rng.standard_normal((t_k, 64)).astype(np.float32))
+    k = np.repeat(kap, bk, axis=0)[:n_kv][None]
+    v = np.repeat(nu, bk, axis=0)[:n_kv][None]
+    q = synth.bf16_round(rng.standard_normal((1, 128, 64)).astype(np.float32))
+    top_k = max(1, t_k // 5)
+    bufs = stage.SparseBuffers.allocate(1, 128, n_kv, 64, 64, top_k, DEV, torch.float32)
+    stage.sparse_stage(bf16_gpu(q), bf16_gpu(k), bf16_gpu(v), 64, 64, top_k, 0.125, bufs,
+                       flags=zb.ZEBRA_SPARSE_LANDMARK_LOG_COUNT)
+    torch.cuda.synchronize()
+    expect = zo.dense_attention(q[0], k[0], v[0], 0.125)
+    assert_close(bufs.out[0], expect, "log-count landmarks, constant tiles")
+
+
+def test_fit_scale_only_parity():
+    rng = np.random.default_rng(6)
+    heads, m = 4, 4096
+    x = rng.standard_normal((heads, m, 64)).astype(np.float32) * 0.01
+    y = (0.8 * x + 0.003 * rng.standard_normal((heads, m, 64)) + 0.001).astype(np.float32)
+    x[2, :, 7] = 0.0  # a degenerate channel
+    a, b, nd = zb.zebra_fit_scale_only(torch.from_numpy(x).to(DEV), torch.from_numpy(y).to(DEV))
+    torch.cuda.synchronize()
+    for h in range(heads):
+        ra, rb, _ = zo.fit_scale_only(x[h], y[h])
+        np.testing.assert_allclose(to_f64(a[h]), ra, rtol=1e-5, atol=1e-7)
+        assert np.all(to_f64(b[h]) == 0.0)
+    assert int(nd.item()) == 1
+
+
+# ----------------------------------------------------------------------------
 # linear attention and the fit
 # ----------------------------------------------------------------------------
 
