@@ -43,6 +43,12 @@ off by default:
      tile, so its logit gains ln(n_j) (the short last tile counts its valid
      tokens).
   V3 uncentered fit: the map through the origin, a = sum x y / sum x^2, b = 0.
+  V4 spatial tiles ("selected spatial tiles", [paper page] abstract; "Tile
+     sparse" vs "Block sparse", appendix Tables 15-17): the tokens are first
+     put in a spatial order and tiles are contiguous runs of that order. Per
+     view (n_special leading tokens, then a grid_h x grid_w row-major patch
+     grid): the special tokens, then the patches in s x s blocks taken in
+     raster order of blocks, each block row-major (edge blocks are smaller).
 
 Parity status: every function on the attention path is pinned by
 ``tests/oracle_pins.py`` against closed forms, library routines or brute
@@ -61,7 +67,7 @@ __all__ = [
     "tile_sparse_attention", "dense_attention", "elu_plus_one",
     "linear_attention", "fit_affine", "fit_scale_only", "affine_apply",
     "mean_attention_sparsity", "block_attention_mass",
-    "retained_mass", "top_mass",
+    "retained_mass", "top_mass", "spatial_token_order", "spatial_tile_sparse_attention",
 ]
 
 
@@ -318,6 +324,36 @@ def fit_scale_only(x, y, degenerate_rel: float = 1e-30):
     ok = sxx > degenerate_rel * m
     a = np.where(ok, sxy / np.where(ok, sxx, 1.0), 0.0)
     return a, np.zeros_like(a), int((~ok).sum())
+
+
+def spatial_token_order(n_views: int, n_special: int, grid_h: int, grid_w: int,
+                        block: int) -> np.ndarray:
+    """Variant V4: position i of the spatial order holds original token order[i]."""
+    per_view = n_special + grid_h * grid_w
+    order = []
+    for view in range(n_views):
+        base = view * per_view
+        order.extend(base + t for t in range(n_special))
+        for r0 in range(0, grid_h, block):
+            for c0 in range(0, grid_w, block):
+                for r in range(r0, min(grid_h, r0 + block)):
+                    for c in range(c0, min(grid_w, c0 + block)):
+                        order.append(base + n_special + r * grid_w + c)
+    return np.asarray(order, dtype=np.int64)
+
+
+def spatial_tile_sparse_attention(q, k, v, order, q_tile: int, k_tile: int, top_k: int,
+                                  scale: float, sel=None, **variant):
+    """Tile-sparse attention with spatial tiles (V4): tokens in ``order`` (the same
+    for queries and keys), tiles as contiguous runs of it, the output returned in
+    the original token order. ``sel`` refers to tiles of the spatial order."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    order = np.asarray(order, dtype=np.int64)
+    out_perm, sel = tile_sparse_attention(q[:, order], k[:, order], v[:, order], q_tile, k_tile,
+                                          top_k, scale, sel=sel, **variant)
+    out = np.empty_like(out_perm)
+    out[:, order] = out_perm
+    return out, sel
 
 
 # ----------------------------------------------------------------------------

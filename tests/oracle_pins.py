@@ -458,6 +458,60 @@ def pin_scale_only_fit_vs_lstsq():
     assert n_deg == 1 and a[2] == 0.0, "degenerate channel"
 
 
+def pin_spatial_order_by_hand_and_special_cases():
+    """A 2x4 grid in 2x2 blocks after one special token, written out by hand; block
+    side 1 or at least the grid gives the row-major order (the identity)."""
+    got = zo.spatial_token_order(2, 1, 2, 4, 2)
+    #  view 0: special 0; patches 1 2 3 4 / 5 6 7 8 -> blocks [1 2 5 6] [3 4 7 8]
+    expect = [0, 1, 2, 5, 6, 3, 4, 7, 8, 9, 10, 11, 14, 15, 12, 13, 16, 17]
+    assert [int(t) for t in got] == expect, got
+    for blk in (1, 7, 40):  # side 1, or one block spanning the 7 columns
+        ident = zo.spatial_token_order(3, 5, 5, 7, blk)
+        assert np.array_equal(ident, np.arange(3 * 40)), f"block {blk}"
+
+
+def pin_spatial_order_is_blockwise_bijection():
+    """VGGT-shaped view (5 + 37 x 37 tokens, 8 x 8 blocks): a permutation of each
+    view's tokens; every block is one contiguous run whose patches span at most
+    8 rows and 8 columns; full blocks hold 64 patches."""
+    n_views, n_sp, g, s = 2, 5, 37, 8
+    order = zo.spatial_token_order(n_views, n_sp, g, g, s)
+    per_view = n_sp + g * g
+    assert sorted(order.tolist()) == list(range(n_views * per_view))
+    for view in range(n_views):
+        seg = order[view * per_view:(view + 1) * per_view] - view * per_view
+        assert seg[:n_sp].tolist() == list(range(n_sp))
+        patches = seg[n_sp:] - n_sp
+        rows, cols = patches // g, patches % g
+        pos = 0
+        for r0 in range(0, g, s):
+            for c0 in range(0, g, s):
+                n = (min(g, r0 + s) - r0) * (min(g, c0 + s) - c0)
+                br, bc = rows[pos:pos + n], cols[pos:pos + n]
+                assert br.min() == r0 and br.max() == min(g, r0 + s) - 1
+                assert bc.min() == c0 and bc.max() == min(g, c0 + s) - 1
+                assert len(set(zip(br.tolist(), bc.tolist()))) == n
+                pos += n
+        assert pos == g * g
+
+
+def pin_spatial_attention_equivariance():
+    """Keeping every tile, spatial tiles give dense attention in the original order
+    (torch's scaled-dot-product attention), and block side 1 gives the plain
+    tile-sparse result."""
+    order = zo.spatial_token_order(2, 2, 3, 5, 2)  # 34 tokens
+    q, k, v = _qkv(49, 2, 34, 34, 8)
+    out, _ = zo.spatial_tile_sparse_attention(q, k, v, order, 4, 4, 9, 0.35)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), scale=0.35).numpy()
+    _close(out, ref, 1e-13, "spatial tiles, every tile kept")
+    ident = zo.spatial_token_order(2, 2, 3, 5, 1)
+    a, sa = zo.spatial_tile_sparse_attention(q, k, v, ident, 4, 4, 2, 0.35)
+    b, sb = zo.tile_sparse_attention(q, k, v, 4, 4, 2, 0.35)
+    _close(a, b, 1e-15, "identity order")
+    assert np.array_equal(sa, sb)
+
+
 ALL_PINS = [
     pin_pool_exact_rational, pin_select_brute_force, pin_select_tiles_orientation,
     pin_dense_vs_sdpa, pin_dense_closed_forms, pin_keep_all_equals_dense,
@@ -469,5 +523,6 @@ ALL_PINS = [
     pin_block_mass_rows_sum_to_one_and_by_hand, pin_block_mass_constant_keys,
     pin_retained_and_top_mass, pin_no_landmarks_is_attention_over_kept_tokens,
     pin_log_count_constant_tiles_is_dense, pin_log_count_unit_tiles_by_hand,
-    pin_scale_only_fit_vs_lstsq,
+    pin_scale_only_fit_vs_lstsq, pin_spatial_order_by_hand_and_special_cases,
+    pin_spatial_order_is_blockwise_bijection, pin_spatial_attention_equivariance,
 ]

@@ -142,6 +142,36 @@ def _scale_fit_keeps_intercept(x, y, degenerate_rel=1e-30):
     return a, b, n
 
 
+def _spatial_order_with(col_major_blocks=False, special_last=False):
+    def order(n_views, n_special, grid_h, grid_w, block):
+        per_view = n_special + grid_h * grid_w
+        out = []
+        for view in range(n_views):
+            base = view * per_view
+            sp = [base + t for t in range(n_special)]
+            if not special_last:
+                out.extend(sp)
+            starts = [(r0, c0) for r0 in range(0, grid_h, block) for c0 in range(0, grid_w, block)]
+            if col_major_blocks:
+                starts.sort(key=lambda rc: (rc[1], rc[0]))
+            for r0, c0 in starts:
+                for r in range(r0, min(grid_h, r0 + block)):
+                    for c in range(c0, min(grid_w, c0 + block)):
+                        out.append(base + n_special + r * grid_w + c)
+            if special_last:
+                out.extend(sp)
+        return np.asarray(out, dtype=np.int64)
+    return order
+
+
+def _spatial_attention_not_unpermuted(q, k, v, order, q_tile, k_tile, top_k, scale, sel=None,
+                                      **variant):
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    order = np.asarray(order)
+    return zo.tile_sparse_attention(q[:, order], k[:, order], v[:, order], q_tile, k_tile,
+                                    top_k, scale, sel=sel, **variant)
+
+
 def _top_mass_lowest(mass, top_k):
     m = np.asarray(mass, np.float64)
     return np.sort(m, axis=1)[:, :top_k].sum(axis=1)
@@ -174,6 +204,12 @@ MUTATIONS = {
                                                    _columns_with(count_full_tiles=True)),
     "uncentered fit centred": ("fit_scale_only", _scale_fit_centred),
     "uncentered fit keeps an intercept": ("fit_scale_only", _scale_fit_keeps_intercept),
+    "spatial blocks in column order": ("spatial_token_order",
+                                       _spatial_order_with(col_major_blocks=True)),
+    "special tokens after the patches": ("spatial_token_order",
+                                         _spatial_order_with(special_last=True)),
+    "spatial output left in the spatial order": ("spatial_tile_sparse_attention",
+                                                 _spatial_attention_not_unpermuted),
 }
 
 
