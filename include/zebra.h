@@ -202,6 +202,39 @@ zebra_status zebra_fit_affine(const float* x, const float* y, int32_t m, int32_t
                               int32_t* n_degenerate_out, void* stream);
 
 /*
+ * Spatial tiles as a token permutation (Zebra3D paper page: softmax is kept
+ * over selected spatial tiles, abstract; block- vs tile-sparse attention,
+ * appendix Tables 15-17). Tiles are contiguous runs of the token order, so
+ * spatial tiles come from a spatial order of the tokens: per view (n_special
+ * leading tokens, then a grid_h x grid_w row-major patch grid; the VGGT-shaped
+ * view is 5 + 37 x 37 = 1,374 tokens), the special tokens, then the patches
+ * in block x block squares in raster order of squares, each square row-major
+ * (squares at the right and bottom edges are smaller). Attention is
+ * equivariant under a common permutation of queries and keys, so
+ *   gather q, k, v by the order -> zebra_tile_sparse_attn -> scatter o back
+ * is tile-sparse attention with spatial tiles, in the original token order.
+ *
+ * zebra_spatial_order: host function (no GPU, no stream). Writes
+ *          order_out[i] = original index of the token at position i,
+ *          order_len = n_views * (n_special + grid_h * grid_w) entries (host
+ *          memory, owned by the caller). block >= 1.
+ * zebra_permute_tokens: moves 64-channel rows on the device.
+ *          inverse = 0: dst[h][i] = src[h][order[i]] (gather);
+ *          inverse = 1: dst[h][order[i]] = src[h][i] (scatter, the inverse).
+ *          src (ss) and dst (ds) have the same n_tokens and n_heads, element
+ *          type dtype (bf16 or float32), 16-byte aligned rows; order is an
+ *          int32 device vector of n_tokens entries, a permutation of
+ *          [0, n_tokens): entries outside that range move nothing, repeated
+ *          entries leave rows unwritten. dst may not overlap src or order.
+ */
+zebra_status zebra_spatial_order(int32_t n_views, int32_t n_special, int32_t grid_h,
+                                 int32_t grid_w, int32_t block, int32_t* order_out,
+                                 int64_t order_len);
+zebra_status zebra_permute_tokens(const void* src, zebra_seq ss, const int32_t* order,
+                                  int32_t inverse, zebra_dtype dtype, void* dst, zebra_seq ds,
+                                  void* stream);
+
+/*
  * Uncentered fit, the variant the Zebra3D paper page's Table 3(a) lists as
  * "Linear, uncentered fit": per (head h, channel c) the least-squares map
  * through the origin, min sum (a x - y)^2:

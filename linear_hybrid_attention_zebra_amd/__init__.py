@@ -30,7 +30,8 @@ ENTRY_POINTS = (
     "zebra_pool_landmarks", "zebra_select_tiles_workspace", "zebra_select_tiles",
     "zebra_tile_sparse_attn_workspace", "zebra_tile_sparse_attn", "zebra_tile_sparse_attn_ex",
     "zebra_linear_attn_workspace", "zebra_linear_attn", "zebra_fit_affine", "zebra_fit_scale_only",
-    "zebra_block_mass_workspace", "zebra_block_mass", "zebra_status_string", "zebra_version",
+    "zebra_block_mass_workspace", "zebra_block_mass", "zebra_spatial_order",
+    "zebra_permute_tokens", "zebra_status_string", "zebra_version",
 )
 
 
@@ -79,6 +80,8 @@ def _declare(lib):
         "zebra_block_mass_workspace": (c_sz, [c_i64, c_i32]),
         "zebra_block_mass": (c_i32, [c_p, ZebraSeq, c_p, ZebraSeq, c_i32, c_i32, c_f, c_p, c_p,
                                      c_sz, c_p]),
+        "zebra_spatial_order": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_p, c_i64]),
+        "zebra_permute_tokens": (c_i32, [c_p, ZebraSeq, c_p, c_i32, c_i32, c_p, ZebraSeq, c_p]),
         "zebra_status_string": (ctypes.c_char_p, [c_i32]),
         "zebra_version": (ctypes.c_char_p, []),
     }
@@ -319,4 +322,33 @@ def zebra_block_mass(q: torch.Tensor, k: torch.Tensor, q_tile: int, k_tile: int,
     _check("zebra_block_mass", lib.zebra_block_mass(
         _ptr(q), seq_of(q), _ptr(k), seq_of(k), q_tile, k_tile, scale, _ptr(out),
         _ptr(workspace), nbytes, _stream(q.device)))
+    return out
+
+
+def zebra_spatial_order(n_views: int, n_special: int, grid_h: int, grid_w: int,
+                        block: int) -> torch.Tensor:
+    """Spatial token order (host int32 tensor): position i holds original token order[i]."""
+    n = n_views * (n_special + grid_h * grid_w)
+    out = torch.empty(n, dtype=torch.int32)
+    _check("zebra_spatial_order", library().zebra_spatial_order(
+        n_views, n_special, grid_h, grid_w, block, out.data_ptr() if n else None, n))
+    return out
+
+
+def zebra_permute_tokens(src: torch.Tensor, order: torch.Tensor, inverse: bool = False,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gather (out[h][i] = src[h][order[i]]) or, with inverse, scatter of [H][N][64] rows."""
+    if src.dtype not in (torch.bfloat16, torch.float32) or not src.is_cuda:
+        raise ValueError("src must be a bfloat16 or float32 CUDA tensor")
+    _need(order, torch.int32, "order")
+    if not order.is_contiguous() or order.numel() != src.shape[1]:
+        raise ValueError("order must be a contiguous int32 vector of N entries")
+    if out is None:
+        out = torch.empty_like(src)
+    if out.dtype != src.dtype:
+        raise ValueError("out must have the dtype of src")
+    _check("zebra_permute_tokens", library().zebra_permute_tokens(
+        _ptr(src), seq_of(src), _ptr(order), 1 if inverse else 0,
+        ZEBRA_F32 if src.dtype == torch.float32 else ZEBRA_BF16, _ptr(out), seq_of(out),
+        _stream(src.device)))
     return out

@@ -92,6 +92,11 @@ hipError_t launch_block_mass(const uint16_t* q, int64_t nq, int64_t qst, int64_t
                              const uint16_t* k, int64_t nk, int64_t kst, int64_t ksh,
                              int32_t heads, int32_t q_tile, int32_t k_tile, float scale,
                              float* mass, void* ws, hipStream_t s);
+int64_t spatial_order(int32_t n_views, int32_t n_special, int32_t grid_h, int32_t grid_w,
+                      int32_t block, int32_t* out);
+hipError_t launch_permute(const void* src, int64_t s_tok, int64_t s_head, void* dst,
+                          int64_t d_tok, int64_t d_head, const int32_t* order, int64_t n,
+                          int32_t heads, int32_t elem_bytes, bool scatter, hipStream_t s);
 hipError_t launch_fit(const float* x, const float* y, int32_t m, int32_t heads, float* a,
                       float* b, int32_t* n_deg, bool centred, hipStream_t s);
 }  // namespace zebra

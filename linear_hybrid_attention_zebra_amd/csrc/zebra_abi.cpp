@@ -351,4 +351,38 @@ zebra_status zebra_fit_scale_only(const float* x, const float* y, int32_t m, int
                     stream);
 }
 
+zebra_status zebra_spatial_order(int32_t n_views, int32_t n_special, int32_t grid_h,
+                                 int32_t grid_w, int32_t block, int32_t* order_out,
+                                 int64_t order_len) {
+  if (n_views < 0 || n_special < 0 || grid_h < 0 || grid_w < 0 || block < 1)
+    return ZEBRA_ERR_INVALID_ARG;
+  const int64_t n = (int64_t)n_views * ((int64_t)n_special + (int64_t)grid_h * grid_w);
+  if (n > (int64_t)INT32_MAX) return ZEBRA_ERR_UNSUPPORTED;
+  if (order_len != n || (n > 0 && order_out == nullptr)) return ZEBRA_ERR_INVALID_ARG;
+  zebra::spatial_order(n_views, n_special, grid_h, grid_w, block, order_out);
+  return ZEBRA_OK;
+}
+
+zebra_status zebra_permute_tokens(const void* src, zebra_seq ss, const int32_t* order,
+                                  int32_t inverse, zebra_dtype dtype, void* dst, zebra_seq ds,
+                                  void* stream) {
+  zebra_status st;
+  if ((st = check_seq(src, ss, false)) != ZEBRA_OK) return st;
+  if ((st = check_seq(dst, ds, true)) != ZEBRA_OK) return st;
+  if (dtype != ZEBRA_BF16 && dtype != ZEBRA_F32) return ZEBRA_ERR_INVALID_ARG;
+  if (inverse != 0 && inverse != 1) return ZEBRA_ERR_INVALID_ARG;
+  if (ss.n_heads != ds.n_heads || ss.n_tokens != ds.n_tokens) return ZEBRA_ERR_INVALID_ARG;
+  if (seq_empty(ss)) return ZEBRA_OK;
+  if (ss.n_tokens > (int64_t)INT32_MAX) return ZEBRA_ERR_UNSUPPORTED;
+  if (order == nullptr || ((uintptr_t)order % 4) != 0) return ZEBRA_ERR_INVALID_ARG;
+  const size_t el = dtype == ZEBRA_F32 ? 4 : 2;
+  const Range sr = seq_range(src, ss, el), dr = seq_range(dst, ds, el);
+  const Range orr = flat_range(order, (uint64_t)ss.n_tokens, 4);
+  if (overlaps(dr, sr) || overlaps(dr, orr)) return ZEBRA_ERR_INVALID_ARG;
+  return hip_status(zebra::launch_permute(src, ss.stride_token, ss.stride_head, dst,
+                                          ds.stride_token, ds.stride_head, order, ss.n_tokens,
+                                          ss.n_heads, (int32_t)el, inverse == 1,
+                                          (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -15,8 +15,9 @@ from typing import Optional
 
 import torch
 
-from . import (ceil_div, zebra_fit_affine, zebra_linear_attn, zebra_pool_landmarks,
-               zebra_select_tiles, zebra_tile_sparse_attn, zebra_tile_sparse_attn_ex)
+from . import (ceil_div, zebra_fit_affine, zebra_linear_attn, zebra_permute_tokens,
+               zebra_pool_landmarks, zebra_select_tiles, zebra_tile_sparse_attn,
+               zebra_tile_sparse_attn_ex)
 
 
 @dataclasses.dataclass
@@ -68,6 +69,21 @@ def sparse_stage(q, k, v, q_tile: int, k_tile: int, top_k: int, scale: float,
     zebra_tile_sparse_attn_ex(q, k, v, bufs.kbar, bufs.vbar, bufs.sel, q_tile, k_tile, top_k,
                               scale, flags, out=bufs.out, workspace=bufs.attn_ws)
     return bufs
+
+
+def spatial_sparse_stage(q, k, v, order: torch.Tensor, q_tile: int, k_tile: int, top_k: int,
+                         scale: float, bufs: Optional[SparseBuffers] = None, flags: int = 0,
+                         out: Optional[torch.Tensor] = None):
+    """A tile-sparse stage with spatial tiles: gather q, k, v into the spatial
+    order (int32 device vector), run the stage there, scatter the output back.
+    Returns (out in the original order, the buffers of the permuted stage)."""
+    qp, kp, vp = (zebra_permute_tokens(t.contiguous() if t.stride(2) != 1 else t, order)
+                  for t in (q, k, v))
+    bufs = sparse_stage(qp, kp, vp, q_tile, k_tile, top_k, scale, bufs, flags)
+    if out is None:
+        out = torch.empty(q.shape, dtype=bufs.out.dtype, device=q.device)
+    zebra_permute_tokens(bufs.out, order, inverse=True, out=out)
+    return out, bufs
 
 
 def linear_stage(q, k, v, aff_scale=None, aff_bias=None, out=None, workspace=None):

@@ -9,6 +9,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import linear_hybrid_attention_zebra_amd as zb
@@ -31,7 +32,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     for name in names:
         assert hasattr(lib, name), f"{name} declared in zebra.h but not exported"
     assert set(names) == set(zb.ENTRY_POINTS)
@@ -197,6 +198,31 @@ def test_scale_only_fit_validation(lib):
         zb.ZEBRA_ERR_UNSUPPORTED
     assert f(P(1 << 16), P(1 << 20), 10, 2, 64, P(1 << 24), P(1 << 24), None, None) == \
         zb.ZEBRA_ERR_INVALID_ARG  # scale and bias outputs overlap
+
+
+def test_spatial_order_matches_oracle(lib):
+    """The host-side spatial order of the library equals the oracle's (host logic)."""
+    import oracle.zebra_oracle as zo
+    for args in [(2, 5, 37, 37, 8), (3, 1, 2, 4, 2), (1, 0, 9, 5, 4), (2, 5, 37, 37, 1)]:
+        got = zb.zebra_spatial_order(*args).numpy()
+        assert np.array_equal(got, zo.spatial_token_order(*args)), args
+    assert lib.zebra_spatial_order(1, 0, 2, 2, 0, P(1 << 16), 4) == zb.ZEBRA_ERR_INVALID_ARG
+    assert lib.zebra_spatial_order(1, 0, 2, 2, 1, P(1 << 16), 5) == zb.ZEBRA_ERR_INVALID_ARG
+
+
+def test_permute_validation(lib):
+    f = lib.zebra_permute_tokens
+    s = seq(256)
+
+    def call(order=P(1 << 24), inverse=0, dtype=0, dst=P(1 << 28), ds=s):
+        return f(P(1 << 16), s, order, inverse, dtype, dst, ds, None)
+
+    assert call(order=None) == zb.ZEBRA_ERR_INVALID_ARG
+    assert call(inverse=2) == zb.ZEBRA_ERR_INVALID_ARG
+    assert call(dtype=5) == zb.ZEBRA_ERR_INVALID_ARG
+    assert call(ds=seq(255)) == zb.ZEBRA_ERR_INVALID_ARG  # lengths differ
+    assert call(dst=P(1 << 16)) == zb.ZEBRA_ERR_INVALID_ARG  # in place
+    assert call(dst=P(1 << 24)) == zb.ZEBRA_ERR_INVALID_ARG  # over the order vector
 
 
 def test_binding_refuses_cpu_tensors():

@@ -349,6 +349,45 @@ def test_fit_scale_only_parity():
 
 
 # ----------------------------------------------------------------------------
+# spatial tiles: token permutation
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_permute_tokens_exact(dtype):
+    rng = np.random.default_rng(8)
+    heads, n = 3, 1000
+    x = rng.standard_normal((heads, n, 64)).astype(np.float32)
+    order = rng.permutation(n).astype(np.int32)
+    xg = torch.from_numpy(x).to(DEV).to(dtype)
+    xg = xg.permute(1, 0, 2).contiguous().permute(1, 0, 2)  # token-major source
+    og = torch.from_numpy(order).to(DEV)
+    g = zb.zebra_permute_tokens(xg, og)
+    back = zb.zebra_permute_tokens(g, og, inverse=True)
+    torch.cuda.synchronize()
+    xr = xg.cpu()
+    assert torch.equal(g.cpu(), xr[:, torch.from_numpy(order).long()])
+    assert torch.equal(back.cpu(), xr)
+
+
+@pytest.mark.parametrize("views,n_special,grid,block,q_tile,k_tile,top_k", [
+    (2, 5, 12, 8, 64, 64, 2), (3, 1, 10, 4, 32, 32, 3), (2, 5, 37, 8, 64, 64, 9),
+])
+def test_spatial_stage_parity(views, n_special, grid, block, q_tile, k_tile, top_k):
+    print(f"[case] spatial tiles views={views} grid={grid} block={block}", flush=True)
+    order = zb.zebra_spatial_order(views, n_special, grid, grid, block).numpy()
+    n = order.size
+    q, k, v = _clustered(n + block, 2, n, n, q_tile, k_tile, 2)
+    og = torch.from_numpy(order).to(DEV)
+    out, bufs = stage.spatial_sparse_stage(bf16_gpu(q), bf16_gpu(k), bf16_gpu(v), og, q_tile,
+                                           k_tile, top_k, 0.125)
+    torch.cuda.synchronize()
+    ref, _ = zo.spatial_tile_sparse_attention(q, k, v, zo.spatial_token_order(
+        views, n_special, grid, grid, block), q_tile, k_tile, top_k, 0.125,
+        sel=bufs.sel.cpu().numpy())
+    assert_close(out, ref, f"spatial tiles {views}x{grid}/{block}")
+
+
+# ----------------------------------------------------------------------------
 # linear attention and the fit
 # ----------------------------------------------------------------------------
 
