@@ -50,6 +50,12 @@ off by default:
      grid): the special tokens, then the patches in s x s blocks taken in
      raster order of blocks, each block row-major (edge blocks are smaller).
 
+Gradients (for the optional refinement, [paper page] Tables 18-19: the
+converted model can be refined with a frozen teacher): the backward passes of
+the two operators for a given output gradient, with the tile selection held
+fixed (top-k is not differentiable). A landmark's key and value are tile
+means, so each token of tile j receives 1/n_j of its landmark's gradient.
+
 Parity status: every function on the attention path is pinned by
 ``tests/oracle_pins.py`` against closed forms, library routines or brute
 force. ``mean_attention_sparsity`` is bookkeeping, not part of the path; the
@@ -68,6 +74,7 @@ __all__ = [
     "linear_attention", "fit_affine", "fit_scale_only", "affine_apply",
     "mean_attention_sparsity", "block_attention_mass",
     "retained_mass", "top_mass", "spatial_token_order", "spatial_tile_sparse_attention",
+    "tile_sparse_attention_backward", "linear_attention_backward",
 ]
 
 
@@ -224,6 +231,50 @@ def tile_sparse_attention(q, k, v, q_tile: int, k_tile: int, top_k: int, scale: 
     return out, np.stack(sels) if sels else np.zeros((0, 0, top_k), dtype=np.int64)
 
 
+def tile_sparse_attention_backward(q, k, v, q_tile: int, k_tile: int, sel, scale: float, dout,
+                                   landmarks: bool = True, landmark_log_count: bool = False):
+    """Gradients (dq, dk, dv) of sum(dout * out) for tile_sparse_attention on the
+    selection ``sel`` ([H][Tq][top_k], held fixed). [H][N][d] arrays.
+
+    Per query row with columns c (attention_columns), logits l_c and P = softmax(l):
+        dP_c = dout . v_c,  D = sum_c P_c dP_c,  dl_c = P_c (dP_c - D),
+        dq = scale sum_c dl_c k_c,  dk_c = scale dl_c q,  dv_c = P_c dout.
+    Kept columns are tokens; a landmark column's dk_c and dv_c go to every
+    token of its tile, divided by the tile's token count.
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    heads, n_q, d = q.shape
+    n_k = k.shape[1]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    kb = tile_bounds(n_k, k_tile)
+    for h in range(heads):
+        for i, (s0, e0) in enumerate(tile_bounds(n_q, q_tile)):
+            kept = sorted(int(j) for j in sel[h][i])
+            ck, cv, bias = attention_columns(k[h], v[h], k_tile, kept, landmarks,
+                                             landmark_log_count)
+            # the token (or tile) each column belongs to
+            owner = [("tok", t) for j in kept for t in range(*kb[j])]
+            if landmarks:
+                owner += [("lm", j) for j in range(len(kb)) if j not in set(kept)]
+            p = _softmax_rows(scale * (q[h, s0:e0] @ ck.T) + bias[None, :])
+            dp = dout[h, s0:e0] @ cv.T
+            dl = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dq[h, s0:e0] = scale * (dl @ ck)
+            dck = scale * (dl.T @ q[h, s0:e0])
+            dcv = p.T @ dout[h, s0:e0]
+            for c, (kind, idx) in enumerate(owner):
+                if kind == "tok":
+                    dk[h, idx] += dck[c]
+                    dv[h, idx] += dcv[c]
+                else:
+                    a, b = kb[idx]
+                    dk[h, a:b] += dck[c] / (b - a)
+                    dv[h, a:b] += dcv[c] / (b - a)
+    return dq, dk, dv
+
+
 def dense_attention(q, k, v, scale: float, row_block: int = 1024) -> np.ndarray:
     """Exact softmax attention of every query over every key, one head: [Nq][d] -> [Nq][d].
 
@@ -269,6 +320,41 @@ def linear_attention(q, k, v, aff_scale=None, aff_bias=None):
     if aff_scale is not None or aff_bias is not None:
         o = affine_apply(o, aff_scale, aff_bias)
     return o, state, z
+
+
+def linear_attention_backward(q, k, v, dout, aff_scale=None, aff_bias=None):
+    """Gradients of sum(dout * out) for linear_attention of one head:
+    (dq, dk, dv, da, db), [N][d] and [d].
+
+    With num = phi(q) S, den = phi(q) . z, o = num / den, out = a * o + b:
+        da = sum_n dout * o,  db = sum_n dout,  do = a * dout,
+        dnum = do / den,  dden = -(do . o) / den,
+        dq = (S dnum + z dden) * phi'(q),
+        dS = sum_n phi(q_n) dnum_n^T,  dz = sum_n phi(q_n) dden_n,
+        dv_m = dS^T phi(k_m),  dk_m = (dS v_m + dz) * phi'(k_m),
+    phi'(x) = 1 for x > 0, exp(x) otherwise.
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    d = v.shape[1]
+    a = np.ones(d) if aff_scale is None else _f64(aff_scale)
+    fq, fk = elu_plus_one(q), elu_plus_one(k)
+    dfq = np.where(q > 0, 1.0, np.exp(np.minimum(q, 0.0)))
+    dfk = np.where(k > 0, 1.0, np.exp(np.minimum(k, 0.0)))
+    state = fk.T @ v
+    z = fk.sum(axis=0)
+    den = fq @ z
+    o = (fq @ state) / den[:, None]
+    da = (dout * o).sum(axis=0)
+    db = dout.sum(axis=0)
+    do = dout * a[None, :]
+    dnum = do / den[:, None]
+    dden = -(do * o).sum(axis=1) / den
+    dq = (dnum @ state.T + dden[:, None] * z[None, :]) * dfq
+    d_state = fq.T @ dnum
+    dz = fq.T @ dden
+    dv = fk @ d_state
+    dk = (v @ d_state.T + dz[None, :]) * dfk
+    return dq, dk, dv, da, db
 
 
 def affine_apply(o, aff_scale=None, aff_bias=None) -> np.ndarray:

@@ -512,6 +512,61 @@ def pin_spatial_attention_equivariance():
     assert np.array_equal(sa, sb)
 
 
+# ----------------------------------------------------------------------------
+# gradients (central finite differences of the oracle's own forward)
+# ----------------------------------------------------------------------------
+
+def _fd_grad(f, x, eps=1e-6):
+    """Central differences of the scalar f at every element of x (x is restored)."""
+    g = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        old = x[i]
+        x[i] = old + eps
+        fp = f()
+        x[i] = old - eps
+        fm = f()
+        x[i] = old
+        g[i] = (fp - fm) / (2 * eps)
+    return g
+
+
+def pin_sparse_backward_finite_differences():
+    """dq, dk, dv of sum(dout * out) against central differences, for a fixed
+    selection with a short last key tile, in all three landmark readings."""
+    rng = np.random.default_rng(50)
+    q = rng.standard_normal((1, 7, 3))
+    k = rng.standard_normal((1, 11, 3))
+    v = rng.standard_normal((1, 11, 2))
+    dout = rng.standard_normal((1, 7, 2))
+    sel = np.array([[[1], [0], [2]]])  # query tiles of 3: key tiles of 4, 4, 3
+    for kw in (dict(), dict(landmark_log_count=True), dict(landmarks=False)):
+        loss = lambda: float((zo.tile_sparse_attention(q, k, v, 3, 4, 1, 0.7, sel=sel, **kw)[0]
+                              * dout).sum())
+        dq, dk, dv = zo.tile_sparse_attention_backward(q, k, v, 3, 4, sel, 0.7, dout, **kw)
+        _close(dq, _fd_grad(loss, q), 1e-7, f"sparse dq {kw}")
+        _close(dk, _fd_grad(loss, k), 1e-7, f"sparse dk {kw}")
+        _close(dv, _fd_grad(loss, v), 1e-7, f"sparse dv {kw}")
+
+
+def pin_linear_backward_finite_differences():
+    """dq, dk, dv, da, db of sum(dout * out) for the linear stage with its affine
+    map against central differences (inputs on both branches of elu + 1)."""
+    rng = np.random.default_rng(51)
+    q = rng.standard_normal((6, 4))
+    k = rng.standard_normal((9, 4))
+    v = rng.standard_normal((9, 3))
+    a = rng.standard_normal(3)
+    b = rng.standard_normal(3)
+    dout = rng.standard_normal((6, 3))
+    loss = lambda: float((zo.linear_attention(q, k, v, a, b)[0] * dout).sum())
+    dq, dk, dv, da, db = zo.linear_attention_backward(q, k, v, dout, a, b)
+    for got, x, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv"), (da, a, "da"),
+                         (db, b, "db")):
+        _close(got, _fd_grad(loss, x), 1e-7, f"linear {name}")
+
+
 ALL_PINS = [
     pin_pool_exact_rational, pin_select_brute_force, pin_select_tiles_orientation,
     pin_dense_vs_sdpa, pin_dense_closed_forms, pin_keep_all_equals_dense,
@@ -525,4 +580,5 @@ ALL_PINS = [
     pin_log_count_constant_tiles_is_dense, pin_log_count_unit_tiles_by_hand,
     pin_scale_only_fit_vs_lstsq, pin_spatial_order_by_hand_and_special_cases,
     pin_spatial_order_is_blockwise_bijection, pin_spatial_attention_equivariance,
+    pin_sparse_backward_finite_differences, pin_linear_backward_finite_differences,
 ]

@@ -172,6 +172,62 @@ def _spatial_attention_not_unpermuted(q, k, v, order, q_tile, k_tile, top_k, sca
                                     top_k, scale, sel=sel, **variant)
 
 
+def _sparse_bwd_with(no_d=False, no_spread=False, dv_from_dl=False, dq_no_scale=False):
+    def bwd(q, k, v, q_tile, k_tile, sel, scale, dout, landmarks=True, landmark_log_count=False):
+        q, k, v, dout = (np.asarray(x, np.float64) for x in (q, k, v, dout))
+        dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+        kb = zo.tile_bounds(k.shape[1], k_tile)
+        for h in range(q.shape[0]):
+            for i, (s0, e0) in enumerate(zo.tile_bounds(q.shape[1], q_tile)):
+                kept = sorted(int(j) for j in sel[h][i])
+                ck, cv, bias = zo.attention_columns(k[h], v[h], k_tile, kept, landmarks,
+                                                    landmark_log_count)
+                owner = [("tok", t) for j in kept for t in range(*kb[j])]
+                if landmarks:
+                    owner += [("lm", j) for j in range(len(kb)) if j not in set(kept)]
+                lg = scale * (q[h, s0:e0] @ ck.T) + bias[None, :]
+                p = np.exp(lg - lg.max(axis=1, keepdims=True))
+                p /= p.sum(axis=1, keepdims=True)
+                dp = dout[h, s0:e0] @ cv.T
+                dl = p * dp if no_d else p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                dq[h, s0:e0] = (1.0 if dq_no_scale else scale) * (dl @ ck)
+                dck = scale * (dl.T @ q[h, s0:e0])
+                dcv = (dl if dv_from_dl else p).T @ dout[h, s0:e0]
+                for c, (kind, idx) in enumerate(owner):
+                    if kind == "tok":
+                        dk[h, idx] += dck[c]
+                        dv[h, idx] += dcv[c]
+                    else:
+                        a, b = kb[idx]
+                        n = 1 if no_spread else b - a
+                        dk[h, a:b] += dck[c] / n
+                        dv[h, a:b] += dcv[c] / n
+        return dq, dk, dv
+    return bwd
+
+
+def _linear_bwd_with(no_dphi=False, dden_sign=False, no_db=False):
+    def bwd(q, k, v, dout, aff_scale=None, aff_bias=None):
+        dq, dk, dv, da, db = _orig["linear_attention_backward"](q, k, v, dout, aff_scale,
+                                                                aff_bias)
+        q, k, v, dout = (np.asarray(x, np.float64) for x in (q, k, v, dout))
+        if no_dphi or dden_sign:
+            a = np.ones(v.shape[1]) if aff_scale is None else np.asarray(aff_scale, np.float64)
+            fq, fk = zo.elu_plus_one(q), zo.elu_plus_one(k)
+            dfq = np.ones_like(q) if no_dphi else np.where(q > 0, 1.0, np.exp(np.minimum(q, 0)))
+            state, z = fk.T @ v, fk.sum(axis=0)
+            den = fq @ z
+            o = (fq @ state) / den[:, None]
+            do = dout * a
+            dnum = do / den[:, None]
+            dden = (1.0 if dden_sign else -1.0) * (do * o).sum(axis=1) / den
+            dq = (dnum @ state.T + dden[:, None] * z[None, :]) * dfq
+        if no_db:
+            db = np.zeros_like(db)
+        return dq, dk, dv, da, db
+    return bwd
+
+
 def _top_mass_lowest(mass, top_k):
     m = np.asarray(mass, np.float64)
     return np.sort(m, axis=1)[:, :top_k].sum(axis=1)
@@ -210,6 +266,19 @@ MUTATIONS = {
                                          _spatial_order_with(special_last=True)),
     "spatial output left in the spatial order": ("spatial_tile_sparse_attention",
                                                  _spatial_attention_not_unpermuted),
+    "sparse backward drops the row term D": ("tile_sparse_attention_backward",
+                                             _sparse_bwd_with(no_d=True)),
+    "landmark gradient not spread over its tile": ("tile_sparse_attention_backward",
+                                                   _sparse_bwd_with(no_spread=True)),
+    "dv from the logit gradient": ("tile_sparse_attention_backward",
+                                   _sparse_bwd_with(dv_from_dl=True)),
+    "dq without the softmax scale": ("tile_sparse_attention_backward",
+                                     _sparse_bwd_with(dq_no_scale=True)),
+    "linear backward without phi'": ("linear_attention_backward", _linear_bwd_with(no_dphi=True)),
+    "linear backward normaliser sign": ("linear_attention_backward",
+                                        _linear_bwd_with(dden_sign=True)),
+    "linear backward drops the bias gradient": ("linear_attention_backward",
+                                                _linear_bwd_with(no_db=True)),
 }
 
 
