@@ -202,6 +202,37 @@ zebra_status zebra_fit_affine(const float* x, const float* y, int32_t m, int32_t
                               int32_t* n_degenerate_out, void* stream);
 
 /*
+ * Gradients of one linear stage (for the optional refinement of a converted
+ * model, Zebra3D paper page, Tables 18-19): for out = a (*) o + b with o the
+ * elu+1 linear attention of zebra_linear_attn, the gradients of
+ * sum(dout * out) with respect to q, k, v, a and b. With num = phi(q) S,
+ * den = phi(q) . z, do = a (*) dout:
+ *   dq = (S dnum + z dden) (*) phi'(q),  dnum = do / den,
+ *   dden = -(do . o) / den,  dS = sum phi(q) dnum^T,  dz = sum phi(q) dden,
+ *   dv = dS^T phi(k),  dk = (dS v + dz) (*) phi'(k),
+ *   da = sum dout (*) o,  db = sum dout,
+ * phi'(x) = 1 for x > 0, e^x otherwise. All products and sums are float32
+ * (partial sums over workgroups float64), deterministic.
+ *
+ * q (qs), k, v (kvs)  bf16 inputs of the forward call.
+ * aff_scale   float32 [H][64], or NULL (a = 1). The bias does not enter.
+ * dout (dos)  output gradient, [H][Nq][64], element type g_dtype.
+ * dq (dqs), dk, dv (dkvs)  gradients, element type g_dtype (bf16 or float32).
+ * d_scale, d_bias  float32 [H][64] gradients of a and b, or NULL (skipped).
+ * workspace at least zebra_linear_attn_backward_workspace(Nq, Nk, H, 64)
+ *          bytes, 16-byte aligned. Outputs may not overlap the inputs or
+ *          each other.
+ */
+size_t zebra_linear_attn_backward_workspace(int64_t n_q, int64_t n_kv, int32_t n_heads,
+                                            int32_t head_dim);
+zebra_status zebra_linear_attn_backward(const void* q, zebra_seq qs, const void* k, const void* v,
+                                        zebra_seq kvs, const float* aff_scale, const void* dout,
+                                        zebra_seq dos, zebra_dtype g_dtype, void* dq,
+                                        zebra_seq dqs, void* dk, void* dv, zebra_seq dkvs,
+                                        float* d_scale, float* d_bias, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/*
  * Spatial tiles as a token permutation (Zebra3D paper page: softmax is kept
  * over selected spatial tiles, abstract; block- vs tile-sparse attention,
  * appendix Tables 15-17). Tiles are contiguous runs of the token order, so

@@ -31,7 +31,8 @@ ENTRY_POINTS = (
     "zebra_tile_sparse_attn_workspace", "zebra_tile_sparse_attn", "zebra_tile_sparse_attn_ex",
     "zebra_linear_attn_workspace", "zebra_linear_attn", "zebra_fit_affine", "zebra_fit_scale_only",
     "zebra_block_mass_workspace", "zebra_block_mass", "zebra_spatial_order",
-    "zebra_permute_tokens", "zebra_status_string", "zebra_version",
+    "zebra_permute_tokens", "zebra_linear_attn_backward_workspace", "zebra_linear_attn_backward",
+    "zebra_status_string", "zebra_version",
 )
 
 
@@ -82,6 +83,10 @@ def _declare(lib):
                                      c_sz, c_p]),
         "zebra_spatial_order": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_p, c_i64]),
         "zebra_permute_tokens": (c_i32, [c_p, ZebraSeq, c_p, c_i32, c_i32, c_p, ZebraSeq, c_p]),
+        "zebra_linear_attn_backward_workspace": (c_sz, [c_i64, c_i64, c_i32, c_i32]),
+        "zebra_linear_attn_backward": (c_i32, [c_p, ZebraSeq, c_p, c_p, ZebraSeq, c_p, c_p,
+                                               ZebraSeq, c_i32, c_p, ZebraSeq, c_p, c_p, ZebraSeq,
+                                               c_p, c_p, c_p, c_sz, c_p]),
         "zebra_status_string": (ctypes.c_char_p, [c_i32]),
         "zebra_version": (ctypes.c_char_p, []),
     }
@@ -352,3 +357,33 @@ def zebra_permute_tokens(src: torch.Tensor, order: torch.Tensor, inverse: bool =
         ZEBRA_F32 if src.dtype == torch.float32 else ZEBRA_BF16, _ptr(out), seq_of(out),
         _stream(src.device)))
     return out
+
+
+def zebra_linear_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                               dout: torch.Tensor, aff_scale: Optional[torch.Tensor] = None,
+                               workspace: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv, d_scale, d_bias) of sum(dout * out) for one linear stage;
+    the gradients take dout's dtype (bfloat16 or float32)."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, name)
+    if dout.dtype not in (torch.bfloat16, torch.float32) or not dout.is_cuda:
+        raise ValueError("dout must be a bfloat16 or float32 CUDA tensor")
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k and v must share shape and strides")
+    if aff_scale is not None:
+        _need(aff_scale, torch.float32, "aff_scale")
+    h = q.shape[0]
+    dq = torch.empty(q.shape, dtype=dout.dtype, device=q.device)
+    dk = torch.empty(k.shape, dtype=dout.dtype, device=q.device)
+    dv = torch.empty(k.shape, dtype=dout.dtype, device=q.device)
+    d_scale = torch.empty((h, HEAD_DIM), dtype=torch.float32, device=q.device)
+    d_bias = torch.empty((h, HEAD_DIM), dtype=torch.float32, device=q.device)
+    lib = library()
+    nbytes = lib.zebra_linear_attn_backward_workspace(q.shape[1], k.shape[1], h, HEAD_DIM)
+    workspace = _workspace(nbytes, q.device, workspace)
+    _check("zebra_linear_attn_backward", lib.zebra_linear_attn_backward(
+        _ptr(q), seq_of(q), _ptr(k), _ptr(v), seq_of(k), _ptr(aff_scale), _ptr(dout),
+        seq_of(dout), ZEBRA_F32 if dout.dtype == torch.float32 else ZEBRA_BF16, _ptr(dq),
+        seq_of(dq), _ptr(dk), _ptr(dv), seq_of(dk), _ptr(d_scale), _ptr(d_bias),
+        _ptr(workspace), nbytes, _stream(q.device)))
+    return dq, dk, dv, d_scale, d_bias

@@ -82,6 +82,18 @@ hipError_t launch_tile_sparse(const uint16_t* q, int64_t nq, int64_t qst, int64_
                               int32_t top_k, float scale, void* o, int64_t ost, int64_t osh,
                               bool o_f32, uint32_t flags, void* ws, hipStream_t s);
 size_t linear_workspace_bytes(int64_t n_kv, int32_t heads);
+// forward state S, z of every head into the linear workspace ([H][S | z] float32)
+hipError_t launch_linear_state(const uint16_t* k, const uint16_t* v, int64_t nk, int64_t kst,
+                               int64_t ksh, int32_t heads, void* ws, float** state_out,
+                               hipStream_t s);
+size_t linear_bwd_workspace_bytes(int64_t n_q, int64_t n_kv, int32_t heads);
+hipError_t launch_linear_bwd(const uint16_t* q, int64_t nq, int64_t qst, int64_t qsh,
+                             const uint16_t* k, const uint16_t* v, int64_t nk, int64_t kst,
+                             int64_t ksh, int32_t heads, const float* aff_scale,
+                             const void* dout, int64_t dst, int64_t dsh, void* dq, int64_t qgst,
+                             int64_t qgsh, void* dk, void* dv, int64_t kgst, int64_t kgsh,
+                             bool g_f32, float* d_scale, float* d_bias, void* ws,
+                             hipStream_t s);
 hipError_t launch_linear(const uint16_t* q, int64_t nq, int64_t qst, int64_t qsh,
                          const uint16_t* k, const uint16_t* v, int64_t nk, int64_t kst,
                          int64_t ksh, int32_t heads, const float* aff_scale,

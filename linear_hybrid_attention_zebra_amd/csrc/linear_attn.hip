@@ -375,24 +375,32 @@ size_t linear_workspace_bytes(int64_t n_kv, int32_t heads) {
   return partial + state;
 }
 
-hipError_t launch_linear(const uint16_t* q, int64_t nq, int64_t qst, int64_t qsh,
-                         const uint16_t* k, const uint16_t* v, int64_t nk, int64_t kst,
-                         int64_t ksh, int32_t heads, const float* aff_scale,
-                         const float* aff_bias, void* o, int64_t ost, int64_t osh, bool o_f32,
-                         void* ws, hipStream_t s) {
-  if (heads == 0 || nq == 0) return hipSuccess;
+hipError_t launch_linear_state(const uint16_t* k, const uint16_t* v, int64_t nk, int64_t kst,
+                               int64_t ksh, int32_t heads, void* ws, float** state_out,
+                               hipStream_t s) {
   int32_t nchunks;
   int64_t chunk_tok;
   state_chunking(nk, heads, nchunks, chunk_tok);
   float* partial = (float*)ws;
   float* state = partial + (size_t)heads * nchunks * kStateFloats;
+  *state_out = state;
   hipLaunchKernelGGL(linear_state_kernel, dim3(nchunks, heads), dim3(256), 0, s, k, v, nk, kst,
                      ksh, chunk_tok, nchunks, partial);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(linear_reduce_kernel, dim3((kStateFloats + 255) / 256, heads), dim3(256), 0,
                      s, partial, nchunks, state);
-  err = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_linear(const uint16_t* q, int64_t nq, int64_t qst, int64_t qsh,
+                         const uint16_t* k, const uint16_t* v, int64_t nk, int64_t kst,
+                         int64_t ksh, int32_t heads, const float* aff_scale,
+                         const float* aff_bias, void* o, int64_t ost, int64_t osh, bool o_f32,
+                         void* ws, hipStream_t s) {
+  if (heads == 0 || nq == 0) return hipSuccess;
+  float* state = nullptr;
+  hipError_t err = launch_linear_state(k, v, nk, kst, ksh, heads, ws, &state, s);
   if (err != hipSuccess) return err;
   // about 2 workgroups of 4 waves per CU per head group; each wave loops over
   // 32-query steps with the next step's loads in flight

@@ -351,6 +351,65 @@ zebra_status zebra_fit_scale_only(const float* x, const float* y, int32_t m, int
                     stream);
 }
 
+size_t zebra_linear_attn_backward_workspace(int64_t n_q, int64_t n_kv, int32_t n_heads,
+                                            int32_t head_dim) {
+  if (n_q < 0 || n_kv < 0 || n_heads <= 0 || head_dim != zebra::kHeadDim) return 0;
+  return zebra::linear_bwd_workspace_bytes(n_q, n_kv, n_heads);
+}
+
+zebra_status zebra_linear_attn_backward(const void* q, zebra_seq qs, const void* k, const void* v,
+                                        zebra_seq kvs, const float* aff_scale, const void* dout,
+                                        zebra_seq dos, zebra_dtype g_dtype, void* dq,
+                                        zebra_seq dqs, void* dk, void* dv, zebra_seq dkvs,
+                                        float* d_scale, float* d_bias, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  zebra_status st;
+  if ((st = check_seq(q, qs, false)) != ZEBRA_OK) return st;
+  if ((st = check_seq(k, kvs, false)) != ZEBRA_OK) return st;
+  if ((st = check_seq(v, kvs, false)) != ZEBRA_OK) return st;
+  if ((st = check_seq(dout, dos, false)) != ZEBRA_OK) return st;
+  if ((st = check_seq(dq, dqs, true)) != ZEBRA_OK) return st;
+  if ((st = check_seq(dk, dkvs, true)) != ZEBRA_OK) return st;
+  if ((st = check_seq(dv, dkvs, true)) != ZEBRA_OK) return st;
+  if (g_dtype != ZEBRA_BF16 && g_dtype != ZEBRA_F32) return ZEBRA_ERR_INVALID_ARG;
+  const int32_t h = qs.n_heads;
+  if (kvs.n_heads != h || dos.n_heads != h || dqs.n_heads != h || dkvs.n_heads != h ||
+      dos.n_tokens != qs.n_tokens || dqs.n_tokens != qs.n_tokens ||
+      dkvs.n_tokens != kvs.n_tokens)
+    return ZEBRA_ERR_INVALID_ARG;
+  if (seq_empty(qs) && seq_empty(kvs)) return ZEBRA_OK;
+  if (kvs.n_tokens == 0) return ZEBRA_ERR_INVALID_ARG;  // the normaliser would be zero
+  const size_t need = zebra::linear_bwd_workspace_bytes(qs.n_tokens, kvs.n_tokens, h);
+  if (workspace == nullptr || workspace_bytes < need) return ZEBRA_ERR_WORKSPACE;
+  if (((uintptr_t)workspace % 16) != 0) return ZEBRA_ERR_INVALID_ARG;
+  if (((uintptr_t)aff_scale % 4) != 0 || ((uintptr_t)d_scale % 4) != 0 ||
+      ((uintptr_t)d_bias % 4) != 0)
+    return ZEBRA_ERR_INVALID_ARG;
+  const size_t gel = g_dtype == ZEBRA_F32 ? 4 : 2;
+  if (g_dtype == ZEBRA_F32) {
+    for (const zebra_seq* g : {&dos, &dqs, &dkvs})
+      if (g->stride_token % 8 != 0 || g->stride_head % 8 != 0) return ZEBRA_ERR_UNSUPPORTED;
+  }
+  const uint64_t hn = (uint64_t)h * zebra::kHeadDim;
+  const Range outs[] = {seq_range(dq, dqs, gel), seq_range(dk, dkvs, gel),
+                        seq_range(dv, dkvs, gel), flat_range(d_scale, hn, 4),
+                        flat_range(d_bias, hn, 4), flat_range(workspace, need, 1)};
+  const Range ins[] = {seq_range(q, qs, 2), seq_range(k, kvs, 2), seq_range(v, kvs, 2),
+                       seq_range(dout, dos, gel), flat_range(aff_scale, hn, 4)};
+  for (size_t i = 0; i < 6; ++i) {
+    for (const Range& r : ins)
+      if (overlaps(outs[i], r)) return ZEBRA_ERR_INVALID_ARG;
+    for (size_t j = i + 1; j < 6; ++j)
+      if (overlaps(outs[i], outs[j])) return ZEBRA_ERR_INVALID_ARG;
+  }
+  return hip_status(zebra::launch_linear_bwd(
+      (const uint16_t*)q, qs.n_tokens, qs.stride_token, qs.stride_head, (const uint16_t*)k,
+      (const uint16_t*)v, kvs.n_tokens, kvs.stride_token, kvs.stride_head, h, aff_scale, dout,
+      dos.stride_token, dos.stride_head, dq, dqs.stride_token, dqs.stride_head, dk, dv,
+      dkvs.stride_token, dkvs.stride_head, g_dtype == ZEBRA_F32, d_scale, d_bias, workspace,
+      (hipStream_t)stream));
+}
+
 zebra_status zebra_spatial_order(int32_t n_views, int32_t n_special, int32_t grid_h,
                                  int32_t grid_w, int32_t block, int32_t* order_out,
                                  int64_t order_len) {

@@ -11,7 +11,7 @@ import torch
 import oracle.zebra_oracle as zo
 import linear_hybrid_attention_zebra_amd as zb
 from linear_hybrid_attention_zebra_amd import stage, synth
-from parity_util import assert_close, bf16_gpu, check_selection, to_f64
+from parity_util import assert_close, assert_grad_close, bf16_gpu, check_selection, to_f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -527,3 +527,36 @@ def test_block_mass_retained_by_gpu_selection():
         assert np.all(kept_ref <= best + 1e-12)
         print(f"[parity] head {h}: retained {kept_ref.mean():.4f} of top {best.mean():.4f}",
               flush=True)
+
+
+# ----------------------------------------------------------------------------
+# gradients
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n_q,n_kv,affine,g_dtype", [
+    (300, 500, True, torch.float32), (1, 5, False, torch.float32), (70, 64, True, torch.bfloat16),
+    (5000, 3000, True, torch.float32), (0, 100, True, torch.float32),
+])
+def test_linear_backward_parity(n_q, n_kv, affine, g_dtype):
+    print(f"[case] linear backward Nq={n_q} Nk={n_kv} affine={affine} {g_dtype}", flush=True)
+    rng = np.random.default_rng(n_q + n_kv)
+    heads = 2
+    q = synth.bf16_round(rng.standard_normal((heads, n_q, 64)).astype(np.float32))
+    k = synth.bf16_round(rng.standard_normal((heads, n_kv, 64)).astype(np.float32))
+    v = synth.bf16_round(rng.standard_normal((heads, n_kv, 64)).astype(np.float32))
+    dout = rng.standard_normal((heads, n_q, 64)).astype(np.float32)
+    if g_dtype == torch.bfloat16:
+        dout = synth.bf16_round(dout)
+    a = rng.uniform(0.5, 1.5, (heads, 64)).astype(np.float32) if affine else None
+    dq, dk, dv, da, db = zb.zebra_linear_attn_backward(
+        bf16_gpu(q), bf16_gpu(k), bf16_gpu(v), torch.from_numpy(dout).to(DEV).to(g_dtype),
+        None if a is None else torch.from_numpy(a).to(DEV))
+    torch.cuda.synchronize()
+    for h in range(heads):
+        rq, rk, rv, ra, rb = zo.linear_attention_backward(q[h], k[h], v[h], dout[h],
+                                                          None if a is None else a[h])
+        assert_grad_close(dq[h], rq, f"linear dq head {h}")
+        assert_grad_close(dk[h], rk, f"linear dk head {h}")
+        assert_grad_close(dv[h], rv, f"linear dv head {h}")
+        assert_grad_close(da[h], ra, f"linear da head {h}")
+        assert_grad_close(db[h], rb, f"linear db head {h}")
