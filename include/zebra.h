@@ -202,6 +202,40 @@ zebra_status zebra_fit_affine(const float* x, const float* y, int32_t m, int32_t
                               int32_t* n_degenerate_out, void* stream);
 
 /*
+ * Gradients of one tile-sparse stage (for the optional refinement of a
+ * converted model, Zebra3D paper page, Tables 18-19): for out of
+ * zebra_tile_sparse_attn_ex with the same arguments and flags, the gradients
+ * of sum(dout * out) with respect to q, k and v, the selection sel held fixed
+ * (top-k is not differentiable). Per query row with columns c and
+ * P = softmax over them:
+ *   dP_c = dout . v_c,  D = dout . out,  dS_c = P_c (dP_c - D),
+ *   dq = scale sum_c dS_c k_c,  dk_c = scale dS_c q,  dv_c = P_c dout,
+ * and every token of tile j receives 1/n_j of its landmark column's dk and
+ * dv (the landmark is the tile mean). The call runs the forward itself (its
+ * float32 output and normaliser go to the workspace); dout enters the bf16
+ * MFMA products rounded to bf16, sums are float32 in a fixed order
+ * (deterministic). sel is required (also when top_k == t_k).
+ *
+ * Arguments as zebra_tile_sparse_attn_ex, plus:
+ * dout (dos)  output gradient [H][Nq][64], element type g_dtype.
+ * dq (dqs), dk, dv (dkvs)  gradients, element type g_dtype (bf16 or float32).
+ * workspace at least zebra_tile_sparse_attn_backward_workspace(Nq, Nk, H,
+ *          64, q_tile, k_tile, top_k) bytes, 16-byte aligned (it includes the
+ *          forward's workspace and 4 bytes per selection entry for the
+ *          per-key-tile query lists). Outputs may not overlap the inputs or
+ *          each other.
+ */
+size_t zebra_tile_sparse_attn_backward_workspace(int64_t n_q, int64_t n_kv, int32_t n_heads,
+                                                 int32_t head_dim, int32_t q_tile, int32_t k_tile,
+                                                 int32_t top_k);
+zebra_status zebra_tile_sparse_attn_backward(
+    const void* q, zebra_seq qs, const void* k, const void* v, zebra_seq kvs, const float* kbar,
+    const float* vbar, const int32_t* sel, int32_t q_tile, int32_t k_tile, int32_t top_k,
+    float scale, uint32_t flags, const void* dout, zebra_seq dos, zebra_dtype g_dtype, void* dq,
+    zebra_seq dqs, void* dk, void* dv, zebra_seq dkvs, void* workspace, size_t workspace_bytes,
+    void* stream);
+
+/*
  * Gradients of one linear stage (for the optional refinement of a converted
  * model, Zebra3D paper page, Tables 18-19): for out = a (*) o + b with o the
  * elu+1 linear attention of zebra_linear_attn, the gradients of

@@ -32,6 +32,7 @@ ENTRY_POINTS = (
     "zebra_linear_attn_workspace", "zebra_linear_attn", "zebra_fit_affine", "zebra_fit_scale_only",
     "zebra_block_mass_workspace", "zebra_block_mass", "zebra_spatial_order",
     "zebra_permute_tokens", "zebra_linear_attn_backward_workspace", "zebra_linear_attn_backward",
+    "zebra_tile_sparse_attn_backward_workspace", "zebra_tile_sparse_attn_backward",
     "zebra_status_string", "zebra_version",
 )
 
@@ -83,6 +84,13 @@ def _declare(lib):
                                      c_sz, c_p]),
         "zebra_spatial_order": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_p, c_i64]),
         "zebra_permute_tokens": (c_i32, [c_p, ZebraSeq, c_p, c_i32, c_i32, c_p, ZebraSeq, c_p]),
+        "zebra_tile_sparse_attn_backward_workspace": (c_sz, [c_i64, c_i64, c_i32, c_i32, c_i32,
+                                                             c_i32, c_i32]),
+        "zebra_tile_sparse_attn_backward": (c_i32, [c_p, ZebraSeq, c_p, c_p, ZebraSeq, c_p, c_p,
+                                                    c_p, c_i32, c_i32, c_i32, c_f,
+                                                    ctypes.c_uint32, c_p, ZebraSeq, c_i32, c_p,
+                                                    ZebraSeq, c_p, c_p, ZebraSeq, c_p, c_sz,
+                                                    c_p]),
         "zebra_linear_attn_backward_workspace": (c_sz, [c_i64, c_i64, c_i32, c_i32]),
         "zebra_linear_attn_backward": (c_i32, [c_p, ZebraSeq, c_p, c_p, ZebraSeq, c_p, c_p,
                                                ZebraSeq, c_i32, c_p, ZebraSeq, c_p, c_p, ZebraSeq,
@@ -387,3 +395,35 @@ def zebra_linear_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
         seq_of(dq), _ptr(dk), _ptr(dv), seq_of(dk), _ptr(d_scale), _ptr(d_bias),
         _ptr(workspace), nbytes, _stream(q.device)))
     return dq, dk, dv, d_scale, d_bias
+
+
+def zebra_tile_sparse_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                    kbar: Optional[torch.Tensor], vbar: Optional[torch.Tensor],
+                                    sel: torch.Tensor, q_tile: int, k_tile: int, top_k: int,
+                                    scale: float, dout: torch.Tensor, flags: int = 0,
+                                    workspace: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv) of sum(dout * out) for one tile-sparse stage, sel fixed;
+    the gradients take dout's dtype (bfloat16 or float32)."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, name)
+    _need(sel, torch.int32, "sel")
+    if dout.dtype not in (torch.bfloat16, torch.float32) or not dout.is_cuda:
+        raise ValueError("dout must be a bfloat16 or float32 CUDA tensor")
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k and v must share shape and strides")
+    for t, name in ((kbar, "kbar"), (vbar, "vbar")):
+        if t is not None:
+            _need(t, torch.float32, name)
+    dq = torch.empty(q.shape, dtype=dout.dtype, device=q.device)
+    dk = torch.empty(k.shape, dtype=dout.dtype, device=q.device)
+    dv = torch.empty(k.shape, dtype=dout.dtype, device=q.device)
+    lib = library()
+    nbytes = lib.zebra_tile_sparse_attn_backward_workspace(q.shape[1], k.shape[1], q.shape[0],
+                                                           HEAD_DIM, q_tile, k_tile, top_k)
+    workspace = _workspace(nbytes, q.device, workspace)
+    _check("zebra_tile_sparse_attn_backward", lib.zebra_tile_sparse_attn_backward(
+        _ptr(q), seq_of(q), _ptr(k), _ptr(v), seq_of(k), _ptr(kbar), _ptr(vbar), _ptr(sel),
+        q_tile, k_tile, top_k, scale, flags, _ptr(dout), seq_of(dout),
+        ZEBRA_F32 if dout.dtype == torch.float32 else ZEBRA_BF16, _ptr(dq), seq_of(dq), _ptr(dk),
+        _ptr(dv), seq_of(dk), _ptr(workspace), nbytes, _stream(q.device)))
+    return dq, dk, dv

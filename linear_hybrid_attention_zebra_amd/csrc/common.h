@@ -80,7 +80,18 @@ hipError_t launch_tile_sparse(const uint16_t* q, int64_t nq, int64_t qst, int64_
                               int64_t ksh, int32_t heads, const float* kbar, const float* vbar,
                               const int32_t* sel, int32_t q_tile, int32_t k_tile,
                               int32_t top_k, float scale, void* o, int64_t ost, int64_t osh,
-                              bool o_f32, uint32_t flags, void* ws, hipStream_t s);
+                              bool o_f32, uint32_t flags, void* ws, hipStream_t s,
+                              float* lse = nullptr);
+size_t sparse_bwd_workspace_bytes(int64_t n_q, int64_t n_kv, int32_t heads, int32_t q_tile,
+                                  int32_t k_tile, int32_t top_k);
+hipError_t launch_tile_sparse_bwd(const uint16_t* q, int64_t nq, int64_t qst, int64_t qsh,
+                                  const uint16_t* k, const uint16_t* v, int64_t nk, int64_t kst,
+                                  int64_t ksh, int32_t heads, const float* kbar,
+                                  const float* vbar, const int32_t* sel, int32_t q_tile,
+                                  int32_t k_tile, int32_t top_k, float scale, uint32_t flags,
+                                  const void* dout, int64_t dst, int64_t dsh, bool g_f32,
+                                  void* dq, int64_t qgst, int64_t qgsh, void* dk, void* dv,
+                                  int64_t kgst, int64_t kgsh, void* ws, hipStream_t s);
 size_t linear_workspace_bytes(int64_t n_kv, int32_t heads);
 // forward state S, z of every head into the linear workspace ([H][S | z] float32)
 hipError_t launch_linear_state(const uint16_t* k, const uint16_t* v, int64_t nk, int64_t kst,

@@ -106,6 +106,7 @@ struct SparseParams {
   const int32_t* coff;     // [H][tq][n_chunks + 1]: first kept entry of each chunk
   float* part_o;           // [H][nq][n_chunks][64] unnormalised outputs
   float2* part_ml;         // [H][nq][n_chunks] (reference, row sum), p = 2^(c s - reference)
+  float* lse;              // [H][nq] log2 of the softmax normaliser (log2 units), or null
 };
 
 // Byte offset of 16-byte chunk `chunk` of 128-byte row `row` in a tile. The
@@ -645,6 +646,8 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
       }
       continue;
     }
+    if (p.lse != nullptr && qvalid && hh == 0)
+      p.lse[(int64_t)h * p.nq + qrow] = (fast ? -nm_fast : mc_run) + __builtin_log2f(l_sum);
     const float inv = 1.0f / l_sum;
     if (qvalid) {
       if (p.o_f32) {
@@ -711,7 +714,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const float2* __restrict__ part_ml,
                                                       int32_t n_chunks, int64_t nq, int64_t rows,
                                                       void* o, int64_t ost, int64_t osh,
-                                                      int32_t o_f32) {
+                                                      int32_t o_f32, float* __restrict__ lse) {
   const int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // (head, query)
   if (r >= rows) return;
   const int sub = threadIdx.x & 15;
@@ -732,6 +735,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
   const float inv = l > 0.f ? 1.0f / l : 0.f;  // l == 0 only without any column
   const int64_t h = r / nq, q = r - h * nq;
+  if (lse != nullptr && sub == 0) lse[r] = ref + __builtin_log2f(l);
   if (o_f32) {
     float* op = (float*)o + h * osh + q * ost + 4 * sub;
     *(f32x4*)op = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
@@ -820,7 +824,8 @@ hipError_t launch_tile_sparse(const uint16_t* q, int64_t nq, int64_t qst, int64_
                               int64_t ksh, int32_t heads, const float* kbar, const float* vbar,
                               const int32_t* sel, int32_t q_tile, int32_t k_tile,
                               int32_t top_k, float scale, void* o, int64_t ost, int64_t osh,
-                              bool o_f32, uint32_t flags, void* ws, hipStream_t s) {
+                              bool o_f32, uint32_t flags, void* ws, hipStream_t s,
+                              float* lse) {
   SparseParams p;
   p.q = q;
   p.k = k;
@@ -842,6 +847,7 @@ hipError_t launch_tile_sparse(const uint16_t* q, int64_t nq, int64_t qst, int64_
   p.coff = nullptr;
   p.part_o = nullptr;
   p.part_ml = nullptr;
+  p.lse = lse;
   p.top_k = top_k;
   p.scale_log2 = scale * kLog2e;
   p.o_f32 = o_f32 ? 1 : 0;
@@ -901,7 +907,7 @@ hipError_t launch_tile_sparse(const uint16_t* q, int64_t nq, int64_t qst, int64_
   const int64_t qrows = (int64_t)heads * nq;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((qrows + 15) / 16)), dim3(256), 0, s,
                      (const float*)p.part_o, (const float2*)p.part_ml, sp.n_chunks, nq, qrows, o,
-                     ost, osh, p.o_f32);
+                     ost, osh, p.o_f32, lse);
   return hipGetLastError();
 }
 

@@ -1,0 +1,769 @@
+// Backward pass of tile-sparse attention with landmarks (gfx950).
+//
+// For the optional refinement of a converted model (Zebra3D paper page,
+// Tables 18-19): the gradients of sum(dout * out) for one tile-sparse stage,
+// the selection held fixed. Per query row with columns c (kept tokens, then
+// one landmark per omitted tile; Figure 1 caption) and P = softmax:
+//   dP_c = dout . v_c,  D = dout . out,  dS_c = P_c (dP_c - D),
+//   dq = scale sum_c dS_c k_c,  dk_c = scale dS_c q,  dv_c = P_c dout.
+// A landmark's key and value are the means of its tile, so every token of
+// tile j receives 1/n_j of the landmark's dk and dv.
+//
+// Steps (the forward runs first, writing the log2 softmax normaliser lse of
+// every query, so P_c = 2^(c s_c + bias_c - lse); dout enters the products
+// in bf16):
+//  1. the kept-tile bit matrix [H][Tq][Tk/32] and, by a stable counting sort
+//     over it, for every key tile the ascending list of query tiles keeping it;
+//  2. dq: one workgroup per (head, query tile), two sweeps over its kept
+//     tiles and landmark blocks: D = sum_c P_c dP_c (equal to dout . out, but
+//     from the same float32 P and dP as the gradient), then dS and dq;
+//  3. dk, dv of the landmark rows: one workgroup per (head, block of KT
+//     landmark rows), over every query tile, the kept tiles masked;
+//  4. dk, dv of the key tiles: one workgroup per (head, key tile), over the
+//     query tiles keeping it, plus the tile's landmark share from step 3.
+// Steps 2-4 recompute S and dP with bf16 MFMA 32x32x16 and accumulate in
+// float32; dS enters its products as a bf16 pair (float32-grade), P as bf16
+// (as in the forward). Sums run in a fixed order: no atomics in any
+// floating-point sum, so the gradients are bitwise reproducible.
+#include <algorithm>
+#include <type_traits>
+
+#include "common.h"
+
+namespace zebra {
+
+namespace {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+constexpr float kLog2eB = 1.4426950408889634f;
+
+// 16-byte chunk `chunk` of 128-byte row `row`, XOR swizzled as in the forward
+__device__ __forceinline__ int swz_f(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ uint32_t swz(int row, int chunk) {
+  return (uint32_t)(row * 128 + ((chunk ^ swz_f(row)) << 4));
+}
+
+// 8 channels of a bf16 or float32 row as bf16 (round to nearest even)
+__device__ __forceinline__ u32x4 load8_bf16(const void* base, int64_t elem, bool f32) {
+  if (!f32) return *(const u32x4*)((const uint16_t*)base + elem);
+  const f32x4 a = *(const f32x4*)((const float*)base + elem);
+  const f32x4 b = *(const f32x4*)((const float*)base + elem + 4);
+  return u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+               pack_bf16x2(b[2], b[3])};
+}
+
+// Operand of a 32x32x16 MFMA whose contraction runs over the rows of an LDS
+// tile (rows x 64 channels, swizzled): lane l holds, for channel
+// 32 db + 16 (G % 2) + 4 (S % 4) + {0..3} (G = l / 16, S = l % 16), the 8 rows
+// 16 m + 4 (G / 2) + S / 4 + {0, 8} ... in the order that matches the
+// C-layout of a 32x32 score block (the forward's V^T read).
+__device__ __forceinline__ bf16x8 tr_operand(const lds_u8* tile, int m, int db, int lane) {
+  const int G = lane >> 4, S = lane & 15;
+  const int col = 32 * db + 16 * (G & 1) + 4 * (S & 3);
+  const int chunk = col >> 3, half = (col & 7) ? 8 : 0;
+  const int r0 = 16 * m + 4 * (G >> 1) + (S >> 2);
+  const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(tile + swz(r0, chunk) + half));
+  const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(tile + swz(r0 + 8, chunk) + half));
+  const u32x2 w0 = __builtin_bit_cast(u32x2, t0), w1 = __builtin_bit_cast(u32x2, t1);
+  return as_bf16x8(u32x4{w0.x, w0.y, w1.x, w1.y});
+}
+
+// Row operand: lane l holds channels 16 s + 8 (l / 32) .. +7 of tile row `row`
+__device__ __forceinline__ bf16x8 row_operand(const lds_u8* tile, int row, int s, int hh) {
+  return as_bf16x8(*(const __attribute__((address_space(3))) u32x4*)(tile + swz(row, 2 * s + hh)));
+}
+
+// 16 scores of one 32x32 C-layout block -> two bf16 operands (16 rows each)
+__device__ __forceinline__ void pack16(const float* x, bf16x8& lo8, bf16x8& hi8) {
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+  lo8 = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+  hi8 = as_bf16x8(u32x4{w[4], w[5], w[6], w[7]});
+}
+
+// The same, float32-grade: x = big + small with both parts bf16 (x - big is
+// exact in float32 and rounds to within 2^-17 of x), so two MFMAs give the
+// product to float32 accuracy. dS = P (dP - D) cancels, which bf16 alone
+// would amplify.
+__device__ __forceinline__ void pack16_split(const float* x, bf16x8& lo8, bf16x8& hi8,
+                                             bf16x8& lo8s, bf16x8& hi8s) {
+  uint32_t w[8], r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    w[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+    r[i] = pack_bf16x2(x[2 * i] - bf16lo(w[i]), x[2 * i + 1] - bf16hi(w[i]));
+  }
+  lo8 = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+  hi8 = as_bf16x8(u32x4{w[4], w[5], w[6], w[7]});
+  lo8s = as_bf16x8(u32x4{r[0], r[1], r[2], r[3]});
+  hi8s = as_bf16x8(u32x4{r[4], r[5], r[6], r[7]});
+}
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* kbar_b;  // bf16 landmark rows [H][tk][64], or null without landmarks
+  const uint16_t* vbar_b;
+  const int32_t* sel;      // [H][tq][top_k]
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t nq, qst, qsh;
+  int64_t nk, kst, ksh;
+  int64_t dst, dsh;        // dout strides
+  int64_t qgst, qgsh;      // dq strides
+  int64_t kgst, kgsh;      // dk, dv strides
+  int32_t heads, tq, tk, top_k, bit_words;
+  float c;                 // scale * log2(e)
+  float scale;
+  int32_t g_f32, landmarks, log_count;
+  float lm_log2_kt, lm_tail_corr;  // log-count biases (log2 units; tail in score units)
+  float* lse;              // [H][nq]; the dq kernel renormalises it in place
+  float* dsum;             // D [H][nq], written by the dq kernel
+  const uint32_t* bits;    // [H][tq][bit_words] kept tiles
+  const int32_t* list_off; // [H][tk + 1]
+  const int32_t* list;     // [H][tq * top_k] query tiles keeping each key tile
+  float* dkbar;            // [H][tk][64] float32 landmark gradients
+  float* dvbar;
+};
+
+// ---------------------------------------------------------------------------
+// 2. kept-tile bits, per-key-tile counts, offsets, ordered lists
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_fill_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256)
+    p[e] = 0u;
+}
+
+__global__ __launch_bounds__(256) void bwd_bits_kernel(const int32_t* __restrict__ sel,
+                                                       int64_t rows, int32_t tq, int32_t tk,
+                                                       int32_t top_k, int32_t bit_words,
+                                                       uint32_t* __restrict__ bits,
+                                                       int32_t* __restrict__ count) {
+  const int64_t row = blockIdx.x;  // (head, query tile)
+  if (row >= rows) return;
+  const int64_t h = row / tq;
+  for (int e = threadIdx.x; e < top_k; e += 256) {
+    const int j = min(max(sel[row * top_k + e], 0), tk - 1);
+    atomicOr(&bits[row * bit_words + (j >> 5)], 1u << (j & 31));
+    atomicAdd(&count[h * tk + j], 1);
+  }
+}
+
+// exclusive scan of the counts of one head -> list offsets (head h starts at
+// h * tq * top_k); off has tk + 1 entries per head
+__global__ __launch_bounds__(256) void bwd_scan_kernel(const int32_t* __restrict__ count,
+                                                       int32_t tk, int64_t per_head,
+                                                       int32_t* __restrict__ off) {
+  __shared__ int32_t part[256];
+  const int h = blockIdx.x, t = threadIdx.x;
+  const int per = (tk + 255) / 256;
+  const int j0 = min(tk, t * per), j1 = min(tk, j0 + per);
+  int s = 0;
+  for (int j = j0; j < j1; ++j) s += count[(int64_t)h * tk + j];
+  part[t] = s;
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int x = part[i];
+      part[i] = run;
+      run += x;
+    }
+  }
+  __syncthreads();
+  int64_t run = (int64_t)h * per_head + part[t];
+  int32_t* oh = off + (int64_t)h * (tk + 1);
+  for (int j = j0; j < j1; ++j) {
+    oh[j] = (int32_t)run;
+    run += count[(int64_t)h * tk + j];
+  }
+  if (t == 255) oh[tk] = (int32_t)run;  // end of the head's last list
+}
+
+// one workgroup of 64 threads per (head, bit word): thread t owns a contiguous
+// range of query tiles; two passes give every key tile of the word its query
+// tiles in ascending order
+__global__ __launch_bounds__(64) void bwd_list_kernel(const uint32_t* __restrict__ bits,
+                                                      int32_t tq, int32_t tk, int32_t bit_words,
+                                                      const int32_t* __restrict__ off,
+                                                      int32_t* __restrict__ list) {
+  __shared__ int32_t cnt[64][33];
+  const int w = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const int per = (tq + 63) / 64;
+  const int i0 = min(tq, t * per), i1 = min(tq, i0 + per);
+  const uint32_t* bh = bits + (int64_t)h * tq * bit_words + w;
+  int c[32];
+#pragma unroll
+  for (int b = 0; b < 32; ++b) c[b] = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t word = bh[(int64_t)i * bit_words];
+#pragma unroll
+    for (int b = 0; b < 32; ++b) c[b] += (word >> b) & 1u;
+  }
+#pragma unroll
+  for (int b = 0; b < 32; ++b) cnt[t][b] = c[b];
+  __syncthreads();
+  if (t < 32) {  // exclusive scan over threads for bit t
+    int run = 0;
+    for (int i = 0; i < 64; ++i) {
+      const int x = cnt[i][t];
+      cnt[i][t] = run;
+      run += x;
+    }
+  }
+  __syncthreads();
+  const int32_t* oh = off + (int64_t)h * (tk + 1);
+#pragma unroll
+  for (int b = 0; b < 32; ++b) {
+    const int j = 32 * w + b;
+    c[b] = j < tk ? oh[j] + cnt[t][b] : 0;
+  }
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t word = bh[(int64_t)i * bit_words];
+#pragma unroll
+    for (int b = 0; b < 32; ++b)
+      if ((word >> b) & 1u) list[c[b]++] = i;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3-4. dk, dv: one workgroup per (head, column block); wave w owns 32 columns
+// ---------------------------------------------------------------------------
+template <int QT, int KT, bool LM>
+__global__ __launch_bounds__(KT * 2) void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int W = KT / 32;
+  constexpr int NT = W * kWave;
+  constexpr int QC = QT / 32;  // 32-query chunks per query tile
+  __shared__ u32x4 qs_t[QT * 8], ds_t[QT * 8];  // Q and dout tiles (QT rows x 128 B)
+  __shared__ float lse_s[QT], dsum_s[QT];
+  const lds_u8* qtile = (const lds_u8*)qs_t;
+  const lds_u8* dtile = (const lds_u8*)ds_t;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int hh = lane >> 5, kl = lane & 31;
+  const int n_blocks = LM ? (p.tk + KT - 1) / KT : p.tk;
+  const bool gf = p.g_f32 != 0;
+  const int h = blockIdx.y;
+  for (int cb = blockIdx.x; cb < n_blocks; cb += gridDim.x) {
+    // this lane's column (key token or landmark row) and its validity
+    const int col = KT * cb + 32 * wave + kl;
+    int rows_valid;  // valid columns of the block
+    const uint16_t* kb;
+    const uint16_t* vb;
+    int64_t kstride;
+    if constexpr (LM) {
+      rows_valid = min(KT, p.tk - KT * cb);
+      kb = p.kbar_b + (int64_t)h * p.tk * kHeadDim;
+      vb = p.vbar_b + (int64_t)h * p.tk * kHeadDim;
+      kstride = kHeadDim;
+    } else {
+      rows_valid = (int)min<int64_t>(KT, p.nk - (int64_t)KT * cb);
+      kb = p.k + (int64_t)h * p.ksh;
+      vb = p.v + (int64_t)h * p.ksh;
+      kstride = p.kst;
+    }
+    const int lcol = 32 * wave + kl;  // column within the block
+    const bool cvalid = lcol < rows_valid;
+    // B operands K^T and V^T of this lane's column: channels 16 s + 8 hh .. +7
+    bf16x8 kop[4], vop[4];
+    {
+      const int64_t row = (int64_t)KT * cb + (cvalid ? lcol : 0);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+        if (cvalid) {
+          a = *(const u32x4*)(kb + row * kstride + 16 * s + 8 * hh);
+          b = *(const u32x4*)(vb + row * kstride + 16 * s + 8 * hh);
+        }
+        kop[s] = as_bf16x8(a);
+        vop[s] = as_bf16x8(b);
+      }
+    }
+    // logit bias of the column in log2 units (landmarks under the log count)
+    float bias = 0.f;
+    if constexpr (LM) {
+      if (p.log_count) {
+        bias = p.lm_log2_kt;
+        const int64_t tail = p.nk - (int64_t)(p.tk - 1) * KT;
+        if (col == p.tk - 1 && tail < KT) bias += p.lm_tail_corr * p.c;
+      }
+    }
+    f32x16 dkacc[2], dvacc[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dkacc[0][i] = 0.f;
+      dkacc[1][i] = 0.f;
+      dvacc[0][i] = 0.f;
+      dvacc[1][i] = 0.f;
+    }
+    int n_i, i_base;
+    if constexpr (LM) {
+      n_i = p.tq;
+      i_base = 0;
+    } else {
+      const int32_t* oh = p.list_off + (int64_t)h * (p.tk + 1);
+      i_base = oh[cb];
+      n_i = oh[cb + 1] - i_base;
+    }
+    for (int ii = 0; ii < n_i; ++ii) {
+      // (a selection with repeated entries would leave list slots unwritten)
+      const int qt = LM ? ii : min(max(p.list[i_base + ii], 0), p.tq - 1);
+      // kept mask of this lane's landmark column for query tile qt
+      bool masked = !cvalid;
+      if constexpr (LM) {
+        const int wi = (KT * cb + 32 * wave) / 32;  // the word of this wave's 32 columns
+        const uint32_t word =
+            wi < p.bit_words ? p.bits[((int64_t)h * p.tq + qt) * p.bit_words + wi] : 0u;
+        masked = masked || ((word >> kl) & 1u);
+      }
+      __syncthreads();  // previous tiles consumed
+      for (int e = tid; e < QT * 8; e += NT) {
+        const int r = e >> 3, c8 = e & 7;
+        const int64_t qrow = (int64_t)qt * QT + r;
+        u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+        if (qrow < p.nq) {
+          a = *(const u32x4*)(p.q + (int64_t)h * p.qsh + qrow * p.qst + 8 * c8);
+          b = load8_bf16(p.dout, (int64_t)h * p.dsh + qrow * p.dst + 8 * c8, gf);
+        }
+        *(__attribute__((address_space(3))) u32x4*)(qtile + swz(r, c8)) = a;
+        *(__attribute__((address_space(3))) u32x4*)(dtile + swz(r, c8)) = b;
+      }
+      for (int r = tid; r < QT; r += NT) {
+        const int64_t qrow = (int64_t)qt * QT + r;
+        const bool ok = qrow < p.nq;
+        lse_s[r] = ok ? p.lse[(int64_t)h * p.nq + qrow] : INFINITY;
+        dsum_s[r] = ok ? p.dsum[(int64_t)h * p.nq + qrow] : 0.f;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int qc = 0; qc < QC; ++qc) {
+        // S = Q K^T and dP = dout V^T for 32 queries x this wave's 32 columns:
+        // lane = column, register v = query 32 qc + 8 (v / 4) + 4 hh + v % 4
+        f32x16 sacc, pacc;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 aq = row_operand(qtile, 32 * qc + kl, s, hh);
+          const bf16x8 ad = row_operand(dtile, 32 * qc + kl, s, hh);
+          if (s == 0) {
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kop[0], f32x16{}, 0, 0, 0);
+            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vop[0], f32x16{}, 0, 0, 0);
+          } else {
+            sacc = mfma32(aq, kop[s], sacc);
+            pacc = mfma32(ad, vop[s], pacc);
+          }
+        }
+        float pr[16], dsr[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int q0 = 32 * qc + 8 * g + 4 * hh;
+          const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4*)&lse_s[q0];
+          const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4*)&dsum_s[q0];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * g + r;
+            const float pv = masked ? 0.f
+                                    : __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], p.c, bias) -
+                                                             l4[r]);
+            pr[i] = pv;
+            dsr[i] = pv * (pacc[i] - d4[r]);
+          }
+        }
+        bf16x8 plo, phi, slo, shi, slo2, shi2;
+        pack16(pr, plo, phi);
+        pack16_split(dsr, slo, shi, slo2, shi2);
+        // dV += P^T dout, dK += dS^T Q over these 32 queries (two 16-query chunks)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const bf16x8 d0 = tr_operand(dtile, 2 * qc, db, lane);
+          const bf16x8 d1 = tr_operand(dtile, 2 * qc + 1, db, lane);
+          const bf16x8 q0 = tr_operand(qtile, 2 * qc, db, lane);
+          const bf16x8 q1 = tr_operand(qtile, 2 * qc + 1, db, lane);
+          dvacc[db] = mfma32(plo, d0, dvacc[db]);
+          dvacc[db] = mfma32(phi, d1, dvacc[db]);
+          dkacc[db] = mfma32(slo, q0, dkacc[db]);
+          dkacc[db] = mfma32(shi, q1, dkacc[db]);
+          dkacc[db] = mfma32(slo2, q0, dkacc[db]);
+          dkacc[db] = mfma32(shi2, q1, dkacc[db]);
+        }
+      }
+    }
+    // epilogue: lane holds channel 32 db + kl of rows (columns of the block)
+    // 32 wave + 8 (v / 4) + 4 hh + v % 4
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int ch = 32 * db + kl;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int lc = 32 * wave + 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (lc >= rows_valid) continue;
+        const int64_t row = (int64_t)KT * cb + lc;
+        float gk = p.scale * dkacc[db][v];
+        float gv = dvacc[db][v];
+        if constexpr (LM) {
+          p.dkbar[((int64_t)h * p.tk + row) * kHeadDim + ch] = gk;
+          p.dvbar[((int64_t)h * p.tk + row) * kHeadDim + ch] = gv;
+        } else {
+          if (p.landmarks && p.dkbar != nullptr) {  // this tile's landmark share
+            const float inv_n = 1.0f / (float)rows_valid;
+            gk += p.dkbar[((int64_t)h * p.tk + cb) * kHeadDim + ch] * inv_n;
+            gv += p.dvbar[((int64_t)h * p.tk + cb) * kHeadDim + ch] * inv_n;
+          }
+          if (gf) {
+            ((float*)p.dk)[(int64_t)h * p.kgsh + row * p.kgst + ch] = gk;
+            ((float*)p.dv)[(int64_t)h * p.kgsh + row * p.kgst + ch] = gv;
+          } else {
+            ((__bf16*)p.dk)[(int64_t)h * p.kgsh + row * p.kgst + ch] = (__bf16)gk;
+            ((__bf16*)p.dv)[(int64_t)h * p.kgsh + row * p.kgst + ch] = (__bf16)gv;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 5. dq: one workgroup per (head, query tile); wave w owns 32 queries
+// ---------------------------------------------------------------------------
+template <int QT, int KT>
+__global__ __launch_bounds__(QT * 2) void bwd_dq_kernel(BwdParams p) {
+  constexpr int W = QT / 32;
+  constexpr int NT = W * kWave;
+  constexpr int NB = KT / 32;
+  __shared__ u32x4 ks_t[KT * 8], vs_t[KT * 8];
+  const lds_u8* ktile = (const lds_u8*)ks_t;
+  const lds_u8* vtile = (const lds_u8*)vs_t;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int qi = lane & 31, hh = lane >> 5;
+  const bool gf = p.g_f32 != 0;
+  const int n_lb_all = p.landmarks ? (p.tk + KT - 1) / KT : 0;
+  const int tail_rows = (int)(p.nk - (int64_t)(p.tk - 1) * KT);
+  const int last_lrows = p.tk - (n_lb_all - 1) * KT;
+  for (int64_t item = blockIdx.x; item < (int64_t)p.heads * p.tq; item += gridDim.x) {
+    const int h = (int)(item / p.tq);
+    const int qt = (int)(item - (int64_t)h * p.tq);
+    const int64_t row = (int64_t)h * p.tq + qt;
+    const int32_t* sel_row = p.sel + row * p.top_k;
+    const int64_t qrow = (int64_t)qt * QT + wave * 32 + qi;
+    const bool qvalid = qrow < p.nq;
+    bf16x8 qop[4], dop[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+      if (qvalid) {
+        a = *(const u32x4*)(p.q + (int64_t)h * p.qsh + qrow * p.qst + 16 * s + 8 * hh);
+        b = load8_bf16(p.dout, (int64_t)h * p.dsh + qrow * p.dst + 16 * s + 8 * hh, gf);
+      }
+      qop[s] = as_bf16x8(a);
+      dop[s] = as_bf16x8(b);
+    }
+    float lse = qvalid ? p.lse[(int64_t)h * p.nq + qrow] : INFINITY;
+    float dsum = 0.f;  // D = sum_c P_c dP_c, from the first sweep
+    f32x16 dqacc[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dqacc[0][i] = 0.f;
+      dqacc[1][i] = 0.f;
+    }
+    const int n_total = p.top_k + n_lb_all;
+    const uint32_t* brow = p.bits + row * p.bit_words;
+    // sweep 0: sum_c P'_c and sum_c P'_c dP_c with P' = 2^(x - lse) in
+    // float32. The forward's normaliser sums bf16-rounded probabilities, so P'
+    // sums to 1 + O(2^-9); renormalising lse by that sum makes P sum to one in
+    // float32, and D = sum P dP then matches dP exactly (dP - D cancels, which
+    // would amplify any mismatch). sweep 1: dS and dq.
+    auto sweep = [&](auto sweep_c) -> f32x2 {
+    constexpr bool kGrad = decltype(sweep_c)::value;
+    float dpart = 0.f, lpart = 0.f;
+    for (int t = 0; t < n_total; ++t) {
+      const bool lm = t >= p.top_k;
+      const uint16_t* kbase;
+      const uint16_t* vbase;
+      int64_t stride;
+      int rows;
+      uint64_t cmask = 0ull;  // excluded columns (bit set)
+      float bias = 0.f;       // log2 units
+      int tail_col = -1;
+      if (!lm) {
+        const int j = min(max(sel_row[t], 0), p.tk - 1);
+        kbase = p.k + (int64_t)h * p.ksh + (int64_t)j * KT * p.kst;
+        vbase = p.v + (int64_t)h * p.ksh + (int64_t)j * KT * p.kst;
+        stride = p.kst;
+        rows = j == p.tk - 1 ? tail_rows : KT;
+      } else {
+        const int b = t - p.top_k;
+        kbase = p.kbar_b + ((int64_t)h * p.tk + (int64_t)b * KT) * kHeadDim;
+        vbase = p.vbar_b + ((int64_t)h * p.tk + (int64_t)b * KT) * kHeadDim;
+        stride = kHeadDim;
+        rows = b == n_lb_all - 1 ? last_lrows : KT;
+        const uint32_t lo = brow[NB * b];
+        const uint32_t hi = KT == 64 && 2 * b + 1 < p.bit_words ? brow[2 * b + 1] : 0u;
+        cmask = ((uint64_t)hi << 32) | lo;
+        if (p.log_count) {
+          bias = p.lm_log2_kt;
+          if (b == n_lb_all - 1 && tail_rows < KT) tail_col = last_lrows - 1;
+        }
+      }
+      if (rows < KT) cmask |= ~0ull << rows;
+      __syncthreads();  // previous block consumed
+      for (int e = tid; e < KT * 8; e += NT) {
+        const int r = e >> 3, c8 = e & 7;
+        const int rr = min(r, rows - 1);  // rows past the end repeat the last one (masked)
+        const u32x4 a = *(const u32x4*)(kbase + (int64_t)rr * stride + 8 * c8);
+        const u32x4 b = *(const u32x4*)(vbase + (int64_t)rr * stride + 8 * c8);
+        *(__attribute__((address_space(3))) u32x4*)(ktile + swz(r, c8)) = a;
+        *(__attribute__((address_space(3))) u32x4*)(vtile + swz(r, c8)) = b;
+      }
+      __syncthreads();
+      // S^T = K Q^T, dP^T = V dout^T: lane = query, register = key
+      // 32 b + 8 (v / 4) + 4 hh + v % 4
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        f32x16 sacc, pacc;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 ak = row_operand(ktile, 32 * b + qi, s, hh);
+          const bf16x8 av = row_operand(vtile, 32 * b + qi, s, hh);
+          if (s == 0) {
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qop[0], f32x16{}, 0, 0, 0);
+            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, dop[0], f32x16{}, 0, 0, 0);
+          } else {
+            sacc = mfma32(ak, qop[s], sacc);
+            pacc = mfma32(av, dop[s], pacc);
+          }
+        }
+        float dsr[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = 32 * b + 8 * (v >> 2) + 4 * hh + (v & 3);
+          float x = __builtin_fmaf(sacc[v], p.c, bias);
+          if (key == tail_col) x += p.lm_tail_corr * p.c;
+          const bool off = (cmask >> key) & 1ull;
+          const float pv = off ? 0.f : __builtin_amdgcn_exp2f(x - lse);
+          if constexpr (kGrad) {
+            dsr[v] = pv * (pacc[v] - dsum);
+          } else {
+            dpart = __builtin_fmaf(pv, pacc[v], dpart);
+            lpart += pv;
+          }
+        }
+        if constexpr (kGrad) {
+          bf16x8 slo, shi, slo2, shi2;
+          pack16_split(dsr, slo, shi, slo2, shi2);
+          // dq^T += K^T dS^T over 16-key chunks 2b and 2b + 1
+#pragma unroll
+          for (int db = 0; db < 2; ++db) {
+            const bf16x8 k0 = tr_operand(ktile, 2 * b, db, lane);
+            const bf16x8 k1 = tr_operand(ktile, 2 * b + 1, db, lane);
+            dqacc[db] = mfma32(k0, slo, dqacc[db]);
+            dqacc[db] = mfma32(k1, shi, dqacc[db]);
+            dqacc[db] = mfma32(k0, slo2, dqacc[db]);
+            dqacc[db] = mfma32(k1, shi2, dqacc[db]);
+          }
+        }
+      }
+    }
+    return f32x2{dpart, lpart};
+    };
+    {
+      const f32x2 d0 = sweep(std::false_type{});
+      const auto sd = __builtin_amdgcn_permlane32_swap(__float_as_uint(d0[0]),
+                                                       __float_as_uint(d0[0]), false, false);
+      const auto sl = __builtin_amdgcn_permlane32_swap(__float_as_uint(d0[1]),
+                                                       __float_as_uint(d0[1]), false, false);
+      const float dtot = __uint_as_float(sd[0]) + __uint_as_float(sd[1]);  // both halves
+      const float ltot = __uint_as_float(sl[0]) + __uint_as_float(sl[1]);
+      if (qvalid) {
+        lse += __builtin_log2f(ltot);
+        dsum = dtot / ltot;
+        if (hh == 0) {
+          p.lse[(int64_t)h * p.nq + qrow] = lse;
+          p.dsum[(int64_t)h * p.nq + qrow] = dsum;
+        }
+      }
+      sweep(std::true_type{});
+    }
+    // epilogue: lane (qi, hh) holds channels 32 db + 8 g + 4 hh + r
+    if (qvalid) {
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t base = (int64_t)h * p.qgsh + qrow * p.qgst + 32 * db + 8 * g + 4 * hh;
+          const float x0 = p.scale * dqacc[db][4 * g], x1 = p.scale * dqacc[db][4 * g + 1];
+          const float x2 = p.scale * dqacc[db][4 * g + 2], x3 = p.scale * dqacc[db][4 * g + 3];
+          if (gf)
+            *(f32x4*)((float*)p.dq + base) = f32x4{x0, x1, x2, x3};
+          else
+            *(u32x2*)((uint16_t*)p.dq + base) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+        }
+    }
+  }
+}
+
+size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct BwdLayout {
+  size_t fwd, o, lse, dsum, dkbar, dvbar, bits, count, off, list, total;
+};
+
+BwdLayout bwd_layout(int64_t nq, int64_t nk, int32_t heads, int32_t q_tile, int32_t k_tile,
+                     int32_t top_k) {
+  BwdLayout L;
+  const int64_t tq = (nq + q_tile - 1) / q_tile, tk = (nk + k_tile - 1) / k_tile;
+  L.fwd = a256(sparse_workspace_bytes(nq, nk, heads, q_tile, k_tile, top_k));
+  L.o = a256((size_t)heads * nq * kHeadDim * sizeof(float));
+  L.lse = a256((size_t)heads * nq * sizeof(float));
+  L.dsum = L.lse;
+  L.dkbar = a256((size_t)heads * tk * kHeadDim * sizeof(float));
+  L.dvbar = L.dkbar;
+  L.bits = a256((size_t)heads * tq * ((tk + 31) / 32) * sizeof(uint32_t));
+  L.count = a256((size_t)heads * tk * sizeof(int32_t));
+  L.off = a256((size_t)heads * (tk + 1) * sizeof(int32_t));
+  L.list = a256((size_t)heads * tq * top_k * sizeof(int32_t));
+  L.total = L.fwd + L.o + L.lse + L.dsum + L.dkbar + L.dvbar + L.bits + L.count + L.off + L.list;
+  return L;
+}
+
+template <int QT, int KT>
+hipError_t launch_bwd_kernels(const BwdParams& p, int32_t heads, hipStream_t s) {
+  hipError_t err;
+  // dq first: it also writes D for the dk, dv kernels
+  const int64_t items = (int64_t)heads * p.tq;
+  hipLaunchKernelGGL((bwd_dq_kernel<QT, KT>), dim3((unsigned)std::min<int64_t>(items, 1 << 24)),
+                     dim3(QT * 2), 0, s, p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (p.landmarks) {
+    const int nb = (p.tk + KT - 1) / KT;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<QT, KT, true>), dim3((unsigned)nb, heads), dim3(KT * 2), 0,
+                       s, p);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL((bwd_dkdv_kernel<QT, KT, false>), dim3((unsigned)p.tk, heads), dim3(KT * 2),
+                     0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t sparse_bwd_workspace_bytes(int64_t n_q, int64_t n_kv, int32_t heads, int32_t q_tile,
+                                  int32_t k_tile, int32_t top_k) {
+  return bwd_layout(n_q, n_kv, heads, q_tile, k_tile, top_k).total;
+}
+
+hipError_t launch_tile_sparse_bwd(const uint16_t* q, int64_t nq, int64_t qst, int64_t qsh,
+                                  const uint16_t* k, const uint16_t* v, int64_t nk, int64_t kst,
+                                  int64_t ksh, int32_t heads, const float* kbar,
+                                  const float* vbar, const int32_t* sel, int32_t q_tile,
+                                  int32_t k_tile, int32_t top_k, float scale, uint32_t flags,
+                                  const void* dout, int64_t dst, int64_t dsh, bool g_f32,
+                                  void* dq, int64_t qgst, int64_t qgsh, void* dk, void* dv,
+                                  int64_t kgst, int64_t kgsh, void* ws, hipStream_t s) {
+  if (heads == 0 || (nq == 0 && nk == 0)) return hipSuccess;
+  const BwdLayout L = bwd_layout(nq, nk, heads, q_tile, k_tile, top_k);
+  uint8_t* w = (uint8_t*)ws;
+  float* o = (float*)(w + L.fwd);
+  float* lse = (float*)(w + L.fwd + L.o);
+  float* dsum = (float*)(w + L.fwd + L.o + L.lse);
+  float* dkbar = (float*)(w + L.fwd + L.o + L.lse + L.dsum);
+  float* dvbar = (float*)((uint8_t*)dkbar + L.dkbar);
+  uint32_t* bits = (uint32_t*)((uint8_t*)dvbar + L.dvbar);
+  int32_t* count = (int32_t*)((uint8_t*)bits + L.bits);
+  int32_t* off = (int32_t*)((uint8_t*)count + L.count);
+  int32_t* list = (int32_t*)((uint8_t*)off + L.off);
+  const int32_t tq = (int32_t)((nq + q_tile - 1) / q_tile);
+  const int32_t tk = (int32_t)((nk + k_tile - 1) / k_tile);
+  const int32_t bit_words = (tk + 31) / 32;
+  const bool landmarks = (flags & kSparseNoLandmarks) == 0 && top_k < tk;
+  hipError_t err;
+  // forward: float32 output and the log2 normaliser (also packs the bf16 landmarks)
+  if (nq > 0) {
+    err = launch_tile_sparse(q, nq, qst, qsh, k, v, nk, kst, ksh, heads, kbar, vbar, sel, q_tile,
+                             k_tile, top_k, scale, o, kHeadDim, nq * kHeadDim, true, flags, w, s,
+                             lse);
+    if (err != hipSuccess) return err;
+  }
+  // kept bits, counts, offsets, lists
+  const int64_t nzero = (int64_t)((uint8_t*)off - (uint8_t*)bits) / 4;  // bits and counts
+  hipLaunchKernelGGL(bwd_fill_u32_kernel, dim3((unsigned)std::min<int64_t>((nzero + 255) / 256,
+                                                                           4096)),
+                     dim3(256), 0, s, bits, nzero);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (tq > 0) {
+    hipLaunchKernelGGL(bwd_bits_kernel, dim3((unsigned)((int64_t)heads * tq)), dim3(256), 0, s,
+                       sel, (int64_t)heads * tq, tq, tk, top_k, bit_words, bits, count);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(bwd_scan_kernel, dim3(heads), dim3(256), 0, s, count, tk,
+                     (int64_t)tq * top_k, off);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(bwd_list_kernel, dim3((unsigned)bit_words, heads), dim3(64), 0, s, bits, tq,
+                     tk, bit_words, off, list);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+
+  BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  // the forward packed the bf16 landmarks at the start of its workspace
+  const size_t lm = a256((size_t)heads * tk * kHeadDim * sizeof(uint16_t));
+  p.kbar_b = landmarks ? (const uint16_t*)w : nullptr;
+  p.vbar_b = landmarks ? (const uint16_t*)(w + lm) : nullptr;
+  p.sel = sel;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.nq = nq;
+  p.qst = qst;
+  p.qsh = qsh;
+  p.nk = nk;
+  p.kst = kst;
+  p.ksh = ksh;
+  p.dst = dst;
+  p.dsh = dsh;
+  p.qgst = qgst;
+  p.qgsh = qgsh;
+  p.kgst = kgst;
+  p.kgsh = kgsh;
+  p.heads = heads;
+  p.tq = tq;
+  p.tk = tk;
+  p.top_k = top_k;
+  p.bit_words = bit_words;
+  p.c = scale * kLog2eB;
+  p.scale = scale;
+  p.g_f32 = g_f32 ? 1 : 0;
+  p.landmarks = landmarks ? 1 : 0;
+  p.log_count = (flags & kSparseLandmarkLogCount) ? 1 : 0;
+  p.lm_log2_kt = __builtin_log2f((float)k_tile);
+  {
+    const int64_t tail = nk - (int64_t)(tk - 1) * k_tile;
+    p.lm_tail_corr = tail > 0 ? (__builtin_log2f((float)tail) - p.lm_log2_kt) / p.c : 0.f;
+  }
+  p.lse = lse;
+  p.dsum = dsum;
+  p.bits = bits;
+  p.list_off = off;
+  p.list = list;
+  p.dkbar = landmarks ? dkbar : nullptr;
+  p.dvbar = landmarks ? dvbar : nullptr;
+  if (k_tile == 64) {
+    if (q_tile == 32) return launch_bwd_kernels<32, 64>(p, heads, s);
+    if (q_tile == 64) return launch_bwd_kernels<64, 64>(p, heads, s);
+    return launch_bwd_kernels<128, 64>(p, heads, s);
+  }
+  if (q_tile == 32) return launch_bwd_kernels<32, 32>(p, heads, s);
+  if (q_tile == 64) return launch_bwd_kernels<64, 32>(p, heads, s);
+  return launch_bwd_kernels<128, 32>(p, heads, s);
+}
+
+}  // namespace zebra

@@ -351,6 +351,88 @@ zebra_status zebra_fit_scale_only(const float* x, const float* y, int32_t m, int
                     stream);
 }
 
+size_t zebra_tile_sparse_attn_backward_workspace(int64_t n_q, int64_t n_kv, int32_t n_heads,
+                                                 int32_t head_dim, int32_t q_tile, int32_t k_tile,
+                                                 int32_t top_k) {
+  if (n_q < 0 || n_kv < 1 || n_heads <= 0 || head_dim != zebra::kHeadDim) return 0;
+  if (q_tile != 32 && q_tile != 64 && q_tile != 128) return 0;
+  if (k_tile != 32 && k_tile != 64) return 0;
+  const int64_t tk = ceil_div(n_kv, k_tile);
+  if (top_k < 1 || top_k > tk) return 0;
+  return zebra::sparse_bwd_workspace_bytes(n_q, n_kv, n_heads, q_tile, k_tile, top_k);
+}
+
+zebra_status zebra_tile_sparse_attn_backward(
+    const void* q, zebra_seq qs, const void* k, const void* v, zebra_seq kvs, const float* kbar,
+    const float* vbar, const int32_t* sel, int32_t q_tile, int32_t k_tile, int32_t top_k,
+    float scale, uint32_t flags, const void* dout, zebra_seq dos, zebra_dtype g_dtype, void* dq,
+    zebra_seq dqs, void* dk, void* dv, zebra_seq dkvs, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  zebra_status st;
+  const uint32_t known = ZEBRA_SPARSE_NO_LANDMARKS | ZEBRA_SPARSE_LANDMARK_LOG_COUNT;
+  if ((flags & ~known) != 0u || flags == known) return ZEBRA_ERR_INVALID_ARG;
+  if ((st = check_seq(q, qs, false)) != ZEBRA_OK) return st;
+  if ((st = check_seq(k, kvs, false)) != ZEBRA_OK) return st;
+  if ((st = check_seq(v, kvs, false)) != ZEBRA_OK) return st;
+  if ((st = check_seq(dout, dos, false)) != ZEBRA_OK) return st;
+  if ((st = check_seq(dq, dqs, true)) != ZEBRA_OK) return st;
+  if ((st = check_seq(dk, dkvs, true)) != ZEBRA_OK) return st;
+  if ((st = check_seq(dv, dkvs, true)) != ZEBRA_OK) return st;
+  if (g_dtype != ZEBRA_BF16 && g_dtype != ZEBRA_F32) return ZEBRA_ERR_INVALID_ARG;
+  const int32_t h = qs.n_heads;
+  if (kvs.n_heads != h || dos.n_heads != h || dqs.n_heads != h || dkvs.n_heads != h ||
+      dos.n_tokens != qs.n_tokens || dqs.n_tokens != qs.n_tokens ||
+      dkvs.n_tokens != kvs.n_tokens)
+    return ZEBRA_ERR_INVALID_ARG;
+  if (q_tile != 32 && q_tile != 64 && q_tile != 128) return ZEBRA_ERR_UNSUPPORTED;
+  if (k_tile != 32 && k_tile != 64) return ZEBRA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || scale > 1e30f) return ZEBRA_ERR_INVALID_ARG;
+  if (kvs.n_tokens == 0) return ZEBRA_ERR_INVALID_ARG;
+  const int64_t tk = ceil_div(kvs.n_tokens, k_tile);
+  if (tk > kMaxKeyTiles) return ZEBRA_ERR_UNSUPPORTED;
+  const int64_t tq = ceil_div(qs.n_tokens, q_tile);
+  if (tq * h > (int64_t)INT32_MAX || tq * top_k > (int64_t)INT32_MAX / (h > 0 ? h : 1))
+    return ZEBRA_ERR_UNSUPPORTED;
+  if (top_k < 1 || top_k > tk) return ZEBRA_ERR_INVALID_ARG;
+  if (sel == nullptr || ((uintptr_t)sel % 4) != 0) return ZEBRA_ERR_INVALID_ARG;
+  const bool use_lm = top_k < tk && (flags & ZEBRA_SPARSE_NO_LANDMARKS) == 0u;
+  if (use_lm && (kbar == nullptr || vbar == nullptr || ((uintptr_t)kbar % 16) != 0 ||
+                 ((uintptr_t)vbar % 16) != 0))
+    return ZEBRA_ERR_INVALID_ARG;
+  if (kvs.stride_token > (int64_t)1 << 24) return ZEBRA_ERR_UNSUPPORTED;
+  const size_t gel = g_dtype == ZEBRA_F32 ? 4 : 2;
+  if (g_dtype == ZEBRA_F32) {
+    for (const zebra_seq* g : {&dos, &dqs, &dkvs})
+      if (g->stride_token % 8 != 0 || g->stride_head % 8 != 0) return ZEBRA_ERR_UNSUPPORTED;
+  }
+  const size_t need = zebra::sparse_bwd_workspace_bytes(qs.n_tokens, kvs.n_tokens, h, q_tile,
+                                                        k_tile, top_k);
+  if (workspace == nullptr || workspace_bytes < need) return ZEBRA_ERR_WORKSPACE;
+  if (((uintptr_t)workspace % 16) != 0) return ZEBRA_ERR_INVALID_ARG;
+  std::vector<Range> ins = {seq_range(q, qs, 2), seq_range(k, kvs, 2), seq_range(v, kvs, 2),
+                            seq_range(dout, dos, gel),
+                            flat_range(sel, (uint64_t)h * tq * top_k, 4)};
+  if (use_lm) {
+    ins.push_back(flat_range(kbar, (uint64_t)h * tk * zebra::kHeadDim, 4));
+    ins.push_back(flat_range(vbar, (uint64_t)h * tk * zebra::kHeadDim, 4));
+  }
+  const Range outs[] = {seq_range(dq, dqs, gel), seq_range(dk, dkvs, gel),
+                        seq_range(dv, dkvs, gel), flat_range(workspace, need, 1)};
+  for (size_t i = 0; i < 4; ++i) {
+    for (const Range& r : ins)
+      if (overlaps(outs[i], r)) return ZEBRA_ERR_INVALID_ARG;
+    for (size_t j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outs[j])) return ZEBRA_ERR_INVALID_ARG;
+  }
+  return hip_status(zebra::launch_tile_sparse_bwd(
+      (const uint16_t*)q, qs.n_tokens, qs.stride_token, qs.stride_head, (const uint16_t*)k,
+      (const uint16_t*)v, kvs.n_tokens, kvs.stride_token, kvs.stride_head, h,
+      use_lm ? kbar : nullptr, use_lm ? vbar : nullptr, sel, q_tile, k_tile, top_k, scale,
+      top_k < tk ? flags : 0u, dout, dos.stride_token, dos.stride_head, g_dtype == ZEBRA_F32, dq,
+      dqs.stride_token, dqs.stride_head, dk, dv, dkvs.stride_token, dkvs.stride_head, workspace,
+      (hipStream_t)stream));
+}
+
 size_t zebra_linear_attn_backward_workspace(int64_t n_q, int64_t n_kv, int32_t n_heads,
                                             int32_t head_dim) {
   if (n_q < 0 || n_kv < 0 || n_heads <= 0 || head_dim != zebra::kHeadDim) return 0;

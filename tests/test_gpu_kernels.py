@@ -560,3 +560,63 @@ def test_linear_backward_parity(n_q, n_kv, affine, g_dtype):
         assert_grad_close(dv[h], rv, f"linear dv head {h}")
         assert_grad_close(da[h], ra, f"linear da head {h}")
         assert_grad_close(db[h], rb, f"linear db head {h}")
+
+
+SPARSE_BWD_CASES = [
+    # (q_tile, k_tile, n_q, n_kv, top_k, n_hot, heads, variant)
+    (64, 64, 300, 300, 2, 2, 2, "default"),
+    (128, 32, 257, 300, 4, 2, 1, "default"),
+    (32, 64, 100, 450, 1, 1, 2, "default"),
+    (64, 32, 130, 200, 3, 2, 2, "log_count"),
+    (64, 64, 300, 300, 2, 2, 2, "no_landmarks"),
+    (32, 32, 2000, 2000, 7, 3, 1, "default"),        # many query tiles per key tile
+    (64, 64, 1000, 1000, 16, 3, 1, "default"),       # every tile kept
+    (64, 64, 300, 65536 + 333, 206, 3, 1, "default"),  # forward in split keys
+]
+BWD_FLAGS = {"default": (0, {}), "no_landmarks": (1, dict(landmarks=False)),
+             "log_count": (2, dict(landmark_log_count=True))}
+
+
+@pytest.mark.parametrize("g_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("case", SPARSE_BWD_CASES, ids=[str(c) for c in SPARSE_BWD_CASES])
+def test_sparse_backward_parity(case, g_dtype):
+    q_tile, k_tile, n_q, n_kv, top_k, n_hot, heads, variant = case
+    flags, kw = BWD_FLAGS[variant]
+    print(f"[case] sparse backward {case} {g_dtype}", flush=True)
+    q, k, v = _clustered(n_q + 3 * n_kv + top_k, heads, n_q, n_kv, q_tile, k_tile, n_hot)
+    rng = np.random.default_rng(n_q * 7 + top_k)
+    dout = synth.bf16_round(rng.standard_normal((heads, n_q, 64)).astype(np.float32))
+    qg, kg, vg = bf16_gpu(q), bf16_gpu(k), bf16_gpu(v)
+    bufs = stage.SparseBuffers.allocate(heads, n_q, n_kv, q_tile, k_tile, top_k, DEV)
+    stage.sparse_stage(qg, kg, vg, q_tile, k_tile, top_k, 0.125, bufs, flags=flags)
+    dq, dk, dv = zb.zebra_tile_sparse_attn_backward(
+        qg, kg, vg, bufs.kbar, bufs.vbar, bufs.sel, q_tile, k_tile, top_k, 0.125,
+        torch.from_numpy(dout).to(DEV).to(g_dtype), flags)
+    torch.cuda.synchronize()
+    sel = bufs.sel.cpu().numpy()
+    rq, rk, rv = zo.tile_sparse_attention_backward(q, k, v, q_tile, k_tile, sel, 0.125, dout, **kw)
+    assert_grad_close(dq, rq, f"sparse dq {case}")
+    assert_grad_close(dk, rk, f"sparse dk {case}")
+    assert_grad_close(dv, rv, f"sparse dv {case}")
+
+
+def test_sparse_backward_running_max_path_and_determinism():
+    """Query tiles with a loose logit bound (the forward's running-maximum path)
+    and bitwise-equal gradients on a second call."""
+    q, k, v = _clustered(41, 2, 700, 700, 64, 64, 3)
+    q = q.copy()
+    q[:, 128:320] *= 8.0
+    q = synth.bf16_round(q)
+    dout = synth.bf16_round(np.random.default_rng(3).standard_normal((2, 700, 64)).astype(np.float32))
+    qg, kg, vg = bf16_gpu(q), bf16_gpu(k), bf16_gpu(v)
+    bufs = stage.sparse_stage(qg, kg, vg, 64, 64, 3, 0.125)
+    dg = torch.from_numpy(dout).to(DEV)
+    g1 = zb.zebra_tile_sparse_attn_backward(qg, kg, vg, bufs.kbar, bufs.vbar, bufs.sel, 64, 64, 3,
+                                            0.125, dg)
+    g2 = zb.zebra_tile_sparse_attn_backward(qg, kg, vg, bufs.kbar, bufs.vbar, bufs.sel, 64, 64, 3,
+                                            0.125, dg)
+    torch.cuda.synchronize()
+    ref = zo.tile_sparse_attention_backward(q, k, v, 64, 64, bufs.sel.cpu().numpy(), 0.125, dout)
+    for a, b, r, name in zip(g1, g2, ref, ("dq", "dk", "dv")):
+        assert torch.equal(a, b), f"{name} not reproducible"
+        assert_grad_close(a, r, f"running-max path {name}")
