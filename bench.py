@@ -52,6 +52,9 @@ def parse():
                    help="only measure how much dense attention mass the pooled-score selection "
                         "keeps, against the top-k blocks by mass, on the workload's first sparse "
                         "stage (at most 65,536 tokens) and exit")
+    p.add_argument("--backward", action="store_true",
+                   help="only time the gradients of the workload's first sparse stage (and, for "
+                        "the stack and linear workloads, of its first linear stage) and exit")
     return p.parse_args()
 
 
@@ -252,6 +255,69 @@ def selection_quality(args, w, torch, zb, synth):
     print(json.dumps({"selection_quality": out}), flush=True)
 
 
+def backward(args, w, torch, zb, stage_mod, synth):
+    """Time zebra_tile_sparse_attn_backward / zebra_linear_attn_backward on one
+    stage of the workload (inputs and output gradient resident in HBM)."""
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    n, heads = w.n_tokens, w.heads
+    stages = list(range(w.n_stages)) if w.kind == "stack" else [0]
+    out = {"workload": w.name, "tokens": n, "heads": heads}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(max(1, args.steps)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ms.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.median([x.elapsed_time(y) for x, y in ms]))
+
+    sparse_s = [s for s in stages if w.stage_kind(s) == "sparse"]
+    if sparse_s:
+        s = sparse_s[0]
+        q, k, v = synth.stage_inputs(w, s, dev)
+        bufs = stage_mod.SparseBuffers.allocate(heads, n, n, w.q_tile, w.k_tile, w.k, dev)
+        stage_mod.sparse_stage(q, k, v, w.q_tile, w.k_tile, w.k, SCALE, bufs)
+        dout = torch.randn((heads, n, 64), generator=g, device=dev).bfloat16()
+        ws = torch.empty(zb.library().zebra_tile_sparse_attn_backward_workspace(
+            n, n, heads, 64, w.q_tile, w.k_tile, w.k), dtype=torch.uint8, device=dev)
+        ms = timed(lambda: zb.zebra_tile_sparse_attn_backward(
+            q, k, v, bufs.kbar, bufs.vbar, bufs.sel, w.q_tile, w.k_tile, w.k, SCALE, dout,
+            workspace=ws))
+        sel_fl, lm_fl = sparse_flops(n, n, w.q_tile, w.k_tile, w.k, bufs.sel.cpu().numpy())
+        # gradient work: S, dP, dq, dk, dv = 10 d flop per column (forward: 4 d)
+        bw = 2.5 * sel_fl / (ms * 1e-3) / 1e12
+        out["sparse"] = {"stage": s, "ms": ms, "bound": "mfma", "achieved": bw,
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": bw / PEAK_BF16_TFLOPS,
+                         "achieved_with_landmarks": 2.5 * (sel_fl + lm_fl) / (ms * 1e-3) / 1e12,
+                         "flops_per_launch": 2.5 * sel_fl, "workspace_bytes": ws.numel()}
+        del q, k, v, bufs, dout, ws
+    linear_s = [s for s in stages if w.stage_kind(s) == "linear"]
+    if linear_s:
+        s = linear_s[0]
+        q, k, v = synth.stage_inputs(w, s, dev)
+        dout = torch.randn((heads, n, 64), generator=g, device=dev).bfloat16()
+        a = torch.rand((heads, 64), generator=g, device=dev) + 0.5
+        ws = torch.empty(zb.library().zebra_linear_attn_backward_workspace(n, n, heads, 64),
+                         dtype=torch.uint8, device=dev)
+        ms = timed(lambda: zb.zebra_linear_attn_backward(q, k, v, dout, a, workspace=ws))
+        # float32 products: 3 (query pass) + 2 (key pass) 64 x 64 products per row
+        fl = 5 * 2 * 64 * 64 * n * heads
+        out["linear"] = {"stage": s, "ms": ms, "bound": "alu", "achieved": fl / (ms * 1e-3) / 1e12,
+                         "peak": 157.3, "unit": "TFLOP/s",
+                         "frac": fl / (ms * 1e-3) / 1e12 / 157.3,
+                         "hbm_bytes": 7 * n * heads * 64 * 2,
+                         "hbm_frac": 7 * n * heads * 64 * 2 / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    print(json.dumps({"backward": out}), flush=True)
+
+
 # ----------------------------------------------------------------------------
 # CPU oracle baseline on a bounded sample of the same workload
 # ----------------------------------------------------------------------------
@@ -333,6 +399,9 @@ def main():
     w = synth.WORKLOADS[args.workload]
     if args.selection_quality:
         selection_quality(args, w, torch, zb, synth)
+        return
+    if args.backward:
+        backward(args, w, torch, zb, stage_mod, synth)
         return
     res, inputs = run_gpu(args, w, torch, zb, stage_mod, synth)
     print(f"[bench] gpu done: {json.dumps(res)}", file=sys.stderr, flush=True)

@@ -21,6 +21,10 @@
 //     landmark rows), over every query tile, the kept tiles masked;
 //  4. dk, dv of the key tiles: one workgroup per (head, key tile), over the
 //     query tiles keeping it, plus the tile's landmark share from step 3.
+// Steps 2-4 run as a sequence of launches over chunks (key tiles for dq,
+// query tiles for dk and dv) so that the workgroups running together share
+// one chunk's operands in L2; each launch adds into float32 accumulators,
+// in launch order.
 // Steps 2-4 recompute S and dP with bf16 MFMA 32x32x16 and accumulate in
 // float32; dS enters its products as a bf16 pair (float32-grade), P as bf16
 // (as in the forward). Sums run in a fixed order: no atomics in any
@@ -130,9 +134,27 @@ struct BwdParams {
   const uint32_t* bits;    // [H][tq][bit_words] kept tiles
   const int32_t* list_off; // [H][tk + 1]
   const int32_t* list;     // [H][tq * top_k] query tiles keeping each key tile
-  float* dkbar;            // [H][tk][64] float32 landmark gradients
+  float* dkbar;            // [H][tk][64] float32 landmark gradients (accumulated per launch)
   float* dvbar;
+  // chunked launches: this launch covers query tiles [q_lo, q_hi) (dk, dv) or
+  // key tiles [k_lo, k_hi) (dq); contributions add up in launch order
+  int32_t q_lo, q_hi, k_lo, k_hi, first, last;
+  float* acc_k;            // [H][nk][64] float32 dk, dv accumulators
+  float* acc_v;
+  float* l_acc;            // [H][nq] sum of P', sum of P' dP (dq sweep 0)
+  float* d_acc;
+  float* dq_acc;           // [H][nq][64] float32 dq accumulator (dq sweep 1)
 };
+
+// first index in [lo, hi) of the ascending array a with a[i] >= x
+__device__ __forceinline__ int lower_bound_i32(const int32_t* a, int lo, int hi, int x) {
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
 
 // ---------------------------------------------------------------------------
 // 2. kept-tile bits, per-key-tile counts, offsets, ordered lists
@@ -306,16 +328,18 @@ __global__ __launch_bounds__(KT * 2) void bwd_dkdv_kernel(BwdParams p) {
     }
     int n_i, i_base;
     if constexpr (LM) {
-      n_i = p.tq;
-      i_base = 0;
-    } else {
+      n_i = p.q_hi - p.q_lo;
+      i_base = p.q_lo;
+    } else {  // the part of the (ascending) list inside [q_lo, q_hi)
       const int32_t* oh = p.list_off + (int64_t)h * (p.tk + 1);
-      i_base = oh[cb];
-      n_i = oh[cb + 1] - i_base;
+      const int b0 = oh[cb], b1 = oh[cb + 1];
+      i_base = lower_bound_i32(p.list, b0, b1, p.q_lo);
+      n_i = lower_bound_i32(p.list, i_base, b1, p.q_hi) - i_base;
     }
+    if (n_i == 0 && !p.first && !p.last) continue;  // nothing to add in this launch
     for (int ii = 0; ii < n_i; ++ii) {
       // (a selection with repeated entries would leave list slots unwritten)
-      const int qt = LM ? ii : min(max(p.list[i_base + ii], 0), p.tq - 1);
+      const int qt = LM ? i_base + ii : min(max(p.list[i_base + ii], 0), p.tq - 1);
       // kept mask of this lane's landmark column for query tile qt
       bool masked = !cvalid;
       if constexpr (LM) {
@@ -407,9 +431,16 @@ __global__ __launch_bounds__(KT * 2) void bwd_dkdv_kernel(BwdParams p) {
         const int64_t row = (int64_t)KT * cb + lc;
         float gk = p.scale * dkacc[db][v];
         float gv = dvacc[db][v];
-        if constexpr (LM) {
-          p.dkbar[((int64_t)h * p.tk + row) * kHeadDim + ch] = gk;
-          p.dvbar[((int64_t)h * p.tk + row) * kHeadDim + ch] = gv;
+        float* ak = LM ? p.dkbar : p.acc_k;
+        float* av = LM ? p.dvbar : p.acc_v;
+        const int64_t ai = ((int64_t)h * (LM ? p.tk : p.nk) + row) * kHeadDim + ch;
+        if (!p.first) {  // add this launch's query tiles to the earlier ones
+          gk += ak[ai];
+          gv += av[ai];
+        }
+        if (LM || !p.last) {
+          ak[ai] = gk;
+          av[ai] = gv;
         } else {
           if (p.landmarks && p.dkbar != nullptr) {  // this tile's landmark share
             const float inv_n = 1.0f / (float)rows_valid;
@@ -432,7 +463,7 @@ __global__ __launch_bounds__(KT * 2) void bwd_dkdv_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // 5. dq: one workgroup per (head, query tile); wave w owns 32 queries
 // ---------------------------------------------------------------------------
-template <int QT, int KT>
+template <int QT, int KT, bool kGrad>
 __global__ __launch_bounds__(QT * 2) void bwd_dq_kernel(BwdParams p) {
   constexpr int W = QT / 32;
   constexpr int NT = W * kWave;
@@ -465,26 +496,31 @@ __global__ __launch_bounds__(QT * 2) void bwd_dq_kernel(BwdParams p) {
       qop[s] = as_bf16x8(a);
       dop[s] = as_bf16x8(b);
     }
-    float lse = qvalid ? p.lse[(int64_t)h * p.nq + qrow] : INFINITY;
-    float dsum = 0.f;  // D = sum_c P_c dP_c, from the first sweep
+    const float lse = qvalid ? p.lse[(int64_t)h * p.nq + qrow] : INFINITY;
+    // sweep 1: D = sum_c P_c dP_c from sweep 0
+    const float dsum = kGrad && qvalid ? p.dsum[(int64_t)h * p.nq + qrow] : 0.f;
     f32x16 dqacc[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       dqacc[0][i] = 0.f;
       dqacc[1][i] = 0.f;
     }
-    const int n_total = p.top_k + n_lb_all;
+    // this launch's key tiles [k_lo, k_hi): kept entries [t0, t1) of the
+    // ascending row, landmark blocks [lb0, lb1)
+    const int t0 = lower_bound_i32(sel_row, 0, p.top_k, p.k_lo);
+    const int t1 = lower_bound_i32(sel_row, t0, p.top_k, p.k_hi);
+    const int lb0 = p.k_lo / KT, lb1 = min(n_lb_all, (p.k_hi + KT - 1) / KT);
+    const int n_kept = t1 - t0;
+    const int n_total = n_kept + max(lb1 - lb0, 0);
     const uint32_t* brow = p.bits + row * p.bit_words;
     // sweep 0: sum_c P'_c and sum_c P'_c dP_c with P' = 2^(x - lse) in
     // float32. The forward's normaliser sums bf16-rounded probabilities, so P'
     // sums to 1 + O(2^-9); renormalising lse by that sum makes P sum to one in
     // float32, and D = sum P dP then matches dP exactly (dP - D cancels, which
     // would amplify any mismatch). sweep 1: dS and dq.
-    auto sweep = [&](auto sweep_c) -> f32x2 {
-    constexpr bool kGrad = decltype(sweep_c)::value;
     float dpart = 0.f, lpart = 0.f;
     for (int t = 0; t < n_total; ++t) {
-      const bool lm = t >= p.top_k;
+      const bool lm = t >= n_kept;
       const uint16_t* kbase;
       const uint16_t* vbase;
       int64_t stride;
@@ -493,13 +529,13 @@ __global__ __launch_bounds__(QT * 2) void bwd_dq_kernel(BwdParams p) {
       float bias = 0.f;       // log2 units
       int tail_col = -1;
       if (!lm) {
-        const int j = min(max(sel_row[t], 0), p.tk - 1);
+        const int j = min(max(sel_row[t0 + t], 0), p.tk - 1);
         kbase = p.k + (int64_t)h * p.ksh + (int64_t)j * KT * p.kst;
         vbase = p.v + (int64_t)h * p.ksh + (int64_t)j * KT * p.kst;
         stride = p.kst;
         rows = j == p.tk - 1 ? tail_rows : KT;
       } else {
-        const int b = t - p.top_k;
+        const int b = lb0 + t - n_kept;
         kbase = p.kbar_b + ((int64_t)h * p.tk + (int64_t)b * KT) * kHeadDim;
         vbase = p.vbar_b + ((int64_t)h * p.tk + (int64_t)b * KT) * kHeadDim;
         stride = kHeadDim;
@@ -571,48 +607,66 @@ __global__ __launch_bounds__(QT * 2) void bwd_dq_kernel(BwdParams p) {
         }
       }
     }
-    return f32x2{dpart, lpart};
-    };
-    {
-      const f32x2 d0 = sweep(std::false_type{});
-      const auto sd = __builtin_amdgcn_permlane32_swap(__float_as_uint(d0[0]),
-                                                       __float_as_uint(d0[0]), false, false);
-      const auto sl = __builtin_amdgcn_permlane32_swap(__float_as_uint(d0[1]),
-                                                       __float_as_uint(d0[1]), false, false);
-      const float dtot = __uint_as_float(sd[0]) + __uint_as_float(sd[1]);  // both halves
-      const float ltot = __uint_as_float(sl[0]) + __uint_as_float(sl[1]);
-      if (qvalid) {
-        lse += __builtin_log2f(ltot);
-        dsum = dtot / ltot;
-        if (hh == 0) {
-          p.lse[(int64_t)h * p.nq + qrow] = lse;
-          p.dsum[(int64_t)h * p.nq + qrow] = dsum;
+    if constexpr (!kGrad) {  // add this launch's sums over both lane halves
+      const auto sd = __builtin_amdgcn_permlane32_swap(__float_as_uint(dpart),
+                                                       __float_as_uint(dpart), false, false);
+      const auto sl = __builtin_amdgcn_permlane32_swap(__float_as_uint(lpart),
+                                                       __float_as_uint(lpart), false, false);
+      float dtot = __uint_as_float(sd[0]) + __uint_as_float(sd[1]);
+      float ltot = __uint_as_float(sl[0]) + __uint_as_float(sl[1]);
+      if (qvalid && hh == 0) {
+        const int64_t qi2 = (int64_t)h * p.nq + qrow;
+        if (!p.first) {
+          dtot += p.d_acc[qi2];
+          ltot += p.l_acc[qi2];
         }
+        p.d_acc[qi2] = dtot;
+        p.l_acc[qi2] = ltot;
       }
-      sweep(std::true_type{});
-    }
-    // epilogue: lane (qi, hh) holds channels 32 db + 8 g + 4 hh + r
-    if (qvalid) {
+    } else if (qvalid) {
+      // epilogue: lane (qi, hh) holds channels 32 db + 8 g + 4 hh + r
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
+          const int64_t ai = ((int64_t)h * p.nq + qrow) * kHeadDim + 32 * db + 8 * g + 4 * hh;
+          f32x4 x = {dqacc[db][4 * g], dqacc[db][4 * g + 1], dqacc[db][4 * g + 2],
+                     dqacc[db][4 * g + 3]};
+          if (!p.first) x += *(const f32x4*)(p.dq_acc + ai);
+          if (!p.last) {
+            *(f32x4*)(p.dq_acc + ai) = x;
+            continue;
+          }
+          x *= p.scale;
           const int64_t base = (int64_t)h * p.qgsh + qrow * p.qgst + 32 * db + 8 * g + 4 * hh;
-          const float x0 = p.scale * dqacc[db][4 * g], x1 = p.scale * dqacc[db][4 * g + 1];
-          const float x2 = p.scale * dqacc[db][4 * g + 2], x3 = p.scale * dqacc[db][4 * g + 3];
           if (gf)
-            *(f32x4*)((float*)p.dq + base) = f32x4{x0, x1, x2, x3};
+            *(f32x4*)((float*)p.dq + base) = x;
           else
-            *(u32x2*)((uint16_t*)p.dq + base) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+            *(u32x2*)((uint16_t*)p.dq + base) = u32x2{pack_bf16x2(x[0], x[1]),
+                                                      pack_bf16x2(x[2], x[3])};
         }
     }
   }
 }
 
+// after the sweep-0 launches: renormalise lse by the sum of P' and form D
+__global__ __launch_bounds__(256) void bwd_finalize_kernel(float* __restrict__ lse,
+                                                           float* __restrict__ dsum,
+                                                           const float* __restrict__ l_acc,
+                                                           const float* __restrict__ d_acc,
+                                                           int64_t n) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  const float l = l_acc[e];
+  lse[e] += __builtin_log2f(l);
+  dsum[e] = d_acc[e] / l;
+}
+
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-  size_t fwd, o, lse, dsum, dkbar, dvbar, bits, count, off, list, total;
+  size_t fwd, dqacc, lse, dsum, lacc, dacc, dkbar, dvbar, acck, accv, bits, count, off, list,
+      total;
 };
 
 BwdLayout bwd_layout(int64_t nq, int64_t nk, int32_t heads, int32_t q_tile, int32_t k_tile,
@@ -620,36 +674,76 @@ BwdLayout bwd_layout(int64_t nq, int64_t nk, int32_t heads, int32_t q_tile, int3
   BwdLayout L;
   const int64_t tq = (nq + q_tile - 1) / q_tile, tk = (nk + k_tile - 1) / k_tile;
   L.fwd = a256(sparse_workspace_bytes(nq, nk, heads, q_tile, k_tile, top_k));
-  L.o = a256((size_t)heads * nq * kHeadDim * sizeof(float));
+  L.dqacc = a256((size_t)heads * nq * kHeadDim * sizeof(float));  // also the forward's output
   L.lse = a256((size_t)heads * nq * sizeof(float));
   L.dsum = L.lse;
+  L.lacc = L.lse;
+  L.dacc = L.lse;
   L.dkbar = a256((size_t)heads * tk * kHeadDim * sizeof(float));
   L.dvbar = L.dkbar;
+  L.acck = a256((size_t)heads * nk * kHeadDim * sizeof(float));
+  L.accv = L.acck;
   L.bits = a256((size_t)heads * tq * ((tk + 31) / 32) * sizeof(uint32_t));
   L.count = a256((size_t)heads * tk * sizeof(int32_t));
   L.off = a256((size_t)heads * (tk + 1) * sizeof(int32_t));
   L.list = a256((size_t)heads * tq * top_k * sizeof(int32_t));
-  L.total = L.fwd + L.o + L.lse + L.dsum + L.dkbar + L.dvbar + L.bits + L.count + L.off + L.list;
+  L.total = L.fwd + L.dqacc + L.lse + L.dsum + L.lacc + L.dacc + L.dkbar + L.dvbar + L.acck +
+            L.accv + L.bits + L.count + L.off + L.list;
   return L;
 }
 
+// Chunks: the workgroups of one launch share about 8 MB of K and V (dq) or Q
+// and dout (dk, dv), which then stay in L2, as in the forward's split keys.
+constexpr int kChunkRows = 32768;
+
 template <int QT, int KT>
-hipError_t launch_bwd_kernels(const BwdParams& p, int32_t heads, hipStream_t s) {
+hipError_t launch_bwd_kernels(BwdParams p, int32_t heads, hipStream_t s) {
   hipError_t err;
-  // dq first: it also writes D for the dk, dv kernels
+  // dq: sweep 0 over key chunks (sums of P' and P' dP), finalize, sweep 1
+  const int ct = kChunkRows / KT;  // key tiles per chunk, a multiple of KT
+  const int nkc = (p.tk + ct - 1) / ct;
   const int64_t items = (int64_t)heads * p.tq;
-  hipLaunchKernelGGL((bwd_dq_kernel<QT, KT>), dim3((unsigned)std::min<int64_t>(items, 1 << 24)),
-                     dim3(QT * 2), 0, s, p);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (p.landmarks) {
-    const int nb = (p.tk + KT - 1) / KT;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<QT, KT, true>), dim3((unsigned)nb, heads), dim3(KT * 2), 0,
-                       s, p);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+  const dim3 qgrid((unsigned)std::min<int64_t>(items, 1 << 24));
+  for (int sweep = 0; sweep < 2; ++sweep) {
+    for (int c = 0; c < nkc; ++c) {
+      p.k_lo = c * ct;
+      p.k_hi = std::min(p.tk, (c + 1) * ct);
+      p.first = c == 0;
+      p.last = c == nkc - 1;
+      if (sweep == 0)
+        hipLaunchKernelGGL((bwd_dq_kernel<QT, KT, false>), qgrid, dim3(QT * 2), 0, s, p);
+      else
+        hipLaunchKernelGGL((bwd_dq_kernel<QT, KT, true>), qgrid, dim3(QT * 2), 0, s, p);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    if (sweep == 0) {
+      const int64_t n = (int64_t)heads * p.nq;
+      hipLaunchKernelGGL(bwd_finalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                         p.lse, p.dsum, (const float*)p.l_acc, (const float*)p.d_acc, n);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
   }
-  hipLaunchKernelGGL((bwd_dkdv_kernel<QT, KT, false>), dim3((unsigned)p.tk, heads), dim3(KT * 2),
-                     0, s, p);
-  return hipGetLastError();
+  // dk, dv: landmark rows, then key tiles, each over query-tile chunks
+  const int qch = std::max(1, kChunkRows / QT);
+  const int nqc = (p.tq + qch - 1) / qch;
+  for (int pass = p.landmarks ? 0 : 1; pass < 2; ++pass) {
+    for (int c = 0; c < nqc; ++c) {
+      p.q_lo = c * qch;
+      p.q_hi = std::min(p.tq, (c + 1) * qch);
+      p.first = c == 0;
+      p.last = c == nqc - 1;
+      if (pass == 0) {
+        const int nb = (p.tk + KT - 1) / KT;
+        hipLaunchKernelGGL((bwd_dkdv_kernel<QT, KT, true>), dim3((unsigned)nb, heads),
+                           dim3(KT * 2), 0, s, p);
+      } else {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<QT, KT, false>), dim3((unsigned)p.tk, heads),
+                           dim3(KT * 2), 0, s, p);
+      }
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -670,12 +764,22 @@ hipError_t launch_tile_sparse_bwd(const uint16_t* q, int64_t nq, int64_t qst, in
   if (heads == 0 || (nq == 0 && nk == 0)) return hipSuccess;
   const BwdLayout L = bwd_layout(nq, nk, heads, q_tile, k_tile, top_k);
   uint8_t* w = (uint8_t*)ws;
-  float* o = (float*)(w + L.fwd);
-  float* lse = (float*)(w + L.fwd + L.o);
-  float* dsum = (float*)(w + L.fwd + L.o + L.lse);
-  float* dkbar = (float*)(w + L.fwd + L.o + L.lse + L.dsum);
-  float* dvbar = (float*)((uint8_t*)dkbar + L.dkbar);
-  uint32_t* bits = (uint32_t*)((uint8_t*)dvbar + L.dvbar);
+  uint8_t* cur = w + L.fwd;
+  auto take = [&](size_t bytes) {
+    uint8_t* r = cur;
+    cur += bytes;
+    return r;
+  };
+  float* dq_acc = (float*)take(L.dqacc);
+  float* lse = (float*)take(L.lse);
+  float* dsum = (float*)take(L.dsum);
+  float* l_acc = (float*)take(L.lacc);
+  float* d_acc = (float*)take(L.dacc);
+  float* dkbar = (float*)take(L.dkbar);
+  float* dvbar = (float*)take(L.dvbar);
+  float* acc_k = (float*)take(L.acck);
+  float* acc_v = (float*)take(L.accv);
+  uint32_t* bits = (uint32_t*)take(L.bits);
   int32_t* count = (int32_t*)((uint8_t*)bits + L.bits);
   int32_t* off = (int32_t*)((uint8_t*)count + L.count);
   int32_t* list = (int32_t*)((uint8_t*)off + L.off);
@@ -687,8 +791,8 @@ hipError_t launch_tile_sparse_bwd(const uint16_t* q, int64_t nq, int64_t qst, in
   // forward: float32 output and the log2 normaliser (also packs the bf16 landmarks)
   if (nq > 0) {
     err = launch_tile_sparse(q, nq, qst, qsh, k, v, nk, kst, ksh, heads, kbar, vbar, sel, q_tile,
-                             k_tile, top_k, scale, o, kHeadDim, nq * kHeadDim, true, flags, w, s,
-                             lse);
+                             k_tile, top_k, scale, dq_acc, kHeadDim, nq * kHeadDim, true, flags, w,
+                             s, lse);
     if (err != hipSuccess) return err;
   }
   // kept bits, counts, offsets, lists
@@ -756,6 +860,12 @@ hipError_t launch_tile_sparse_bwd(const uint16_t* q, int64_t nq, int64_t qst, in
   p.list = list;
   p.dkbar = landmarks ? dkbar : nullptr;
   p.dvbar = landmarks ? dvbar : nullptr;
+  p.acc_k = acc_k;
+  p.acc_v = acc_v;
+  p.l_acc = l_acc;
+  p.d_acc = d_acc;
+  p.dq_acc = dq_acc;
+  p.q_lo = p.q_hi = p.k_lo = p.k_hi = p.first = p.last = 0;
   if (k_tile == 64) {
     if (q_tile == 32) return launch_bwd_kernels<32, 64>(p, heads, s);
     if (q_tile == 64) return launch_bwd_kernels<64, 64>(p, heads, s);
