@@ -108,3 +108,61 @@ def test_full_size_block_mass_sampled():
         s0, e0 = i * w.q_tile, min(w.n_tokens, (i + 1) * w.q_tile)
         ref = zo.block_attention_mass(qh[s0:e0], kh, w.q_tile, w.k_tile, SCALE)[0]
         np.testing.assert_allclose(g[h, i], ref, rtol=1e-3, atol=1e-6)
+
+
+def test_full_size_sparse_backward_sampled():
+    """Gradients of the 16-view stage: one whole head for dq, dk, dv (every query
+    tile reaches every key tile, directly or through its landmark), dq on
+    sampled query tiles of the other heads (dq of a tile depends on its own
+    columns only)."""
+    from parity_util import assert_grad_close
+    w = synth.WORKLOADS["sparse-16v"]
+    n = w.n_tokens
+    print(f"[case] full-size sparse backward {w.name}: N={n} H={w.heads}", flush=True)
+    q, k, v = synth.stage_inputs(w, 0, DEV)
+    bufs = stage_mod.SparseBuffers.allocate(w.heads, n, n, w.q_tile, w.k_tile, w.k, DEV)
+    stage_mod.sparse_stage(q, k, v, w.q_tile, w.k_tile, w.k, SCALE, bufs)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11)
+    dout = torch.randn((w.heads, n, 64), generator=g, device=DEV).bfloat16()
+    dq, dk, dv = zb.zebra_tile_sparse_attn_backward(q, k, v, bufs.kbar, bufs.vbar, bufs.sel,
+                                                    w.q_tile, w.k_tile, w.k, SCALE, dout)
+    torch.cuda.synchronize()
+    sel = bufs.sel.cpu().numpy()
+    h0 = 5
+    rq, rk, rv = zo.tile_sparse_attention_backward(
+        _head(q, h0)[None], _head(k, h0)[None], _head(v, h0)[None], w.q_tile, w.k_tile,
+        sel[h0:h0 + 1], SCALE, _head(dout, h0)[None])
+    assert_grad_close(dq[h0], rq[0], "full-size dq, whole head")
+    assert_grad_close(dk[h0], rk[0], "full-size dk, whole head")
+    assert_grad_close(dv[h0], rv[0], "full-size dv, whole head")
+    for h, i in synth.sample_rows(w.heads, w.t_q, 4, 400):
+        s0, e0 = i * w.q_tile, min(n, (i + 1) * w.q_tile)
+        ref, _, _ = zo.tile_sparse_attention_backward(
+            _head(q, h)[None, s0:e0], _head(k, h)[None], _head(v, h)[None], w.q_tile, w.k_tile,
+            sel[h:h + 1, i:i + 1], SCALE, _head(dout, h)[None, s0:e0])
+        assert_grad_close(dq[h, s0:e0], ref[0], f"full-size dq head {h} tile {i}")
+
+
+def test_full_size_stack_backward_dq_sampled():
+    """dq of two sampled query tiles of the 512-view sparse stage 9 (forward and
+    gradients in split-key chunks, 2,199 of 10,992 key tiles kept)."""
+    from parity_util import assert_grad_close
+    w = synth.WORKLOADS["stack24-512v"]
+    n = w.n_tokens
+    print(f"[case] full-size backward dq {w.name} stage 9: N={n}", flush=True)
+    q, k, v = synth.stage_inputs(w, 9, DEV)
+    bufs = stage_mod.SparseBuffers.allocate(w.heads, n, n, w.q_tile, w.k_tile, w.k, DEV)
+    stage_mod.sparse_stage(q, k, v, w.q_tile, w.k_tile, w.k, SCALE, bufs)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(12)
+    dout = torch.randn((w.heads, n, 64), generator=g, device=DEV).bfloat16()
+    dq, _, _ = zb.zebra_tile_sparse_attn_backward(q, k, v, bufs.kbar, bufs.vbar, bufs.sel,
+                                                  w.q_tile, w.k_tile, w.k, SCALE, dout)
+    torch.cuda.synchronize()
+    for h, i in synth.sample_rows(w.heads, w.t_q, 2, 401):
+        s0, e0 = i * w.q_tile, min(n, (i + 1) * w.q_tile)
+        ref, _, _ = zo.tile_sparse_attention_backward(
+            _head(q, h)[None, s0:e0], _head(k, h)[None], _head(v, h)[None], w.q_tile, w.k_tile,
+            bufs.sel[h:h + 1, i:i + 1].cpu().numpy(), SCALE, _head(dout, h)[None, s0:e0])
+        assert_grad_close(dq[h, s0:e0], ref[0], f"512-view dq head {h} tile {i}")
