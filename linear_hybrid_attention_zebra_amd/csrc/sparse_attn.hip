@@ -127,6 +127,13 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// The value must be computed at this point of the program (an empty asm
+// that reads it); keeps the compiler from sinking its computation further.
+template <typename T>
+__device__ __forceinline__ void keep_vgpr(T x) {
+  asm volatile("" ::"v"(x));
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");
@@ -399,21 +406,20 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
     };
 
     // ---- products
-    auto qk = [&](auto kst_c, f32x16 (&sacc)[NB]) {  // S^T of the block in K stage kst_c
+    // K operands of one block (A of S^T = K Q^T): ka[b][s] = K[32b + qi][16s + 8hh .. +7]
+    auto read_k = [&](auto kst_c, bf16x8 (&ka)[NB][4]) {
       const lds_u8* ks = (const lds_u8*)kbuf(kst_c);
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int row = 32 * b + qi;
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 a = as_bf16x8(
-              *(const __attribute__((address_space(3))) u32x4*)(ks + swz(row, 2 * s + hh)));
-          if (s == 0)
-            sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[0], f32x16{}, 0, 0, 0);
-          else
-            sacc[b] = mfma32(a, qop[s], sacc[b]);
-        }
-      }
+        for (int s = 0; s < 4; ++s)
+          ka[b][s] = as_bf16x8(*(const __attribute__((address_space(3))) u32x4*)(
+              ks + swz(32 * b + qi, 2 * s + hh)));
+    };
+    auto qk_b = [&](const bf16x8 (&ka)[NB][4], f32x16& sacc, int b) {
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[b][0], qop[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+      for (int s = 1; s < 4; ++s) sacc = mfma32(ka[b][s], qop[s], sacc);
     };
     f32x16 oacc[2];
 #pragma unroll
@@ -421,25 +427,31 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
       oacc[0][i] = 0.f;
       oacc[1][i] = 0.f;
     }
-    // O^T[d][q] += V^T[d][key] P^T[key][q], 16 keys per MFMA. Lane group
-    // G = lane/16 covers d offset 16(G%2) and key half G/2; each of the two
-    // transposed reads returns 4 consecutive keys for the lane's channel.
-    auto pv_chunk = [&](auto vst_c, int m, bf16x8 pop) {
+    // V operands (A of O^T[d][q] += V^T[d][key] P^T[key][q]), 16 keys per
+    // MFMA. Lane group G = lane/16 covers d offset 16(G%2) and key half G/2;
+    // each of the two transposed reads returns 4 consecutive keys for the
+    // lane's channel. va[m][db]: keys 16m.., channels 32db..
+    auto read_v = [&](auto vst_c, u32x4 (&va)[2 * NB][2], int m_lo, int m_hi) {
       const lds_u8* vs = (const lds_u8*)vbuf(vst_c);
       const int G = lane >> 4, S = lane & 15;
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        const int col = 32 * db + 16 * (G & 1) + 4 * (S & 3);
-        const int chunk = col >> 3, half = (col & 7) ? 8 : 0;
-        const int r0 = 16 * m + 4 * (G >> 1) + (S >> 2);
-        const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vs + swz(r0, chunk) + half));
-        const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vs + swz(r0 + 8, chunk) + half));
-        const u32x2 w0 = __builtin_bit_cast(u32x2, t0), w1 = __builtin_bit_cast(u32x2, t1);
-        const u32x4 w = {w0.x, w0.y, w1.x, w1.y};
-        oacc[db] = mfma32(as_bf16x8(w), pop, oacc[db]);
-      }
+      for (int m = m_lo; m < m_hi; ++m)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const int col = 32 * db + 16 * (G & 1) + 4 * (S & 3);
+          const int chunk = col >> 3, half = (col & 7) ? 8 : 0;
+          const int r0 = 16 * m + 4 * (G >> 1) + (S >> 2);
+          const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vs + swz(r0, chunk) + half));
+          const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vs + swz(r0 + 8, chunk) + half));
+          const u32x2 w0 = __builtin_bit_cast(u32x2, t0), w1 = __builtin_bit_cast(u32x2, t1);
+          va[m][db] = u32x4{w0.x, w0.y, w1.x, w1.y};
+        }
+    };
+    auto pv_m = [&](const u32x4 (&va)[2 * NB][2], bf16x8 pop, int m) {
+#pragma unroll
+      for (int db = 0; db < 2; ++db) oacc[db] = mfma32(as_bf16x8(va[m][db]), pop, oacc[db]);
     };
     const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
     float l_run = 0.f;
@@ -474,8 +486,20 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
       lo8 = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
       hi8 = as_bf16x8(u32x4{w[4], w[5], w[6], w[7]});
     };
-    // fallback: running maximum, lazy rescale of O and l; returns -reference
-    auto online_ref = [&](const f32x16 (&sacc)[NB]) -> float {
+    // one pair of probabilities (registers 2i, 2i+1 of a score block) as a
+    // packed bf16 word; row sum updated
+    auto prob_pair = [&](const f32x16& s, int i, float nm) -> uint32_t {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i], c, nm));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i + 1], c, nm));
+      const uint32_t w = pack_bf16x2(p0, p1);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, l_run, false);
+      return w;
+    };
+    // fallback: running maximum with lazy rescale of l; returns -reference.
+    // When the reference moves, alpha (per lane) is the factor that O takes
+    // once the pending PV product of the previous block is in, and the return
+    // flag (uniform) says so.
+    auto online_ref = [&](const f32x16 (&sacc)[NB], float& nm, float& alpha) -> bool {
       float tm0 = sacc[0][0], tm1 = sacc[0][1];
 #pragma unroll
       for (int b = 0; b < NB; ++b)
@@ -489,18 +513,17 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
                                                        __float_as_uint(tmax), false, false);
       tmax = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       const float tmc = tmax * c;
+      bool moved = false;
+      alpha = 1.f;
       if (__any(tmc > mc_run + kRescaleSlack)) {
         const float m_new = __builtin_elementwise_maximum(mc_run, tmc);
-        const float alpha = __builtin_amdgcn_exp2f(mc_run - m_new);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          oacc[0][i] *= alpha;
-          oacc[1][i] *= alpha;
-        }
+        alpha = __builtin_amdgcn_exp2f(mc_run - m_new);
         l_run *= alpha;
         mc_run = m_new;
+        moved = true;
       }
-      return -mc_run;
+      nm = -mc_run;
+      return moved;
     };
 
     // variant V2: the landmark of the short last key tile counts its tail_rows
@@ -519,77 +542,140 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
         }
     };
 
-    f32x16 sa0[NB], sa1[NB];
-    auto sbuf = [&](auto par) -> f32x16(&)[NB] {
-      if constexpr (decltype(par)::value == 0) return sa0;
-      else return sa1;
+    // S(t) of the current block; P of the last two blocks (bf16 PV operands),
+    // indexed by block parity. P(-1) = 0, so the PV step of block -1 adds
+    // nothing.
+    f32x16 sacc[NB];
+    bf16x8 pb0[2 * NB], pb1[2 * NB];
+#pragma unroll
+    for (int m = 0; m < 2 * NB; ++m) pb1[m] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    auto pbuf = [&](auto par) -> bf16x8(&)[2 * NB] {
+      if constexpr (decltype(par)::value == 0) return pb0;
+      else return pb1;
     };
 
-    // One step t: wait for K(t+1) and V(t), issue K(t+2) and V(t+1), then
-    // QK(t+1), softmax(t), PV(t). The first two steps (t = -2, -1) only fill
-    // the rings and compute QK(0). Every step issues the same number of loads
-    // (past either end of the list the nearest block is loaded again), so the
-    // outstanding-load count the waits rely on is exact.
+    // One step t (parity par = t & 1): wait for K(t+1) and V(t-1), issue
+    // K(t+2) into K stage par and V(t) into V stage par, then the softmax of
+    // block t (S(t) -> P(t)) interleaved with PV(t-1), then QK(t+1). The
+    // first two steps (t = -2, -1) only fill the rings and compute QK(0); a
+    // last PV step follows the loop. Every step issues the same number of
+    // loads (past either end of the list the nearest block is loaded again),
+    // so the outstanding-load count the waits rely on is exact.
     auto run = [&](auto fast_c) {
       constexpr bool kFast = decltype(fast_c)::value;
-      // QK(t+1), softmax(t), PV(t) as one basic block: the scheduler can then
-      // interleave the score MFMAs of the next block with this block's
-      // softmax arithmetic (the groups below ask for that order).
       auto body = [&](auto par, auto masked_c, uint64_t cmask, float nm_add, int tail_col) {
         constexpr bool kMasked = decltype(masked_c)::value;
-        using Q = std::integral_constant<int, 1 - decltype(par)::value>;
-        f32x16(&cur)[NB] = sbuf(par);
+        using R = std::integral_constant<int, 1 - decltype(par)::value>;
+        u32x4 va[2 * NB][2];
+        bf16x8 ka[NB][4];
+        read_v(R{}, va, 0, 2);  // V(t-1), first 32 keys
+        read_k(R{}, ka);        // K(t+1); past the end a repeated block
         if constexpr (kMasked) {
-          if (tail_col >= 0) add_col(cur, tail_col, p.lm_tail_corr);
+          if (tail_col >= 0) add_col(sacc, tail_col, p.lm_tail_corr);
+          apply_mask(sacc, cmask);
         }
-        qk(Q{}, sbuf(Q{}));  // QK(t+1); past the end it reads a repeated block
-        if constexpr (kMasked) apply_mask(cur, cmask);
-        float nm = nm_fast;
-        if constexpr (!kFast) nm = online_ref(cur);
+        float nm = nm_fast, alpha = 1.f;
+        bool moved = false;
+        if constexpr (!kFast) moved = online_ref(sacc, nm, alpha);
         if constexpr (kMasked) nm += nm_add;  // landmark blocks: log2(KT) under V2
+        bf16x8(&pw)[2 * NB] = pbuf(par);
+        bf16x8(&pr)[2 * NB] = pbuf(R{});
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          bf16x8 lo8, hi8;
-          probs(cur[b], nm, lo8, hi8);
-          pv_chunk(par, 2 * b, lo8);
-          pv_chunk(par, 2 * b + 1, hi8);
+          if (b == 1) read_v(R{}, va, 2, 4);  // V(t-1), last 32 keys
+          probs(sacc[b], nm, pw[2 * b], pw[2 * b + 1]);
+          pv_m(va, pr[2 * b], 2 * b);
+          pv_m(va, pr[2 * b + 1], 2 * b + 1);
         }
-        if constexpr (kFast && !kMasked && KT == 64) {
-          // QK(t+1): its K reads two ahead, each MFMA followed by 6 VALU ops
-          // (the softmax of score block 0); then PV(t): the V reads of the
-          // next 16-key chunk ahead of each MFMA pair, the first four MFMAs
-          // each followed by 12 VALU ops (score block 1)
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        if constexpr (!kFast) {
+          if (moved) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            for (int i = 0; i < 16; ++i) {
+              oacc[0][i] *= alpha;
+              oacc[1][i] *= alpha;
+            }
           }
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        }
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            if (m < 3) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (m < 2) __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (m < 2) __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+        for (int b = 0; b < NB; ++b) qk_b(ka, sacc[b], b);  // QK(t+1)
+        // P(t) and the row sum are complete within this step (keeps the
+        // compiler from sinking the softmax into the next step, past its barrier)
+#pragma unroll
+        for (int m = 0; m < 2 * NB; ++m)
+          keep_vgpr(__builtin_bit_cast(u32x4, pw[m]));
+        keep_vgpr(l_run);
+      };
+      // The plain fast step of 64-key blocks with the instruction order fixed
+      // by scheduling fences: 16 MFMA slots, and the 16 pair jobs (two
+      // probabilities each) spread over the first 12 so that each wave's
+      // MFMAs run while it issues its own softmax arithmetic. Two jobs while
+      // the operand reads land; slots 1-8: PV(t-1) (P(t-1) and V(t-1) are
+      // ready), one job each; slots 9-12: QK(t+1) into score block 0 (its
+      // probabilities are out), the last six jobs; 13-16: QK(t+1) into score
+      // block 1.
+      auto body_fast64 = [&](auto par) {
+        if constexpr (KT == 64) {
+          using R = std::integral_constant<int, 1 - decltype(par)::value>;
+          u32x4 va[4][2];
+          bf16x8 ka[2][4];
+          uint32_t w0[8], w1[8];
+          bf16x8(&pw)[4] = pbuf(par);
+          bf16x8(&pr)[4] = pbuf(R{});
+          const float nm = nm_fast;
+          read_v(R{}, va, 0, 2);  // V(t-1), first 32 keys
+          read_k(R{}, ka);        // K(t+1); past the end a repeated block
+          // pair jobs in order: score block 0 pairs 0-7, then block 1 pairs 0-7
+          auto job = [&](int n) {
+            if (n < 8)
+              w0[n] = prob_pair(sacc[0], n, nm);
+            else
+              w1[n - 8] = prob_pair(sacc[1], n - 8, nm);
+          };
+          job(0);  // while the operand reads land
+          job(1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {  // slots 1-8: PV(t-1), jobs 2-9
+            oacc[j & 1] = mfma32(as_bf16x8(va[j >> 1][j & 1]), pr[j >> 1], oacc[j & 1]);
+            job(2 + j);
+            if (j == 1) read_v(R{}, va, 2, 4);  // V(t-1), last 32 keys
+            __builtin_amdgcn_sched_barrier(0);
           }
+          pw[0] = as_bf16x8(u32x4{w0[0], w0[1], w0[2], w0[3]});
+          pw[1] = as_bf16x8(u32x4{w0[4], w0[5], w0[6], w0[7]});
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {  // slots 9-12: QK(t+1) of score block 0, jobs 10-15
+            sacc[0] = j == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0][0], qop[0], f32x16{},
+                                                                        0, 0, 0)
+                             : mfma32(ka[0][j], qop[j], sacc[0]);
+            job(10 + (j < 2 ? 2 * j : j + 2));
+            if (j < 2) job(11 + 2 * j);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          pw[2] = as_bf16x8(u32x4{w1[0], w1[1], w1[2], w1[3]});
+          pw[3] = as_bf16x8(u32x4{w1[4], w1[5], w1[6], w1[7]});
+          qk_b(ka, sacc[1], 1);  // slots 13-16
+#pragma unroll
+          for (int m = 0; m < 4; ++m) keep_vgpr(__builtin_bit_cast(u32x4, pw[m]));
+          keep_vgpr(l_run);
         }
       };
       // masked_c: the block may exclude columns (landmark blocks and a short
       // last kept tile); the other blocks run the branch-free body
       auto step = [&](int t, auto par, auto masked_c) {
-        constexpr int PAR = decltype(par)::value;
-        using Q = std::integral_constant<int, 1 - PAR>;
-        wait_vmcnt<0>();  // this wave's loads of K(t+1), V(t) have landed
-        lds_barrier();    // ... and every other wave's; stages PAR (K), 1-PAR (V) are free
+        wait_vmcnt<0>();  // this wave's loads of K(t+1), V(t-1) have landed
+        lds_barrier();    // ... and every other wave's; stage par of both rings is free
         const int tkn = min(t + 2, n_total - 1);
-        const int tvn = max(min(t + 1, n_total - 1), 0);
+        const int tvn = max(min(t, n_total - 1), 0);
         ensure_window(tvn, tkn);
         issue(tkn, kh, klm, kbuf(par));
-        issue(tvn, vh, vlm, vbuf(Q{}));
-        if (t == -1) qk(Q{}, sbuf(Q{}));
+        issue(tvn, vh, vlm, vbuf(par));
+        if (t == -1) {
+          bf16x8 ka[NB][4];
+          read_k(P0{}, ka);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) qk_b(ka, sacc[b], b);  // QK(0)
+        }
         if (t < 0) return;
         if constexpr (decltype(masked_c)::value) {
           const bool lm = t >= n_kept;
@@ -597,9 +683,21 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
                                ? last_lrows - 1
                                : -1;
           body(par, masked_c, block_mask(t), lm ? lm_shift : 0.f, tcol);
+        } else if constexpr (kFast && KT == 64) {
+          body_fast64(par);
         } else {
           body(par, masked_c, 0ull, 0.f, -1);
         }
+      };
+      // PV of the last block t = n_total - 1 (parity par)
+      auto drain = [&](auto par) {
+        wait_vmcnt<0>();  // also: no direct-to-LDS load outlives the item
+        lds_barrier();
+        u32x4 va[2 * NB][2];
+        read_v(par, va, 0, 2 * NB);
+        bf16x8(&pr)[2 * NB] = pbuf(par);
+#pragma unroll
+        for (int m = 0; m < 2 * NB; ++m) pv_m(va, pr[m], m);
       };
       using Plain = std::false_type;
       using Masked = std::true_type;
@@ -619,7 +717,10 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
         step(t + 1, P1{}, Masked{});
       }
       if (t < n_total) step(t, P0{}, Masked{});
-      wait_vmcnt<0>();  // no direct-to-LDS load may outlive the item
+      if ((n_total - 1) & 1)
+        drain(P1{});
+      else
+        drain(P0{});
     };
     if (n_total > 0) {  // an item may have no columns: split keys without landmarks
       if (fast)
