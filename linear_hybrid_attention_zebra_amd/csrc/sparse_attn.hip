@@ -55,11 +55,14 @@
 // probability by KT so that the landmarks' stay below 2^60.
 //
 // Pipeline. K and V blocks go global -> LDS directly
-// (global_load_lds_dwordx4) into two-stage rings, the K ring one block ahead
-// of the V ring: step t issues K(t+2) and V(t+1), then computes QK(t+1),
-// the softmax of block t and PV(t), so the next block's score MFMAs overlap
-// this block's softmax arithmetic. One barrier per step. 16-byte LDS chunks
-// are XOR swizzled by row so both operand reads are bank-conflict free.
+// (global_load_lds_dwordx4) into two-stage rings: step t issues K(t+2) and
+// V(t), then computes the softmax of block t (S(t) -> bf16 P(t)) together
+// with PV(t-1), and then QK(t+1). The PV product of the previous block does
+// not depend on this block's softmax, so each wave's MFMAs run while the
+// same wave issues its softmax arithmetic; one score buffer and two P
+// buffers (bf16) keep the operands of the next block's reads in registers.
+// One barrier per step. 16-byte LDS chunks are XOR swizzled by row so both
+// operand reads are bank-conflict free.
 #include <algorithm>
 #include <type_traits>
 
@@ -407,14 +410,16 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
 
     // ---- products
     // K operands of one block (A of S^T = K Q^T): ka[b][s] = K[32b + qi][16s + 8hh .. +7]
-    auto read_k = [&](auto kst_c, bf16x8 (&ka)[NB][4]) {
+    auto read_k1 = [&](auto kst_c, bf16x8 (&ka)[NB][4], int b, int s) {
       const lds_u8* ks = (const lds_u8*)kbuf(kst_c);
+      ka[b][s] = as_bf16x8(
+          *(const __attribute__((address_space(3))) u32x4*)(ks + swz(32 * b + qi, 2 * s + hh)));
+    };
+    auto read_k = [&](auto kst_c, bf16x8 (&ka)[NB][4]) {
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          ka[b][s] = as_bf16x8(*(const __attribute__((address_space(3))) u32x4*)(
-              ks + swz(32 * b + qi, 2 * s + hh)));
+        for (int s = 0; s < 4; ++s) read_k1(kst_c, ka, b, s);
     };
     auto qk_b = [&](const bf16x8 (&ka)[NB][4], f32x16& sacc, int b) {
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[b][0], qop[0], f32x16{}, 0, 0, 0);
@@ -460,17 +465,22 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
     // lane holds keys 32b + 8g + 4hh + r in register 4g + r of score block b.
     // colmask is uniform: per register, the excluded lanes form a 64-bit lane
     // mask built with scalar ops, applied by one v_cndmask.
+    // register i of score block b holds key 32b + 8(i/4) + 4hh + i%4: the
+    // lanes (half hh = 0: low 32, hh = 1: high 32) whose key is set in the
+    // uniform column mask, as a 64-bit lane mask (two sign-extended bits)
+    auto lanes_of = [&](uint64_t colmask, int b, int i) -> uint64_t {
+      const uint32_t w = (uint32_t)(colmask >> (32 * b));
+      const int off = 8 * (i >> 2) + (i & 3);
+      const uint32_t lo = (uint32_t)(((int32_t)(w << (31 - off))) >> 31);
+      const uint32_t hi = (uint32_t)(((int32_t)(w << (27 - off))) >> 31);
+      return ((uint64_t)hi << 32) | lo;
+    };
     auto apply_mask = [&](f32x16 (&sacc)[NB], uint64_t colmask) {
-      const uint64_t m0 = colmask, m1 = colmask >> 4;  // lane halves 0 and 1
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int bit = 32 * b + 8 * (i >> 2) + (i & 3);
-          const uint64_t lanes = (((m0 >> bit) & 1ull) ? 0x00000000ffffffffull : 0ull) |
-                                 (((m1 >> bit) & 1ull) ? 0xffffffff00000000ull : 0ull);
-          if (__builtin_amdgcn_inverse_ballot_w64(lanes)) sacc[b][i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i)
+          if (__builtin_amdgcn_inverse_ballot_w64(lanes_of(colmask, b, i))) sacc[b][i] = -INFINITY;
     };
     // probabilities of one score block -> two PV operands, row sum updated
     auto probs = [&](const f32x16& s, float nm, bf16x8& lo8, bf16x8& hi8) {
@@ -530,16 +540,12 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
     // tokens, not KT: add corr to the score of column col (uniform) of the block,
     // with the same uniform lane masks as apply_mask
     auto add_col = [&](f32x16 (&sacc)[NB], int col, float corr) {
-      const uint64_t m0 = 1ull << col, m1 = m0 >> 4;  // lane halves 0 and 1
+      const uint64_t m = 1ull << col;
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int bit = 32 * b + 8 * (i >> 2) + (i & 3);
-          const uint64_t lanes = (((m0 >> bit) & 1ull) ? 0x00000000ffffffffull : 0ull) |
-                                 (((m1 >> bit) & 1ull) ? 0xffffffff00000000ull : 0ull);
-          if (__builtin_amdgcn_inverse_ballot_w64(lanes)) sacc[b][i] += corr;
-        }
+        for (int i = 0; i < 16; ++i)
+          if (__builtin_amdgcn_inverse_ballot_w64(lanes_of(m, b, i))) sacc[b][i] += corr;
     };
 
     // S(t) of the current block; P of the last two blocks (bf16 PV operands),
@@ -605,7 +611,7 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
           keep_vgpr(__builtin_bit_cast(u32x4, pw[m]));
         keep_vgpr(l_run);
       };
-      // The plain fast step of 64-key blocks with the instruction order fixed
+      // The fast step of 64-key blocks with the instruction order fixed
       // by scheduling fences: 16 MFMA slots, and the 16 pair jobs (two
       // probabilities each) spread over the first 12 so that each wave's
       // MFMAs run while it issues its own softmax arithmetic. Two jobs while
@@ -613,7 +619,8 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
       // ready), one job each; slots 9-12: QK(t+1) into score block 0 (its
       // probabilities are out), the last six jobs; 13-16: QK(t+1) into score
       // block 1.
-      auto body_fast64 = [&](auto par) {
+      auto body_fast64 = [&](auto par, auto masked_c, uint64_t cmask, float nm_add,
+                             int tail_col) {
         if constexpr (KT == 64) {
           using R = std::integral_constant<int, 1 - decltype(par)::value>;
           u32x4 va[4][2];
@@ -621,9 +628,13 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
           uint32_t w0[8], w1[8];
           bf16x8(&pw)[4] = pbuf(par);
           bf16x8(&pr)[4] = pbuf(R{});
-          const float nm = nm_fast;
+          float nm = nm_fast;
           read_v(R{}, va, 0, 2);  // V(t-1), first 32 keys
-          read_k(R{}, ka);        // K(t+1); past the end a repeated block
+          if constexpr (decltype(masked_c)::value) {
+            if (tail_col >= 0) add_col(sacc, tail_col, p.lm_tail_corr);
+            apply_mask(sacc, cmask);
+            nm += nm_add;  // landmark blocks: log2(KT) under V2
+          }
           // pair jobs in order: score block 0 pairs 0-7, then block 1 pairs 0-7
           auto job = [&](int n) {
             if (n < 8)
@@ -638,7 +649,14 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
           for (int j = 0; j < 8; ++j) {  // slots 1-8: PV(t-1), jobs 2-9
             oacc[j & 1] = mfma32(as_bf16x8(va[j >> 1][j & 1]), pr[j >> 1], oacc[j & 1]);
             job(2 + j);
-            if (j == 1) read_v(R{}, va, 2, 4);  // V(t-1), last 32 keys
+            // the other operand reads, at most 15 in flight: K(t+1) of score
+            // block 0 (slots 1-2), V(t-1) of the last 32 keys (3-4), K(t+1)
+            // of score block 1 (5-6); past the end a repeated block
+            if (j < 2 || (j >= 4 && j < 6)) {
+              read_k1(R{}, ka, j >> 2, 2 * (j & 1));
+              read_k1(R{}, ka, j >> 2, 2 * (j & 1) + 1);
+            }
+            if (j == 2 || j == 3) read_v(R{}, va, j, j + 1);
             __builtin_amdgcn_sched_barrier(0);
           }
           pw[0] = as_bf16x8(u32x4{w0[0], w0[1], w0[2], w0[3]});
@@ -682,9 +700,12 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
           const int tcol = lm && log_count && lb0 + t - n_kept == n_lb_all - 1 && tail_rows < KT
                                ? last_lrows - 1
                                : -1;
-          body(par, masked_c, block_mask(t), lm ? lm_shift : 0.f, tcol);
+          if constexpr (kFast && KT == 64)
+            body_fast64(par, masked_c, block_mask(t), lm ? lm_shift : 0.f, tcol);
+          else
+            body(par, masked_c, block_mask(t), lm ? lm_shift : 0.f, tcol);
         } else if constexpr (kFast && KT == 64) {
-          body_fast64(par);
+          body_fast64(par, masked_c, 0ull, 0.f, -1);
         } else {
           body(par, masked_c, 0ull, 0.f, -1);
         }
