@@ -260,6 +260,28 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
   // ---- direct-to-LDS staging. 1 KB block u of a tile holds rows 8u..8u+7;
   // lane i writes physical chunk i%8 of row r = 8u + i/8, i.e. logical chunk
   // (i%8) ^ swz_f(r). This wave stages blocks u = wave + W v.
+  // Per-lane byte offsets of the MFMA operand reads within a staged block
+  // (the same for every item). K: key row qi, chunk 2s + hh; the second score
+  // block is 32 rows (4096 bytes) further. V (transposed reads): lane group
+  // G = lane/16 covers channel offset 16(G%2) and key half G/2; each of the
+  // two reads returns 4 consecutive keys (rows r0 and r0 + 8) of the lane's
+  // channel, channel block db adds 32 channels; each further 16 keys are 16
+  // rows (2048 bytes) further. The swizzle depends on row bits 1-3 only, so
+  // those row steps are plain offsets.
+  uint32_t koff[4], voff[2][2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) koff[s] = swz(qi, 2 * s + hh);
+  {
+    const int G = lane >> 4, S = lane & 15;
+    const int r0 = 4 * (G >> 1) + (S >> 2);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int col = 32 * db + 16 * (G & 1) + 4 * (S & 3);
+      const int chunk = col >> 3, half = (col & 7) ? 8 : 0;
+      voff[db][0] = swz(r0, chunk) + half;
+      voff[db][1] = swz(r0 + 8, chunk) + half;
+    }
+  }
   const int lrow = lane >> 3;
   int lchunk[NU];
   uint32_t off_kv[NU], off_lm[NU];
@@ -412,8 +434,8 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
     // K operands of one block (A of S^T = K Q^T): ka[b][s] = K[32b + qi][16s + 8hh .. +7]
     auto read_k1 = [&](auto kst_c, bf16x8 (&ka)[NB][4], int b, int s) {
       const lds_u8* ks = (const lds_u8*)kbuf(kst_c);
-      ka[b][s] = as_bf16x8(
-          *(const __attribute__((address_space(3))) u32x4*)(ks + swz(32 * b + qi, 2 * s + hh)));
+      ka[b][s] =
+          as_bf16x8(*(const __attribute__((address_space(3))) u32x4*)(ks + koff[s] + 4096 * b));
     };
     auto read_k = [&](auto kst_c, bf16x8 (&ka)[NB][4]) {
 #pragma unroll
@@ -433,23 +455,17 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
       oacc[1][i] = 0.f;
     }
     // V operands (A of O^T[d][q] += V^T[d][key] P^T[key][q]), 16 keys per
-    // MFMA. Lane group G = lane/16 covers d offset 16(G%2) and key half G/2;
-    // each of the two transposed reads returns 4 consecutive keys for the
-    // lane's channel. va[m][db]: keys 16m.., channels 32db..
+    // MFMA. va[m][db]: keys 16m.., channels 32db..
     auto read_v = [&](auto vst_c, u32x4 (&va)[2 * NB][2], int m_lo, int m_hi) {
       const lds_u8* vs = (const lds_u8*)vbuf(vst_c);
-      const int G = lane >> 4, S = lane & 15;
 #pragma unroll
       for (int m = m_lo; m < m_hi; ++m)
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
-          const int col = 32 * db + 16 * (G & 1) + 4 * (S & 3);
-          const int chunk = col >> 3, half = (col & 7) ? 8 : 0;
-          const int r0 = 16 * m + 4 * (G >> 1) + (S >> 2);
           const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(vs + swz(r0, chunk) + half));
+              (__attribute__((address_space(3))) i16x4*)(vs + voff[db][0] + 2048 * m));
           const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(vs + swz(r0 + 8, chunk) + half));
+              (__attribute__((address_space(3))) i16x4*)(vs + voff[db][1] + 2048 * m));
           const u32x2 w0 = __builtin_bit_cast(u32x2, t0), w1 = __builtin_bit_cast(u32x2, t1);
           va[m][db] = u32x4{w0.x, w0.y, w1.x, w1.y};
         }
