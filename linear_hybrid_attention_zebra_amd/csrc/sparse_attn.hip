@@ -81,6 +81,7 @@ constexpr int kWin = 2040;                  // kept-list window entries in LDS
 constexpr int kMaxKeyTiles = 32768;
 constexpr int kBitWords = kMaxKeyTiles / 32;
 constexpr int kRangeParts = 64;             // per-head partial maxima (one per lane)
+constexpr int kBufferFlags = 0x00020000;    // buffer resource word 3: 32-bit data format
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;  // LDS bytes
@@ -135,6 +136,17 @@ __device__ __forceinline__ void lds_barrier() {
 template <typename T>
 __device__ __forceinline__ void keep_vgpr(T x) {
   asm volatile("" ::"v"(x));
+}
+
+// 16 bytes per lane from a buffer resource straight into LDS (the buffer
+// form of the direct-to-LDS load: reads past the records return zeros)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferFlags);
+}
+__device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t r,
+                                              __attribute__((address_space(3))) void* dst,
+                                              uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
 }
 
 template <int N>
@@ -387,9 +399,14 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&dst[u][0],
                                        16, 0, 0);
     };
-    // stage block t of the list: kept key tile (rows past a short last tile
-    // repeat its last row) or landmark block (rows past tk repeat row tk-1)
-    auto issue = [&](int t, const uint8_t* th, const uint8_t* tl, lds_blk* dst) {
+    // sources of block t of the list: kept key tile (rows past a short last
+    // tile repeat its last row) or landmark block (rows past tk repeat row
+    // tk-1); this wave's 1 KB pieces v = 0..NU-1 go to blocks wave + W v
+    struct Src {
+      const uint8_t* base;
+      uint32_t off[NU];
+    };
+    auto prep = [&](int t, const uint8_t* th, const uint8_t* tl) -> Src {
       const uint8_t* base;
       uint32_t off[NU];
       int rows;
@@ -416,8 +433,19 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
           off[v] = (uint32_t)(r * row_bytes + lchunk[v] * 16);
         }
       }
+      Src src;
+      src.base = base;
 #pragma unroll
-      for (int v = 0; v < NU; ++v) dma(base + off[v], dst, wave + W * v);
+      for (int v = 0; v < NU; ++v) src.off[v] = off[v];
+      return src;
+    };
+    auto fire = [&](const Src& src, lds_blk* dst, int v) {
+      dma(src.base + src.off[v], dst, wave + W * v);
+    };
+    auto issue = [&](int t, const uint8_t* th, const uint8_t* tl, lds_blk* dst) {
+      const Src src = prep(t, th, tl);
+#pragma unroll
+      for (int v = 0; v < NU; ++v) fire(src, dst, v);
     };
     // excluded columns of block t (bit set = excluded), or 0
     auto block_mask = [&](int t) -> uint64_t {
@@ -636,7 +664,7 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
       // probabilities are out), the last six jobs; 13-16: QK(t+1) into score
       // block 1.
       auto body_fast64 = [&](auto par, auto masked_c, uint64_t cmask, float nm_add,
-                             int tail_col) {
+                             int tail_col, const Src& sk, const Src& sv) {
         if constexpr (KT == 64) {
           using R = std::integral_constant<int, 1 - decltype(par)::value>;
           u32x4 va[4][2];
@@ -673,6 +701,16 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
               read_k1(R{}, ka, j >> 2, 2 * (j & 1) + 1);
             }
             if (j == 2 || j == 3) read_v(R{}, va, j, j + 1);
+            // the loads of K(t+2) and V(t): 2 NU pieces over slots 1-8
+            constexpr int kPer = (2 * NU + 7) / 8;
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+              const int q = j * kPer + k;
+              if (q < NU)
+                fire(sk, kbuf(par), q);
+              else if (q < 2 * NU)
+                fire(sv, vbuf(par), q - NU);
+            }
             __builtin_amdgcn_sched_barrier(0);
           }
           pw[0] = as_bf16x8(u32x4{w0[0], w0[1], w0[2], w0[3]});
@@ -702,8 +740,15 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
         const int tkn = min(t + 2, n_total - 1);
         const int tvn = max(min(t, n_total - 1), 0);
         ensure_window(tvn, tkn);
-        issue(tkn, kh, klm, kbuf(par));
-        issue(tvn, vh, vlm, vbuf(par));
+        const Src sk = prep(tkn, kh, klm), sv = prep(tvn, vh, vlm);
+        // the fast 64-key steps issue these loads inside their MFMA slots
+        constexpr bool kSpread = kFast && KT == 64;
+        if (!kSpread || t < 0) {
+#pragma unroll
+          for (int v = 0; v < NU; ++v) fire(sk, kbuf(par), v);
+#pragma unroll
+          for (int v = 0; v < NU; ++v) fire(sv, vbuf(par), v);
+        }
         if (t == -1) {
           bf16x8 ka[NB][4];
           read_k(P0{}, ka);
@@ -717,11 +762,11 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
                                ? last_lrows - 1
                                : -1;
           if constexpr (kFast && KT == 64)
-            body_fast64(par, masked_c, block_mask(t), lm ? lm_shift : 0.f, tcol);
+            body_fast64(par, masked_c, block_mask(t), lm ? lm_shift : 0.f, tcol, sk, sv);
           else
             body(par, masked_c, block_mask(t), lm ? lm_shift : 0.f, tcol);
         } else if constexpr (kFast && KT == 64) {
-          body_fast64(par, masked_c, 0ull, 0.f, -1);
+          body_fast64(par, masked_c, 0ull, 0.f, -1, sk, sv);
         } else {
           body(par, masked_c, 0ull, 0.f, -1);
         }
@@ -806,6 +851,596 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
           for (int g = 0; g < 4; ++g) {
             u32x2 w = {pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
                        pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+            *(u32x2*)(op + 32 * db + 8 * g) = w;
+          }
+      }
+    }
+  }
+}
+
+// Key-half decomposition (64-key tiles; 64 or 128 queries per item, i.e. 2
+// or 4 waves). Wave w takes key half kh = w % 2 (keys 32kh .. 32kh + 31 of
+// every block) for query group qg = w / 2 (64 queries, two 32-query MFMA
+// column tiles qh = 0, 1). Every K or V operand fragment read from LDS then
+// feeds two MFMAs, one per query half: half the LDS operand traffic of the
+// one-wave-per-32-queries layout, the other large user of LDS bandwidth
+// besides the direct-to-LDS loads. Rings, block list and pipeline are those
+// of tile_sparse_kernel. At the end of an item the two key halves of a query
+// group meet in LDS: wave kh keeps query half kh and hands the other half's
+// partial output, row sum and reference to its partner. With the fixed
+// reference both partials share it and simply add; on the fallback path each
+// is first scaled to the larger of the two running maxima.
+template <int QT>
+__global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) void tile_sparse_kh_kernel(
+    SparseParams p, const int32_t* __restrict__ sel) {
+  constexpr int KT = 64;
+  constexpr int W = QT / 32;             // waves: (query group, key half) pairs
+  constexpr int NT = W * kWave;
+  constexpr int KB_PER_TILE = KT * 128 / 1024;
+  constexpr int NU = KB_PER_TILE / W;    // 1 KB direct-to-LDS pieces per wave per tensor
+  static_assert(KB_PER_TILE % W == 0 && W >= 2, "load split");
+
+  __shared__ u32x4 ks0[KB_PER_TILE][64], ks1[KB_PER_TILE][64];
+  __shared__ u32x4 vs0[KB_PER_TILE][64], vs1[KB_PER_TILE][64];
+  __shared__ uint16_t win[kWin];
+  __shared__ uint32_t kept_bits[kBitWords];
+  __shared__ int32_t slow_item;
+  typedef __attribute__((address_space(3))) u32x4 lds_blk[64];
+  auto kbuf = [&](auto stc) -> lds_blk* {
+    if constexpr (decltype(stc)::value == 0) return (lds_blk*)ks0;
+    else return (lds_blk*)ks1;
+  };
+  auto vbuf = [&](auto stc) -> lds_blk* {
+    if constexpr (decltype(stc)::value == 0) return (lds_blk*)vs0;
+    else return (lds_blk*)vs1;
+  };
+  // end-of-item exchange: wave w's 8 KB of partial output in ring block w
+  auto xbuf = [&](int w) -> __attribute__((address_space(3))) f32x4* {
+    u32x4* b = w == 0 ? &ks0[0][0] : (w == 1 ? &ks1[0][0] : (w == 2 ? &vs0[0][0] : &vs1[0][0]));
+    return (__attribute__((address_space(3))) f32x4*)b;
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int kh = wave & 1, qg = wave >> 1;
+  const int lane = tid % kWave;
+  const int qi = lane & 31;
+  const int hh = lane >> 5;
+  const bool dense = sel == nullptr;
+  const int n_lb_all = dense || !p.landmarks ? 0 : (p.tk + KT - 1) / KT;
+  const int tail_rows = (int)(p.nk - (int64_t)(p.tk - 1) * KT);
+  const int last_lrows = p.tk - (n_lb_all - 1) * KT;
+  const float c = p.scale_log2;
+  const bool log_count = p.log_count != 0;
+  const float lm_shift = log_count ? p.lm_log2_kt : 0.f;
+  const int n_ch = p.n_chunks;
+  const int lb_per_chunk = p.chunk_tiles / KT;
+  const int64_t items_per_head = (int64_t)n_ch * p.tq;
+
+  // Operand read offsets within a staged block (see tile_sparse_kernel); the
+  // key half adds 32 rows (4096 bytes).
+  uint32_t koff[4], voff[2][2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) koff[s] = swz(qi, 2 * s + hh) + 4096 * kh;
+  {
+    const int G = lane >> 4, S = lane & 15;
+    const int r0 = 4 * (G >> 1) + (S >> 2);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int col = 32 * db + 16 * (G & 1) + 4 * (S & 3);
+      const int chunk = col >> 3, half = (col & 7) ? 8 : 0;
+      voff[db][0] = swz(r0, chunk) + half + 4096 * kh;
+      voff[db][1] = swz(r0 + 8, chunk) + half + 4096 * kh;
+    }
+  }
+  // direct-to-LDS staging as in tile_sparse_kernel, through buffer
+  // resources: piece v covers rows 8(wave + W v) + lane/8 of a block; W is
+  // even, so the lane's swizzled chunk is the same for every piece. The
+  // resource of a block ends at its last valid row, so the rows past a short
+  // last tile read as zeros (their columns are masked).
+  const int lrow = lane >> 3;
+  const int r_lane = 8 * wave + lrow;
+  const int lchunk = (lane & 7) ^ swz_f(r_lane);
+  // (key/value rows are 128 bytes apart here, like landmark rows)
+  uint32_t off_v[NU];
+#pragma unroll
+  for (int v = 0; v < NU; ++v) off_v[v] = (uint32_t)((r_lane + 8 * W * v) * 128 + lchunk * 16);
+
+  for (int64_t item = blockIdx.x; item < p.n_items; item += gridDim.x) {
+    const int h = (int)(item / items_per_head);
+    const int64_t rem = item - (int64_t)h * items_per_head;
+    const int ch = (int)(rem / p.tq);
+    const int qtile = (int)(rem - (int64_t)ch * p.tq);
+    const int64_t row = (int64_t)h * p.tq + qtile;
+    int kept0 = 0, n_kept = dense ? p.tk : p.top_k, lb0 = 0, n_lb = n_lb_all;
+    if (n_ch > 1) {
+      const int32_t* co = p.coff + row * (n_ch + 1) + ch;
+      kept0 = __builtin_amdgcn_readfirstlane(co[0]);
+      n_kept = max(__builtin_amdgcn_readfirstlane(co[1]) - kept0, 0);
+      lb0 = ch * lb_per_chunk;
+      n_lb = n_lb_all > 0 ? min(lb_per_chunk, n_lb_all - lb0) : 0;
+    }
+    const int n_total = n_kept + n_lb;
+    const int32_t* sel_row = dense ? nullptr : sel + row * p.top_k + kept0;
+    const uint8_t* khp = (const uint8_t*)(p.k + (int64_t)h * p.ksh);
+    const uint8_t* vhp = (const uint8_t*)(p.v + (int64_t)h * p.ksh);
+    const bool has_lm = n_lb_all > 0;
+    const uint8_t* klm =
+        has_lm ? (const uint8_t*)(p.kbar_b + (int64_t)h * p.tk * kHeadDim) : nullptr;
+    const uint8_t* vlm =
+        has_lm ? (const uint8_t*)(p.vbar_b + (int64_t)h * p.tk * kHeadDim) : nullptr;
+
+    lds_barrier();  // every wave is done with the previous item's LDS
+    if (tid == 0) slow_item = 0;
+    if (n_lb > 0) {
+      const int words = 2 * n_lb;
+      for (int e = tid; e < words; e += NT) kept_bits[2 * lb0 + e] = 0u;
+    }
+    if (!dense) {
+      const int nw = min(kWin, n_kept);
+      for (int e = tid; e < nw; e += NT) win[e] = (uint16_t)min(max(sel_row[e], 0), p.tk - 1);
+    }
+    // query operands of both query halves: Q[q][16s + 8hh .. +7]
+    const int64_t qbase = (int64_t)qtile * QT + 64 * qg + qi;
+    bf16x8 qop[2][4];
+    float qq[2] = {0.f, 0.f};
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      const int64_t qr = qbase + 32 * qh;
+      const uint16_t* qp = p.q + (int64_t)h * p.qsh + qr * p.qst + 8 * hh;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (qr < p.nq) w = *(const u32x4*)(qp + 16 * s);
+        qop[qh][s] = as_bf16x8(w);
+        qq[qh] += sum8_sq(w);
+      }
+    }
+    float k2 = p.range[((int64_t)h * kRangeParts + lane) * 2];
+    float vmax = p.range[((int64_t)h * kRangeParts + lane) * 2 + 1];
+    const int last_kept =
+        dense ? p.tk - 1 : (n_kept > 0 ? min(max(sel_row[n_kept - 1], 0), p.tk - 1) : -1);
+    __syncthreads();
+    if (n_lb > 0)
+      for (int e = tid; e < n_kept; e += NT) {
+        const int j = min(max(sel_row[e], 0), p.tk - 1);
+        atomicOr(&kept_bits[j >> 5], 1u << (j & 31));
+      }
+    k2 = wave_max(k2);
+    vmax = wave_max(vmax);
+    float m_q[2], nm_fast[2];
+    bool fast_ok = vmax <= kVLimit;
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(qq[qh]),
+                                                       __float_as_uint(qq[qh]), false, false);
+      const float q2 = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      m_q[qh] = c * __builtin_sqrtf(q2) * __builtin_sqrtf(k2) * (1.0f + 1.0f / 64.0f) + 1.0f;
+      fast_ok = fast_ok && m_q[qh] <= kBoundLimit;
+      nm_fast[qh] = kPShift - m_q[qh] - lm_shift;
+    }
+    if (!__all(fast_ok) && lane == 0) slow_item = 1;
+    __syncthreads();
+    const bool fast = slow_item == 0;
+    const int last_rows = last_kept == p.tk - 1 ? tail_rows : KT;
+
+    int win_lo = 0;
+    auto ensure_window = [&](int t_v, int t_k) {
+      if (dense || t_v >= n_kept) return;
+      const int hi = min(t_k, n_kept - 1);
+      if (t_v >= win_lo && hi < win_lo + kWin) return;
+      win_lo = t_v;
+      const int nw = min(kWin, n_kept - t_v);
+      for (int e = tid; e < nw; e += NT)
+        win[e] = (uint16_t)min(max(sel_row[t_v + e], 0), p.tk - 1);
+      __syncthreads();  // no direct-to-LDS load is in flight here
+    };
+    // a block as a buffer resource whose records end at its last valid row
+    typedef __amdgpu_buffer_rsrc_t Src;
+    auto prep = [&](int t, const uint8_t* th, const uint8_t* tl) -> Src {
+      const uint8_t* base;
+      int rows;
+      if (t < n_kept) {
+        const int j = dense ? t : __builtin_amdgcn_readfirstlane(win[t - win_lo]);
+        rows = j == p.tk - 1 ? tail_rows : KT;
+        base = th + (int64_t)j * KT * 128;
+      } else {
+        const int b = lb0 + t - n_kept;
+        rows = b == n_lb_all - 1 ? last_lrows : KT;
+        base = tl + (int64_t)b * KT * 128;
+      }
+      return block_rsrc(base, rows * 128);
+    };
+    auto fire = [&](const Src& src, lds_blk* dst, int v) {
+      buffer_to_lds(src, (__attribute__((address_space(3))) void*)&dst[wave + W * v][0], off_v[v]);
+    };
+    auto block_mask = [&](int t) -> uint64_t {
+      if (t < n_kept) return t == n_kept - 1 && last_rows < KT ? ~0ull << last_rows : 0ull;
+      const int b = lb0 + t - n_kept;
+      const uint32_t lo = __builtin_amdgcn_readfirstlane(kept_bits[2 * b]);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane(kept_bits[2 * b + 1]);
+      uint64_t m = ((uint64_t)hi << 32) | lo;
+      if (b == n_lb_all - 1 && last_lrows < KT) m |= ~0ull << last_lrows;
+      return m;
+    };
+
+    // ---- products (this wave's 32 keys of a block; both query halves)
+    auto read_k1 = [&](auto kst_c, bf16x8 (&ka)[4], int s) {
+      const lds_u8* ks = (const lds_u8*)kbuf(kst_c);
+      ka[s] = as_bf16x8(*(const __attribute__((address_space(3))) u32x4*)(ks + koff[s]));
+    };
+    auto read_v = [&](auto vst_c, u32x4 (&va)[2][2]) {
+      const lds_u8* vs = (const lds_u8*)vbuf(vst_c);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vs + voff[db][0] + 2048 * m));
+          const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vs + voff[db][1] + 2048 * m));
+          const u32x2 w0 = __builtin_bit_cast(u32x2, t0), w1 = __builtin_bit_cast(u32x2, t1);
+          va[m][db] = u32x4{w0.x, w0.y, w1.x, w1.y};
+        }
+    };
+    f32x16 oacc[2][2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      oacc[0][0][i] = 0.f;
+      oacc[0][1][i] = 0.f;
+      oacc[1][0][i] = 0.f;
+      oacc[1][1][i] = 0.f;
+    }
+    auto qk_q = [&](const bf16x8 (&ka)[4], f32x16& sacc, int qh) {
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qop[qh][0], f32x16{}, 0, 0, 0);
+#pragma unroll
+      for (int s = 1; s < 4; ++s) sacc = mfma32(ka[s], qop[qh][s], sacc);
+    };
+    const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+    float l_run[2] = {0.f, 0.f};
+    float mc_run[2] = {-INFINITY, -INFINITY};
+    // register i holds key 32kh + 8(i/4) + 4hh + i%4 of the block
+    auto lanes_of = [&](uint32_t w, int i) -> uint64_t {
+      const int off = 8 * (i >> 2) + (i & 3);
+      const uint32_t lo = (uint32_t)(((int32_t)(w << (31 - off))) >> 31);
+      const uint32_t hi = (uint32_t)(((int32_t)(w << (27 - off))) >> 31);
+      return ((uint64_t)hi << 32) | lo;
+    };
+    auto apply_mask = [&](f32x16 (&sacc)[2], uint64_t colmask) {
+      const uint32_t w = (uint32_t)(colmask >> (32 * kh));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bool ex = __builtin_amdgcn_inverse_ballot_w64(lanes_of(w, i));
+        if (ex) {
+          sacc[0][i] = -INFINITY;
+          sacc[1][i] = -INFINITY;
+        }
+      }
+    };
+    auto add_col = [&](f32x16 (&sacc)[2], int col, float corr) {
+      const int lc = col - 32 * kh;
+      if (lc < 0 || lc >= 32) return;  // uniform
+      const uint32_t w = 1u << lc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (__builtin_amdgcn_inverse_ballot_w64(lanes_of(w, i))) {
+          sacc[0][i] += corr;
+          sacc[1][i] += corr;
+        }
+    };
+    auto prob_pair = [&](const f32x16& s, int i, float nm, float& l) -> uint32_t {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i], c, nm));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i + 1], c, nm));
+      const uint32_t w = pack_bf16x2(p0, p1);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, l, false);
+      return w;
+    };
+    // fallback: running maximum per query half with lazy rescale of l;
+    // returns whether any reference moved (alpha then scales O after the
+    // pending PV product)
+    auto online_ref = [&](const f32x16 (&sacc)[2], float (&nm)[2], float (&alpha)[2]) -> bool {
+      bool moved_any = false;
+      float tmc[2];
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh) {
+        float tm0 = sacc[qh][0], tm1 = sacc[qh][1];
+#pragma unroll
+        for (int i = 2; i < 16; i += 2) {
+          tm0 = __builtin_elementwise_maximum(tm0, sacc[qh][i]);
+          tm1 = __builtin_elementwise_maximum(tm1, sacc[qh][i + 1]);
+        }
+        float tmax = __builtin_elementwise_maximum(tm0, tm1);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax),
+                                                         __float_as_uint(tmax), false, false);
+        tmax = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        tmc[qh] = tmax * c;
+      }
+      if (__any(tmc[0] > mc_run[0] + kRescaleSlack || tmc[1] > mc_run[1] + kRescaleSlack)) {
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) {
+          const float m_new = __builtin_elementwise_maximum(mc_run[qh], tmc[qh]);
+          alpha[qh] = __builtin_amdgcn_exp2f(mc_run[qh] - m_new);
+          l_run[qh] *= alpha[qh];
+          mc_run[qh] = m_new;
+        }
+        moved_any = true;
+      }
+      // a key half can see only excluded columns so far (a short last block):
+      // any finite shift then gives them probability zero
+      nm[0] = mc_run[0] == -INFINITY ? 0.f : -mc_run[0];
+      nm[1] = mc_run[1] == -INFINITY ? 0.f : -mc_run[1];
+      return moved_any;
+    };
+
+    // S(t) of both query halves; P of the last two blocks by block parity,
+    // pb[qh][m] = keys 16m.. of this wave's half
+    f32x16 sacc[2];
+    bf16x8 pb0[2][2], pb1[2][2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) pb1[qh][m] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    auto pbuf = [&](auto par) -> bf16x8(&)[2][2] {
+      if constexpr (decltype(par)::value == 0) return pb0;
+      else return pb1;
+    };
+
+    auto run = [&](auto fast_c) {
+      constexpr bool kFast = decltype(fast_c)::value;
+      // One step: softmax of block t (both query halves, 16 pair jobs) with
+      // PV(t-1) (8 MFMAs), then QK(t+1) (8 MFMAs). The fast path fixes the
+      // order with scheduling fences: two jobs while the operand reads land,
+      // slots 1-8 PV(t-1) with one job each, slots 9-12 QK(t+1) of query
+      // half 0 with the last six jobs, slots 13-16 QK(t+1) of query half 1;
+      // the loads of K(t+2) and V(t) go out in slots 1-8.
+      auto body = [&](auto par, auto masked_c, uint64_t cmask, float nm_add, int tail_col,
+                      const Src& sk, const Src& sv) {
+        constexpr bool kMasked = decltype(masked_c)::value;
+        using R = std::integral_constant<int, 1 - decltype(par)::value>;
+        u32x4 va[2][2];
+        bf16x8 ka[4];
+        uint32_t w[2][8];
+        bf16x8(&pw)[2][2] = pbuf(par);
+        bf16x8(&pr)[2][2] = pbuf(R{});
+        read_v(R{}, va);  // V(t-1)
+        if constexpr (kMasked) {
+          if (tail_col >= 0) add_col(sacc, tail_col, p.lm_tail_corr);
+          apply_mask(sacc, cmask);
+        }
+        float nm[2] = {nm_fast[0], nm_fast[1]}, alpha[2] = {1.f, 1.f};
+        bool moved = false;
+        if constexpr (!kFast) moved = online_ref(sacc, nm, alpha);
+        if constexpr (kMasked) {
+          nm[0] += nm_add;
+          nm[1] += nm_add;
+        }
+        auto job = [&](int n) {
+          const int qh = n >> 3, i = n & 7;
+          w[qh][i] = prob_pair(sacc[qh], i, nm[qh], l_run[qh]);
+        };
+        job(0);
+        job(1);
+        if constexpr (kFast) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {  // slots 1-8: PV(t-1)
+          const int qh = j >> 2, m = (j >> 1) & 1, db = j & 1;
+          oacc[qh][db] = mfma32(as_bf16x8(va[m][db]), pr[qh][m], oacc[qh][db]);
+          job(2 + j);
+          if (j < 2) {
+            read_k1(R{}, ka, 2 * j);  // K(t+1); past the end a repeated block
+            read_k1(R{}, ka, 2 * j + 1);
+          }
+          constexpr int kPer = (2 * NU + 7) / 8;
+#pragma unroll
+          for (int k = 0; k < kPer; ++k) {
+            const int q = j * kPer + k;
+            if (q < NU)
+              fire(sk, kbuf(par), q);
+            else if (q < 2 * NU)
+              fire(sv, vbuf(par), q - NU);
+          }
+          if constexpr (kFast) __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (!kFast) {
+          if (moved) {
+#pragma unroll
+            for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+              for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[qh][db][i] *= alpha[qh];
+          }
+        }
+        pw[0][0] = as_bf16x8(u32x4{w[0][0], w[0][1], w[0][2], w[0][3]});
+        pw[0][1] = as_bf16x8(u32x4{w[0][4], w[0][5], w[0][6], w[0][7]});
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {  // slots 9-12: QK(t+1) of query half 0
+          sacc[0] = j == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qop[0][0], f32x16{},
+                                                                      0, 0, 0)
+                           : mfma32(ka[j], qop[0][j], sacc[0]);
+          job(10 + (j < 2 ? 2 * j : j + 2));
+          if (j < 2) job(11 + 2 * j);
+          if constexpr (kFast) __builtin_amdgcn_sched_barrier(0);
+        }
+        pw[1][0] = as_bf16x8(u32x4{w[1][0], w[1][1], w[1][2], w[1][3]});
+        pw[1][1] = as_bf16x8(u32x4{w[1][4], w[1][5], w[1][6], w[1][7]});
+        qk_q(ka, sacc[1], 1);  // slots 13-16
+        // P(t) and the row sums are complete within this step
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+          for (int m = 0; m < 2; ++m) keep_vgpr(__builtin_bit_cast(u32x4, pw[qh][m]));
+        keep_vgpr(l_run[0]);
+        keep_vgpr(l_run[1]);
+      };
+      auto step = [&](int t, auto par, auto masked_c) {
+        wait_vmcnt<0>();
+        lds_barrier();
+        const int tkn = min(t + 2, n_total - 1);
+        const int tvn = max(min(t, n_total - 1), 0);
+        ensure_window(tvn, tkn);
+        const Src sk = prep(tkn, khp, klm), sv = prep(tvn, vhp, vlm);
+        if (t < 0) {
+#pragma unroll
+          for (int v = 0; v < NU; ++v) fire(sk, kbuf(par), v);
+#pragma unroll
+          for (int v = 0; v < NU; ++v) fire(sv, vbuf(par), v);
+        }
+        if (t == -1) {
+          bf16x8 ka[4];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) read_k1(P0{}, ka, s);
+          qk_q(ka, sacc[0], 0);  // QK(0)
+          qk_q(ka, sacc[1], 1);
+        }
+        if (t < 0) return;
+        if constexpr (decltype(masked_c)::value) {
+          const bool lm = t >= n_kept;
+          const int tcol = lm && log_count && lb0 + t - n_kept == n_lb_all - 1 && tail_rows < KT
+                               ? last_lrows - 1
+                               : -1;
+          body(par, masked_c, block_mask(t), lm ? lm_shift : 0.f, tcol, sk, sv);
+        } else {
+          body(par, masked_c, 0ull, 0.f, -1, sk, sv);
+        }
+      };
+      auto drain = [&](auto par) {  // PV of the last block
+        wait_vmcnt<0>();
+        lds_barrier();
+        u32x4 va[2][2];
+        read_v(par, va);
+        bf16x8(&pr)[2][2] = pbuf(par);
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+              oacc[qh][db] = mfma32(as_bf16x8(va[m][db]), pr[qh][m], oacc[qh][db]);
+      };
+      using Plain = std::false_type;
+      using Masked = std::true_type;
+      const int n_plain = last_rows < KT ? n_kept - 1 : n_kept;
+      step(-2, P0{}, Plain{});
+      step(-1, P1{}, Plain{});
+      int t = 0;
+      for (; t + 2 <= n_plain; t += 2) {
+        step(t, P0{}, Plain{});
+        step(t + 1, P1{}, Plain{});
+      }
+      if (t < n_plain) step(t++, P0{}, Plain{});
+      if ((t & 1) && t < n_total) step(t++, P1{}, Masked{});
+      for (; t + 2 <= n_total; t += 2) {
+        step(t, P0{}, Masked{});
+        step(t + 1, P1{}, Masked{});
+      }
+      if (t < n_total) step(t, P0{}, Masked{});
+      if ((n_total - 1) & 1)
+        drain(P1{});
+      else
+        drain(P0{});
+    };
+    if (n_total > 0) {
+      if (fast)
+        run(std::true_type{});
+      else
+        run(std::false_type{});
+    }
+
+    // ---- merge the key halves. Row sums over the lane halves first.
+    float l_q[2], ref_q[2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run[qh]),
+                                                        __float_as_uint(l_run[qh]), false, false);
+      l_q[qh] = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
+      ref_q[qh] = fast ? -nm_fast[qh] : mc_run[qh];
+    }
+    // wave kh keeps query half kh and hands over query half 1 - kh: its
+    // partial output (lane-major f32x4 slots) and per-query (reference, sum)
+    lds_barrier();  // every wave is done with the rings
+    // (kh is uniform: both branches index the register arrays statically)
+    auto put = [&](const f32x16 (&og)[2], float r, float l) {
+      __attribute__((address_space(3))) f32x4* xb = xbuf(wave);
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          xb[(db * 4 + g) * 64 + lane] =
+              f32x4{og[db][4 * g], og[db][4 * g + 1], og[db][4 * g + 2], og[db][4 * g + 3]};
+      float2* xm = (float2*)win;  // 32 (reference, sum) pairs per wave
+      if (hh == 0) xm[wave * 32 + qi] = float2{r, l};
+    };
+    if (kh == 0)
+      put(oacc[1], ref_q[1], l_q[1]);
+    else
+      put(oacc[0], ref_q[0], l_q[0]);
+    __syncthreads();
+    const int keep = kh;
+    f32x16 o[2];
+    float l_sum, ref;
+    auto merge = [&](const f32x16 (&om)[2], float r_mine, float l_mine) {
+      const int partner = wave ^ 1;
+      const __attribute__((address_space(3))) f32x4* xb = xbuf(partner);
+      const float2 pm = ((const float2*)win)[partner * 32 + qi];
+      ref = __builtin_elementwise_maximum(r_mine, pm.x);
+      // a partial without columns (l = 0) carries no weight
+      const float a_mine = l_mine > 0.f ? __builtin_amdgcn_exp2f(r_mine - ref) : 0.f;
+      const float a_part = pm.y > 0.f ? __builtin_amdgcn_exp2f(pm.x - ref) : 0.f;
+      l_sum = l_mine * a_mine + pm.y * a_part;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 x = xb[(db * 4 + g) * 64 + lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            o[db][4 * g + r] = om[db][4 * g + r] * a_mine + x[r] * a_part;
+        }
+      if (l_sum == 0.f) ref = r_mine;  // no columns at all (split keys, no landmarks)
+    };
+    if (kh == 0)
+      merge(oacc[0], ref_q[0], l_q[0]);
+    else
+      merge(oacc[1], ref_q[1], l_q[1]);
+    const int64_t qrow = qbase + 32 * keep;
+    const bool qvalid = qrow < p.nq;
+    if (n_ch > 1) {  // split keys: unnormalised partial and (reference, row sum)
+      if (qvalid) {
+        const int64_t prow = ((int64_t)h * p.nq + qrow) * n_ch + ch;
+        float* op = p.part_o + prow * kHeadDim + 4 * hh;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *(f32x4*)(op + 32 * db + 8 * g) =
+                f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+        if (hh == 0) p.part_ml[prow] = float2{ref, l_sum};
+      }
+      continue;
+    }
+    if (p.lse != nullptr && qvalid && hh == 0)
+      p.lse[(int64_t)h * p.nq + qrow] = ref + __builtin_log2f(l_sum);
+    const float inv = 1.0f / l_sum;
+    if (qvalid) {
+      if (p.o_f32) {
+        float* op = (float*)p.o + (int64_t)h * p.osh + qrow * p.ost + 4 * hh;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *(f32x4*)(op + 32 * db + 8 * g) = f32x4{o[db][4 * g] * inv, o[db][4 * g + 1] * inv,
+                                                    o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
+      } else {
+        uint16_t* op = (uint16_t*)p.o + (int64_t)h * p.osh + qrow * p.ost + 4 * hh;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            u32x2 w = {pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                       pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
             *(u32x2*)(op + 32 * db + 8 * g) = w;
           }
       }
@@ -928,6 +1563,14 @@ template <int QT, int KT>
 hipError_t launch_kernel(const SparseParams& p, const int32_t* sel, hipStream_t s) {
   // one workgroup per item (the item loop serves the rest when the grid is capped)
   const int64_t grid = std::min<int64_t>(p.n_items, (int64_t)1 << 24);
+  // key-half kernel: 64-key tiles, 64 or 128 queries, 128-byte key rows
+  if constexpr (KT == 64 && QT >= 64) {
+    if (p.kst == kHeadDim) {
+      hipLaunchKernelGGL((tile_sparse_kh_kernel<QT>), dim3((unsigned)grid), dim3(QT * 2), 0, s,
+                         p, sel);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((tile_sparse_kernel<QT, KT>), dim3((unsigned)grid), dim3(QT * 2), 0, s, p,
                      sel);
   return hipGetLastError();
