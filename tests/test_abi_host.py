@@ -38,6 +38,17 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == set(zb.ENTRY_POINTS)
 
 
+def test_no_unresolved_library_symbols(lib):
+    """Every symbol of the library's own namespace is defined in it (a kernel
+    whose host launch stub was not emitted would only fail at load time on a
+    machine that binds eagerly)."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", zb.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    missing = [line.split()[-1] for line in out.splitlines() if "5zebra" in line]
+    assert not missing, missing
+
+
 def test_version_and_status_strings(lib):
     assert "gfx950" in zb.version()
     for s in range(5):
