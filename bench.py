@@ -101,7 +101,7 @@ def recorded_traffic(workload: str):
     if workload != "stack24-512v":
         return None
     root = os.path.dirname(os.path.abspath(__file__))
-    summary = os.path.join(root, "profiles", "tile_sparse_kernel_stack24-512v_hbm_bytes.md")
+    summary = os.path.join(root, "profiles", "tile_sparse_kh_kernel_stack24-512v_hbm_bytes.md")
     source = os.path.join(root, "linear_hybrid_attention_zebra_amd", "csrc", "sparse_attn.hip")
     try:
         text = open(summary).read()
@@ -434,7 +434,7 @@ def main():
     if "sparse_attn_ms" in res:
         sec = res["sparse_attn_ms"] * 1e-3
         achieved = res["selected_flops"] / sec / 1e12
-        out["roofline"] = {"kernel": "tile_sparse_kernel (timed as its whole zebra_tile_sparse_attn "
+        out["roofline"] = {"kernel": "tile_sparse_kh_kernel (timed as its whole zebra_tile_sparse_attn "
                                      "call: landmark packing, key ranges, chunk offsets, the kernel "
                                      "and the split-key combine)", "bound": "mfma",
                            "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

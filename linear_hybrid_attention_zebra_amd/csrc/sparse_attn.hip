@@ -895,9 +895,14 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     else return (lds_blk*)vs1;
   };
   // end-of-item exchange: wave w's 8 KB of partial output in ring block w
+  // (the lane's slot address is formed where it is used: an empty asm hides
+  // the uniform base from loop-invariant code motion, which would otherwise
+  // keep one address per slot live across the item loop)
   auto xbuf = [&](int w) -> __attribute__((address_space(3))) f32x4* {
     u32x4* b = w == 0 ? &ks0[0][0] : (w == 1 ? &ks1[0][0] : (w == 2 ? &vs0[0][0] : &vs1[0][0]));
-    return (__attribute__((address_space(3))) f32x4*)b;
+    uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) u32x4*)b;
+    asm volatile("" : "+s"(a));
+    return (__attribute__((address_space(3))) f32x4*)(uintptr_t)a;
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
@@ -949,6 +954,14 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
   for (int v = 0; v < NU; ++v) off_v[v] = (uint32_t)((r_lane + 8 * W * v) * 128 + lchunk * 16);
 
   for (int64_t item = blockIdx.x; item < p.n_items; item += gridDim.x) {
+    // per-item copies of the argument pointers that lane addresses are formed
+    // from: hidden from loop-invariant code motion, which would hoist one
+    // 64-bit address per lane out of the item loop and spill it
+    const uint16_t* q_arg = p.q;
+    const float* range_arg = p.range;
+    void* o_arg = p.o;
+    float* part_o_arg = p.part_o;
+    asm volatile("" : "+s"(q_arg), "+s"(range_arg), "+s"(o_arg), "+s"(part_o_arg));
     const int h = (int)(item / items_per_head);
     const int64_t rem = item - (int64_t)h * items_per_head;
     const int ch = (int)(rem / p.tq);
@@ -989,7 +1002,7 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
       const int64_t qr = qbase + 32 * qh;
-      const uint16_t* qp = p.q + (int64_t)h * p.qsh + qr * p.qst + 8 * hh;
+      const uint16_t* qp = q_arg + (int64_t)h * p.qsh + qr * p.qst + 8 * hh;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         u32x4 w = {0u, 0u, 0u, 0u};
@@ -998,8 +1011,8 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         qq[qh] += sum8_sq(w);
       }
     }
-    float k2 = p.range[((int64_t)h * kRangeParts + lane) * 2];
-    float vmax = p.range[((int64_t)h * kRangeParts + lane) * 2 + 1];
+    float k2 = range_arg[((int64_t)h * kRangeParts + lane) * 2];
+    float vmax = range_arg[((int64_t)h * kRangeParts + lane) * 2 + 1];
     const int last_kept =
         dense ? p.tk - 1 : (n_kept > 0 ? min(max(sel_row[n_kept - 1], 0), p.tk - 1) : -1);
     __syncthreads();
@@ -1378,18 +1391,16 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     else
       put(oacc[0], ref_q[0], l_q[0]);
     __syncthreads();
-    const int keep = kh;
-    f32x16 o[2];
-    float l_sum, ref;
-    auto merge = [&](const f32x16 (&om)[2], float r_mine, float l_mine) {
+    // merge into the kept half's accumulators and write the query half kh
+    auto finish = [&](f32x16 (&om)[2], float r_mine, float l_mine) {
       const int partner = wave ^ 1;
       const __attribute__((address_space(3))) f32x4* xb = xbuf(partner);
       const float2 pm = ((const float2*)win)[partner * 32 + qi];
-      ref = __builtin_elementwise_maximum(r_mine, pm.x);
+      float ref = __builtin_elementwise_maximum(r_mine, pm.x);
       // a partial without columns (l = 0) carries no weight
       const float a_mine = l_mine > 0.f ? __builtin_amdgcn_exp2f(r_mine - ref) : 0.f;
       const float a_part = pm.y > 0.f ? __builtin_amdgcn_exp2f(pm.x - ref) : 0.f;
-      l_sum = l_mine * a_mine + pm.y * a_part;
+      const float l_sum = l_mine * a_mine + pm.y * a_part;
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -1397,54 +1408,51 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
           const f32x4 x = xb[(db * 4 + g) * 64 + lane];
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            o[db][4 * g + r] = om[db][4 * g + r] * a_mine + x[r] * a_part;
+            om[db][4 * g + r] = om[db][4 * g + r] * a_mine + x[r] * a_part;
         }
       if (l_sum == 0.f) ref = r_mine;  // no columns at all (split keys, no landmarks)
-    };
-    if (kh == 0)
-      merge(oacc[0], ref_q[0], l_q[0]);
-    else
-      merge(oacc[1], ref_q[1], l_q[1]);
-    const int64_t qrow = qbase + 32 * keep;
-    const bool qvalid = qrow < p.nq;
-    if (n_ch > 1) {  // split keys: unnormalised partial and (reference, row sum)
-      if (qvalid) {
+      const int64_t qrow = qbase + 32 * kh;
+      if (qrow >= p.nq) return;
+      if (n_ch > 1) {  // split keys: unnormalised partial and (reference, row sum)
         const int64_t prow = ((int64_t)h * p.nq + qrow) * n_ch + ch;
-        float* op = p.part_o + prow * kHeadDim + 4 * hh;
+        float* op = part_o_arg + prow * kHeadDim + 4 * hh;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
           for (int g = 0; g < 4; ++g)
             *(f32x4*)(op + 32 * db + 8 * g) =
-                f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+                f32x4{om[db][4 * g], om[db][4 * g + 1], om[db][4 * g + 2], om[db][4 * g + 3]};
         if (hh == 0) p.part_ml[prow] = float2{ref, l_sum};
+        return;
       }
-      continue;
-    }
-    if (p.lse != nullptr && qvalid && hh == 0)
-      p.lse[(int64_t)h * p.nq + qrow] = ref + __builtin_log2f(l_sum);
-    const float inv = 1.0f / l_sum;
-    if (qvalid) {
+      if (p.lse != nullptr && hh == 0)
+        p.lse[(int64_t)h * p.nq + qrow] = ref + __builtin_log2f(l_sum);
+      const float inv = 1.0f / l_sum;
       if (p.o_f32) {
-        float* op = (float*)p.o + (int64_t)h * p.osh + qrow * p.ost + 4 * hh;
+        float* op = (float*)o_arg + (int64_t)h * p.osh + qrow * p.ost + 4 * hh;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
           for (int g = 0; g < 4; ++g)
-            *(f32x4*)(op + 32 * db + 8 * g) = f32x4{o[db][4 * g] * inv, o[db][4 * g + 1] * inv,
-                                                    o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
+            *(f32x4*)(op + 32 * db + 8 * g) =
+                f32x4{om[db][4 * g] * inv, om[db][4 * g + 1] * inv, om[db][4 * g + 2] * inv,
+                      om[db][4 * g + 3] * inv};
       } else {
-        uint16_t* op = (uint16_t*)p.o + (int64_t)h * p.osh + qrow * p.ost + 4 * hh;
+        uint16_t* op = (uint16_t*)o_arg + (int64_t)h * p.osh + qrow * p.ost + 4 * hh;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            u32x2 w = {pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
-                       pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+            u32x2 w = {pack_bf16x2(om[db][4 * g] * inv, om[db][4 * g + 1] * inv),
+                       pack_bf16x2(om[db][4 * g + 2] * inv, om[db][4 * g + 3] * inv)};
             *(u32x2*)(op + 32 * db + 8 * g) = w;
           }
       }
-    }
+    };
+    if (kh == 0)
+      finish(oacc[0], ref_q[0], l_q[0]);
+    else
+      finish(oacc[1], ref_q[1], l_q[1]);
   }
 }
 
