@@ -102,8 +102,11 @@ class Calibration:
 
 
 def calibrate_linear(q, k, v, sample_index: torch.Tensor, scale: float, k_tile: int = 64,
-                     q_tile: int = 64) -> Calibration:
-    """Fit a, b of one linear stage against dense softmax attention at the sampled queries."""
+                     q_tile: int = 128) -> Calibration:
+    """Fit a, b of one linear stage against dense softmax attention at the sampled queries.
+
+    The dense target runs in 128-query tiles (tiling does not change dense
+    attention; four waves then share each staged key/value block)."""
     qs = q.index_select(1, sample_index).contiguous()
     t_k = ceil_div(k.shape[1], k_tile)
     y = zebra_tile_sparse_attn(qs, k, v, None, None, None, q_tile, k_tile, t_k, scale,

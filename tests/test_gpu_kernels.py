@@ -216,18 +216,26 @@ def test_sparse_both_softmax_references(kind):
     assert_close(to_f64(out) / v_scale, ref / v_scale, f"reference paths {kind}")
 
 
-def test_sparse_strided_layout():
+# (q_tile, n, top_k): key rows 192 bytes apart take the 32-query layout for
+# every tile shape, including split keys (n >= 2 x 32,768)
+STRIDED_CASES = [(64, 250, 2), (128, 300, 2), (64, 65536 + 100, 40)]
+
+
+@pytest.mark.parametrize("q_tile,n,top_k", STRIDED_CASES, ids=[str(c) for c in STRIDED_CASES])
+def test_sparse_strided_layout(q_tile, n, top_k):
     """Token-major [N][H][64] storage for q, k, v and the output."""
-    q, k, v = _clustered(9, 3, 250, 250, 64, 64, 2)
+    print(f"[case] strided sparse q_tile={q_tile} N={n} top_k={top_k}", flush=True)
+    nq = 250 if n > 1000 else n
+    q, k, v = _clustered(9, 3, nq, n, q_tile, 64, 2)
     tm = lambda x: bf16_gpu(x).permute(1, 0, 2).contiguous().permute(1, 0, 2)
     qg, kg, vg = tm(q), tm(k), tm(v)
-    out = torch.empty((250, 3, 64), dtype=torch.bfloat16, device=DEV).permute(1, 0, 2)
-    bufs = stage.SparseBuffers.allocate(3, 250, 250, 64, 64, 2, DEV)
+    out = torch.empty((nq, 3, 64), dtype=torch.bfloat16, device=DEV).permute(1, 0, 2)
+    bufs = stage.SparseBuffers.allocate(3, nq, n, q_tile, 64, top_k, DEV)
     bufs.out = out
-    stage.sparse_stage(qg, kg, vg, 64, 64, 2, 0.125, bufs)
+    stage.sparse_stage(qg, kg, vg, q_tile, 64, top_k, 0.125, bufs)
     torch.cuda.synchronize()
     sel = bufs.sel.cpu().numpy()
-    ref, _ = zo.tile_sparse_attention(q, k, v, 64, 64, 2, 0.125, sel=sel)
+    ref, _ = zo.tile_sparse_attention(q, k, v, q_tile, 64, top_k, 0.125, sel=sel)
     assert_close(out, ref, "strided sparse")
 
 
