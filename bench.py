@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB three times (the "
                         "reference kernel that scales the HBM byte counters) and exit")
+    p.add_argument("--peak-probe", action="store_true",
+                   help="only measure the achievable peaks the rooflines are read against: a "
+                        "large bf16 GEMM (torch.matmul) and a 4 GiB device copy, and exit")
     p.add_argument("--selection-quality", action="store_true",
                    help="only measure how much dense attention mass the pooled-score selection "
                         "keeps, against the top-k blocks by mass, on the workload's first sparse "
@@ -69,6 +72,36 @@ def copy_probe(mib: int):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+
+
+def peak_probe():
+    """Achievable bf16 MFMA rate (an 8192^3 GEMM through the vendor library) and
+    achievable HBM rate (a 4 GiB copy reads and writes 8 GiB), median of 10."""
+    import torch
+    n = 8192
+    a = torch.randn((n, n), device="cuda").bfloat16()
+    b = torch.randn((n, n), device="cuda").bfloat16()
+    src = torch.empty(4 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+
+    def med_ms(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    gemm_ms = med_ms(lambda: torch.matmul(a, b))
+    copy_ms = med_ms(lambda: dst.copy_(src))
+    print(json.dumps({"gemm_bf16_tflops": 2.0 * n ** 3 / (gemm_ms * 1e-3) / 1e12,
+                      "copy_gbs": 2.0 * src.numel() / (copy_ms * 1e-3) / 1e9,
+                      "gemm_ms": gemm_ms, "copy_ms": copy_ms}), flush=True)
 
 
 # ----------------------------------------------------------------------------
@@ -383,6 +416,9 @@ def main():
     args = parse()
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.peak_probe:
+        peak_probe()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path "
