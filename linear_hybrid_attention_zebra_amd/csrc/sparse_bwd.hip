@@ -146,6 +146,21 @@ struct BwdParams {
   float* dq_acc;           // [H][nq][64] float32 dq accumulator (dq sweep 1)
 };
 
+// The lanes of a 32x32 C-layout block whose row (key) is set in a uniform
+// 32-bit column mask, for the register whose rows are off + 4 hh (hh = lane
+// half): a 64-bit lane mask of two sign-extended bits, built with scalar ops.
+__device__ __forceinline__ uint64_t half_lanes(uint32_t w, int off) {
+  const uint32_t lo = (uint32_t)(((int32_t)(w << (31 - off))) >> 31);
+  const uint32_t hi = (uint32_t)(((int32_t)(w << (27 - off))) >> 31);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// 16 bytes per lane global -> LDS directly (the lane's bytes land at
+// dst + 16 lane)
+__device__ __forceinline__ void g2l16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
 // first index in [lo, hi) of the ascending array a with a[i] >= x
 __device__ __forceinline__ int lower_bound_i32(const int32_t* a, int lo, int hi, int x) {
   while (lo < hi) {
@@ -464,13 +479,16 @@ __global__ __launch_bounds__(KT * 2) void bwd_dkdv_kernel(BwdParams p) {
 // 5. dq: one workgroup per (head, query tile); wave w owns 32 queries
 // ---------------------------------------------------------------------------
 template <int QT, int KT, bool kGrad>
-__global__ __launch_bounds__(QT * 2) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(BwdParams p) {
   constexpr int W = QT / 32;
-  constexpr int NT = W * kWave;
   constexpr int NB = KT / 32;
-  __shared__ u32x4 ks_t[KT * 8], vs_t[KT * 8];
-  const lds_u8* ktile = (const lds_u8*)ks_t;
-  const lds_u8* vtile = (const lds_u8*)vs_t;
+  constexpr int KB = KT * 128 / 1024;  // 1 KB pieces per K (or V) block
+  constexpr int NU = KB / W;           // pieces per wave per tensor
+  static_assert(KB % W == 0, "load split");
+  // Two-stage rings, loaded global -> LDS directly one block ahead. Distinct
+  // arrays indexed with compile-time stage numbers let the compiler tell the
+  // stage being read from the stage being loaded.
+  __shared__ u32x4 ks0[KT * 8], vs0[KT * 8], ks1[KT * 8], vs1[KT * 8];
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int qi = lane & 31, hh = lane >> 5;
@@ -478,6 +496,12 @@ __global__ __launch_bounds__(QT * 2) void bwd_dq_kernel(BwdParams p) {
   const int n_lb_all = p.landmarks ? (p.tk + KT - 1) / KT : 0;
   const int tail_rows = (int)(p.nk - (int64_t)(p.tk - 1) * KT);
   const int last_lrows = p.tk - (n_lb_all - 1) * KT;
+  // piece v of a block: rows 8 (wave + W v) + lane / 8; the lane writes
+  // physical chunk lane % 8, i.e. logical chunk (lane % 8) ^ swz_f(row) of
+  // the row (the swizzled layout the operand reads expect)
+  const int lrow = lane >> 3;
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
   for (int64_t item = blockIdx.x; item < (int64_t)p.heads * p.tq; item += gridDim.x) {
     const int h = (int)(item / p.tq);
     const int qt = (int)(item - (int64_t)h * p.tq);
@@ -513,52 +537,79 @@ __global__ __launch_bounds__(QT * 2) void bwd_dq_kernel(BwdParams p) {
     const int n_kept = t1 - t0;
     const int n_total = n_kept + max(lb1 - lb0, 0);
     const uint32_t* brow = p.bits + row * p.bit_words;
+    // block t of the list: kept key tile (ascending) or landmark block
+    struct Blk {
+      const uint16_t* kbase;
+      const uint16_t* vbase;
+      int64_t stride;
+      int rows;
+      bool lm;
+      int b;  // landmark block index
+    };
+    auto blk = [&](int t) -> Blk {
+      Blk r;
+      r.lm = t >= n_kept;
+      if (!r.lm) {
+        const int j = min(max(sel_row[t0 + t], 0), p.tk - 1);
+        r.kbase = p.k + (int64_t)h * p.ksh + (int64_t)j * KT * p.kst;
+        r.vbase = p.v + (int64_t)h * p.ksh + (int64_t)j * KT * p.kst;
+        r.stride = p.kst;
+        r.rows = j == p.tk - 1 ? tail_rows : KT;
+        r.b = 0;
+      } else {
+        r.b = lb0 + t - n_kept;
+        r.kbase = p.kbar_b + ((int64_t)h * p.tk + (int64_t)r.b * KT) * kHeadDim;
+        r.vbase = p.vbar_b + ((int64_t)h * p.tk + (int64_t)r.b * KT) * kHeadDim;
+        r.stride = kHeadDim;
+        r.rows = r.b == n_lb_all - 1 ? last_lrows : KT;
+      }
+      return r;
+    };
+    // stage block t (rows past the end repeat the last one; they are masked)
+    auto issue = [&](int t, auto stc) {
+      const Blk bk = blk(t);
+      u32x4* kd = decltype(stc)::value == 0 ? ks0 : ks1;
+      u32x4* vd = decltype(stc)::value == 0 ? vs0 : vs1;
+#pragma unroll
+      for (int v = 0; v < NU; ++v) {
+        const int u = wave + W * v;
+        const int r = 8 * u + lrow;
+        const int rr = min(r, bk.rows - 1);
+        const int64_t e = (int64_t)rr * bk.stride + 8 * ((lane & 7) ^ swz_f(r));
+        g2l16(bk.kbase + e, &kd[64 * u]);
+        g2l16(bk.vbase + e, &vd[64 * u]);
+      }
+    };
     // sweep 0: sum_c P'_c and sum_c P'_c dP_c with P' = 2^(x - lse) in
     // float32. The forward's normaliser sums bf16-rounded probabilities, so P'
     // sums to 1 + O(2^-9); renormalising lse by that sum makes P sum to one in
     // float32, and D = sum P dP then matches dP exactly (dP - D cancels, which
     // would amplify any mismatch). sweep 1: dS and dq.
     float dpart = 0.f, lpart = 0.f;
-    for (int t = 0; t < n_total; ++t) {
-      const bool lm = t >= n_kept;
-      const uint16_t* kbase;
-      const uint16_t* vbase;
-      int64_t stride;
-      int rows;
+    auto step = [&](int t, auto stc) {
+      __syncthreads();  // block t has landed for every wave; the other stage is free
+      if (t + 1 < n_total) {
+        if constexpr (decltype(stc)::value == 0)
+          issue(t + 1, S1{});
+        else
+          issue(t + 1, S0{});
+      }
+      const lds_u8* ktile = (const lds_u8*)(decltype(stc)::value == 0 ? ks0 : ks1);
+      const lds_u8* vtile = (const lds_u8*)(decltype(stc)::value == 0 ? vs0 : vs1);
+      const Blk bk = blk(t);
       uint64_t cmask = 0ull;  // excluded columns (bit set)
       float bias = 0.f;       // log2 units
       int tail_col = -1;
-      if (!lm) {
-        const int j = min(max(sel_row[t0 + t], 0), p.tk - 1);
-        kbase = p.k + (int64_t)h * p.ksh + (int64_t)j * KT * p.kst;
-        vbase = p.v + (int64_t)h * p.ksh + (int64_t)j * KT * p.kst;
-        stride = p.kst;
-        rows = j == p.tk - 1 ? tail_rows : KT;
-      } else {
-        const int b = lb0 + t - n_kept;
-        kbase = p.kbar_b + ((int64_t)h * p.tk + (int64_t)b * KT) * kHeadDim;
-        vbase = p.vbar_b + ((int64_t)h * p.tk + (int64_t)b * KT) * kHeadDim;
-        stride = kHeadDim;
-        rows = b == n_lb_all - 1 ? last_lrows : KT;
-        const uint32_t lo = brow[NB * b];
-        const uint32_t hi = KT == 64 && 2 * b + 1 < p.bit_words ? brow[2 * b + 1] : 0u;
+      if (bk.lm) {
+        const uint32_t lo = brow[NB * bk.b];
+        const uint32_t hi = KT == 64 && 2 * bk.b + 1 < p.bit_words ? brow[2 * bk.b + 1] : 0u;
         cmask = ((uint64_t)hi << 32) | lo;
         if (p.log_count) {
           bias = p.lm_log2_kt;
-          if (b == n_lb_all - 1 && tail_rows < KT) tail_col = last_lrows - 1;
+          if (bk.b == n_lb_all - 1 && tail_rows < KT) tail_col = last_lrows - 1;
         }
       }
-      if (rows < KT) cmask |= ~0ull << rows;
-      __syncthreads();  // previous block consumed
-      for (int e = tid; e < KT * 8; e += NT) {
-        const int r = e >> 3, c8 = e & 7;
-        const int rr = min(r, rows - 1);  // rows past the end repeat the last one (masked)
-        const u32x4 a = *(const u32x4*)(kbase + (int64_t)rr * stride + 8 * c8);
-        const u32x4 b = *(const u32x4*)(vbase + (int64_t)rr * stride + 8 * c8);
-        *(__attribute__((address_space(3))) u32x4*)(ktile + swz(r, c8)) = a;
-        *(__attribute__((address_space(3))) u32x4*)(vtile + swz(r, c8)) = b;
-      }
-      __syncthreads();
+      if (bk.rows < KT) cmask |= ~0ull << bk.rows;
       // S^T = K Q^T, dP^T = V dout^T: lane = query, register = key
       // 32 b + 8 (v / 4) + 4 hh + v % 4
 #pragma unroll
@@ -576,14 +627,27 @@ __global__ __launch_bounds__(QT * 2) void bwd_dq_kernel(BwdParams p) {
             pacc = mfma32(av, dop[s], pacc);
           }
         }
+        // excluded columns (landmark blocks, a short last tile) as -inf
+        // scores and the short last landmark's correction, with uniform lane
+        // masks (register v holds key 32 b + 8 (v / 4) + 4 hh + v % 4); the
+        // other blocks skip both
+        if (cmask != 0ull || tail_col >= 0) {
+          const uint32_t w = (uint32_t)(cmask >> (32 * b));
+          const uint32_t tw =
+              tail_col >= 32 * b && tail_col < 32 * b + 32 ? 1u << (tail_col - 32 * b) : 0u;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int off = 8 * (v >> 2) + (v & 3);
+            if (__builtin_amdgcn_inverse_ballot_w64(half_lanes(tw, off)))
+              sacc[v] += p.lm_tail_corr;
+            if (__builtin_amdgcn_inverse_ballot_w64(half_lanes(w, off))) sacc[v] = -INFINITY;
+          }
+        }
+        const float nb = bias - lse;
         float dsr[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int key = 32 * b + 8 * (v >> 2) + 4 * hh + (v & 3);
-          float x = __builtin_fmaf(sacc[v], p.c, bias);
-          if (key == tail_col) x += p.lm_tail_corr * p.c;
-          const bool off = (cmask >> key) & 1ull;
-          const float pv = off ? 0.f : __builtin_amdgcn_exp2f(x - lse);
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], p.c, nb));
           if constexpr (kGrad) {
             dsr[v] = pv * (pacc[v] - dsum);
           } else {
@@ -606,7 +670,15 @@ __global__ __launch_bounds__(QT * 2) void bwd_dq_kernel(BwdParams p) {
           }
         }
       }
+    };
+    __syncthreads();  // every wave is done with the previous item's rings
+    if (n_total > 0) issue(0, S0{});
+    int t = 0;
+    for (; t + 2 <= n_total; t += 2) {
+      step(t, S0{});
+      step(t + 1, S1{});
     }
+    if (t < n_total) step(t, S0{});
     if constexpr (!kGrad) {  // add this launch's sums over both lane halves
       const auto sd = __builtin_amdgcn_permlane32_swap(__float_as_uint(dpart),
                                                        __float_as_uint(dpart), false, false);
