@@ -116,6 +116,7 @@ struct BwdParams {
   const uint16_t* vbar_b;
   const int32_t* sel;      // [H][tq][top_k]
   const void* dout;
+  const uint16_t* dout_b;  // dout packed as bf16 [H][nq][64]
   void* dq;
   void* dk;
   void* dv;
@@ -161,6 +162,11 @@ __device__ __forceinline__ void g2l16(const void* src, void* dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 }
 
+// 4 bytes per lane global -> LDS directly (the lane's word lands at dst + 4 lane)
+__device__ __forceinline__ void g2l4(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+}
+
 // first index in [lo, hi) of the ascending array a with a[i] >= x
 __device__ __forceinline__ int lower_bound_i32(const int32_t* a, int lo, int hi, int x) {
   while (lo < hi) {
@@ -177,6 +183,20 @@ __device__ __forceinline__ int lower_bound_i32(const int32_t* a, int lo, int hi,
 __global__ __launch_bounds__(256) void bwd_fill_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256)
     p[e] = 0u;
+}
+
+// dout (bf16 or float32, any token/head strides) -> packed bf16 [H][nq][64],
+// 8 channels per thread; the dk, dv kernels stage it global -> LDS directly
+__global__ __launch_bounds__(256) void bwd_pack_dout_kernel(const void* __restrict__ dout,
+                                                            int64_t dst, int64_t dsh, int32_t f32,
+                                                            int64_t nq, int64_t n_pieces,
+                                                            uint16_t* __restrict__ out) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n_pieces;
+       e += (int64_t)gridDim.x * 256) {
+    const int64_t rowi = e >> 3, c8 = e & 7;
+    const int64_t h = rowi / nq, q = rowi - h * nq;
+    *(u32x4*)(out + rowi * kHeadDim + 8 * c8) = load8_bf16(dout, h * dsh + q * dst + 8 * c8, f32 != 0);
+  }
 }
 
 __global__ __launch_bounds__(256) void bwd_bits_kernel(const int32_t* __restrict__ sel,
@@ -275,7 +295,264 @@ __global__ __launch_bounds__(64) void bwd_list_kernel(const uint32_t* __restrict
 // 3-4. dk, dv: one workgroup per (head, column block); wave w owns 32 columns
 // ---------------------------------------------------------------------------
 template <int QT, int KT, bool LM>
-__global__ __launch_bounds__(KT * 2) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(KT * 2) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int W = KT / 32;
+  constexpr int QC = QT / 32;  // 32-query chunks per query tile
+  constexpr int KB = QT * 128 / 1024;  // 1 KB pieces per Q (or dout) tile
+  constexpr int NU = KB / W;           // pieces per wave per tensor
+  static_assert(KB % W == 0, "load split");
+  // Two-stage rings of the query side (Q, dout, lse, D), loaded global -> LDS
+  // directly one query tile ahead; distinct arrays per stage (see the dq kernel).
+  __shared__ u32x4 qs0[QT * 8], ds0[QT * 8], qs1[QT * 8], ds1[QT * 8];
+  __shared__ float lse0[QT], dsm0[QT], lse1[QT], dsm1[QT];
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int hh = lane >> 5, kl = lane & 31;
+  const int n_blocks = LM ? (p.tk + KT - 1) / KT : p.tk;
+  const int h = blockIdx.y;
+  const int lrow = lane >> 3;
+  const bool gf = p.g_f32 != 0;
+  for (int cb = blockIdx.x; cb < n_blocks; cb += gridDim.x) {
+    // this lane's column (key token or landmark row) and its validity
+    const int col = KT * cb + 32 * wave + kl;
+    int rows_valid;  // valid columns of the block
+    const uint16_t* kb;
+    const uint16_t* vb;
+    int64_t kstride;
+    if constexpr (LM) {
+      rows_valid = min(KT, p.tk - KT * cb);
+      kb = p.kbar_b + (int64_t)h * p.tk * kHeadDim;
+      vb = p.vbar_b + (int64_t)h * p.tk * kHeadDim;
+      kstride = kHeadDim;
+    } else {
+      rows_valid = (int)min<int64_t>(KT, p.nk - (int64_t)KT * cb);
+      kb = p.k + (int64_t)h * p.ksh;
+      vb = p.v + (int64_t)h * p.ksh;
+      kstride = p.kst;
+    }
+    const int lcol = 32 * wave + kl;  // column within the block
+    const bool cvalid = lcol < rows_valid;
+    // B operands K^T and V^T of this lane's column: channels 16 s + 8 hh .. +7
+    bf16x8 kop[4], vop[4];
+    {
+      const int64_t row = (int64_t)KT * cb + (cvalid ? lcol : 0);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+        if (cvalid) {
+          a = *(const u32x4*)(kb + row * kstride + 16 * s + 8 * hh);
+          b = *(const u32x4*)(vb + row * kstride + 16 * s + 8 * hh);
+        }
+        kop[s] = as_bf16x8(a);
+        vop[s] = as_bf16x8(b);
+      }
+    }
+    // logit bias of the column in log2 units (landmarks under the log count)
+    float bias = 0.f;
+    if constexpr (LM) {
+      if (p.log_count) {
+        bias = p.lm_log2_kt;
+        const int64_t tail = p.nk - (int64_t)(p.tk - 1) * KT;
+        if (col == p.tk - 1 && tail < KT) bias += p.lm_tail_corr * p.c;
+      }
+    }
+    f32x16 dkacc[2], dvacc[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dkacc[0][i] = 0.f;
+      dkacc[1][i] = 0.f;
+      dvacc[0][i] = 0.f;
+      dvacc[1][i] = 0.f;
+    }
+    int n_i, i_base;
+    if constexpr (LM) {
+      n_i = p.q_hi - p.q_lo;
+      i_base = p.q_lo;
+    } else {  // the part of the (ascending) list inside [q_lo, q_hi)
+      const int32_t* oh = p.list_off + (int64_t)h * (p.tk + 1);
+      const int b0 = oh[cb], b1 = oh[cb + 1];
+      i_base = lower_bound_i32(p.list, b0, b1, p.q_lo);
+      n_i = lower_bound_i32(p.list, i_base, b1, p.q_hi) - i_base;
+    }
+    if (n_i == 0 && !p.first && !p.last) continue;  // nothing to add in this launch
+    // query tile of list entry ii (a selection with repeated entries would
+    // leave list slots unwritten)
+    auto qtile_of = [&](int ii) -> int {
+      return LM ? i_base + ii : min(max(p.list[i_base + ii], 0), p.tq - 1);
+    };
+    // stage query tile qt: rows past nq repeat the last row (masked below)
+    auto issue = [&](int qt, auto stc) {
+      constexpr bool kS1 = decltype(stc)::value == 1;
+      u32x4* qd = kS1 ? qs1 : qs0;
+      u32x4* dd = kS1 ? ds1 : ds0;
+      const int64_t last = p.nq - 1;
+#pragma unroll
+      for (int v = 0; v < NU; ++v) {
+        const int u = wave + W * v;
+        const int r = 8 * u + lrow;
+        const int64_t qr = min((int64_t)qt * QT + r, last);
+        const int c = (lane & 7) ^ swz_f(r);
+        g2l16(p.q + (int64_t)h * p.qsh + qr * p.qst + 8 * c, &qd[64 * u]);
+        g2l16(p.dout_b + ((int64_t)h * p.nq + qr) * kHeadDim + 8 * c, &dd[64 * u]);
+      }
+      // lse and D of the tile's rows, 4 bytes per lane in pieces of 64 rows:
+      // piece j holds rows 64 (j / 2).. of lse (j even) or D (j odd)
+      constexpr int NL = QT >= 64 ? QT / 64 : 1;
+#pragma unroll
+      for (int j = wave; j < 2 * NL; j += W) {
+        const int r = 64 * (j >> 1) + lane;
+        if (r < QT) {
+          const int64_t qr = min((int64_t)qt * QT + r, last);
+          const float* src = ((j & 1) ? p.dsum : p.lse) + (int64_t)h * p.nq + qr;
+          float* dst = (j & 1) ? (kS1 ? dsm1 : dsm0) : (kS1 ? lse1 : lse0);
+          g2l4(src, dst + 64 * (j >> 1));
+        }
+      }
+    };
+    auto step = [&](int ii, auto stc) {
+      constexpr bool kS1 = decltype(stc)::value == 1;
+      __syncthreads();  // tile ii has landed for every wave; the other stage is free
+      if (ii + 1 < n_i) {
+        if constexpr (kS1)
+          issue(qtile_of(ii + 1), S0{});
+        else
+          issue(qtile_of(ii + 1), S1{});
+      }
+      __builtin_amdgcn_sched_barrier(0);  // (keeps the load addressing out of the products)
+      const lds_u8* qtile = (const lds_u8*)(kS1 ? qs1 : qs0);
+      const lds_u8* dtile = (const lds_u8*)(kS1 ? ds1 : ds0);
+      const float* lse_s = kS1 ? lse1 : lse0;
+      const float* dsum_s = kS1 ? dsm1 : dsm0;
+      const int qt = qtile_of(ii);
+      // rows of the tile past nq (only the last query tile): excluded
+      const int64_t vr = p.nq - (int64_t)qt * QT;
+      // kept mask of this lane's landmark column for query tile qt
+      bool masked = !cvalid;
+      if constexpr (LM) {
+        const int wi = (KT * cb + 32 * wave) / 32;  // the word of this wave's 32 columns
+        const uint32_t word =
+            wi < p.bit_words ? p.bits[((int64_t)h * p.tq + qt) * p.bit_words + wi] : 0u;
+        masked = masked || ((word >> kl) & 1u);
+      }
+#pragma unroll
+      for (int qc = 0; qc < QC; ++qc) {
+        // S = Q K^T and dP = dout V^T for 32 queries x this wave's 32 columns:
+        // lane = column, register v = query 32 qc + 8 (v / 4) + 4 hh + v % 4
+        f32x16 sacc, pacc;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 aq = row_operand(qtile, 32 * qc + kl, s, hh);
+          const bf16x8 ad = row_operand(dtile, 32 * qc + kl, s, hh);
+          if (s == 0) {
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kop[0], f32x16{}, 0, 0, 0);
+            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vop[0], f32x16{}, 0, 0, 0);
+          } else {
+            sacc = mfma32(aq, kop[s], sacc);
+            pacc = mfma32(ad, vop[s], pacc);
+          }
+        }
+        // excluded query rows of this chunk as -inf scores
+        const int64_t vq = vr - 32 * qc;  // valid rows of the chunk
+        const uint32_t w = vq >= 32 ? 0u : (vq <= 0 ? ~0u : ~0u << vq);
+        if (w != 0u) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (__builtin_amdgcn_inverse_ballot_w64(half_lanes(w, 8 * (v >> 2) + (v & 3))))
+              sacc[v] = -INFINITY;
+        }
+        float pr[16], dsr[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int q0 = 32 * qc + 8 * g + 4 * hh;
+          const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4*)&lse_s[q0];
+          const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4*)&dsum_s[q0];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * g + r;
+            const float pv = masked ? 0.f
+                                    : __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], p.c, bias) -
+                                                             l4[r]);
+            pr[i] = pv;
+            dsr[i] = pv * (pacc[i] - d4[r]);
+          }
+        }
+        bf16x8 plo, phi, slo, shi, slo2, shi2;
+        pack16(pr, plo, phi);
+        pack16_split(dsr, slo, shi, slo2, shi2);
+        // dV += P^T dout, dK += dS^T Q over these 32 queries (two 16-query chunks)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const bf16x8 d0 = tr_operand(dtile, 2 * qc, db, lane);
+          const bf16x8 d1 = tr_operand(dtile, 2 * qc + 1, db, lane);
+          const bf16x8 q0 = tr_operand(qtile, 2 * qc, db, lane);
+          const bf16x8 q1 = tr_operand(qtile, 2 * qc + 1, db, lane);
+          dvacc[db] = mfma32(plo, d0, dvacc[db]);
+          dvacc[db] = mfma32(phi, d1, dvacc[db]);
+          dkacc[db] = mfma32(slo, q0, dkacc[db]);
+          dkacc[db] = mfma32(shi, q1, dkacc[db]);
+          dkacc[db] = mfma32(slo2, q0, dkacc[db]);
+          dkacc[db] = mfma32(shi2, q1, dkacc[db]);
+        }
+      }
+    };
+    __syncthreads();  // every wave is done with the previous block's rings
+    if (n_i > 0) issue(qtile_of(0), S0{});
+    {
+      int ii = 0;
+      for (; ii + 2 <= n_i; ii += 2) {
+        step(ii, S0{});
+        step(ii + 1, S1{});
+      }
+      if (ii < n_i) step(ii, S0{});
+    }
+    // epilogue: lane holds channel 32 db + kl of rows (columns of the block)
+    // 32 wave + 8 (v / 4) + 4 hh + v % 4
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int ch = 32 * db + kl;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int lc = 32 * wave + 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (lc >= rows_valid) continue;
+        const int64_t row = (int64_t)KT * cb + lc;
+        float gk = p.scale * dkacc[db][v];
+        float gv = dvacc[db][v];
+        float* ak = LM ? p.dkbar : p.acc_k;
+        float* av = LM ? p.dvbar : p.acc_v;
+        const int64_t ai = ((int64_t)h * (LM ? p.tk : p.nk) + row) * kHeadDim + ch;
+        if (!p.first) {  // add this launch's query tiles to the earlier ones
+          gk += ak[ai];
+          gv += av[ai];
+        }
+        if (LM || !p.last) {
+          ak[ai] = gk;
+          av[ai] = gv;
+        } else {
+          if (p.landmarks && p.dkbar != nullptr) {  // this tile's landmark share
+            const float inv_n = 1.0f / (float)rows_valid;
+            gk += p.dkbar[((int64_t)h * p.tk + cb) * kHeadDim + ch] * inv_n;
+            gv += p.dvbar[((int64_t)h * p.tk + cb) * kHeadDim + ch] * inv_n;
+          }
+          if (gf) {
+            ((float*)p.dk)[(int64_t)h * p.kgsh + row * p.kgst + ch] = gk;
+            ((float*)p.dv)[(int64_t)h * p.kgsh + row * p.kgst + ch] = gv;
+          } else {
+            ((__bf16*)p.dk)[(int64_t)h * p.kgsh + row * p.kgst + ch] = (__bf16)gk;
+            ((__bf16*)p.dv)[(int64_t)h * p.kgsh + row * p.kgst + ch] = (__bf16)gv;
+          }
+        }
+      }
+    }
+  }
+}
+
+// The same with the query-side tiles loaded synchronously per query tile:
+// for query tiles larger than key tiles, whose two-stage rings would leave
+// one wave per SIMD (LDS).
+template <int QT, int KT, bool LM>
+__global__ __launch_bounds__(KT * 2) void bwd_dkdv_sync_kernel(BwdParams p) {
   constexpr int W = KT / 32;
   constexpr int NT = W * kWave;
   constexpr int QC = QT / 32;  // 32-query chunks per query tile
@@ -737,8 +1014,8 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(float* __restrict__ l
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-  size_t fwd, dqacc, lse, dsum, lacc, dacc, dkbar, dvbar, acck, accv, bits, count, off, list,
-      total;
+  size_t fwd, dqacc, lse, dsum, lacc, dacc, dkbar, dvbar, acck, accv, doutb, bits, count, off,
+      list, total;
 };
 
 BwdLayout bwd_layout(int64_t nq, int64_t nk, int32_t heads, int32_t q_tile, int32_t k_tile,
@@ -755,12 +1032,13 @@ BwdLayout bwd_layout(int64_t nq, int64_t nk, int32_t heads, int32_t q_tile, int3
   L.dvbar = L.dkbar;
   L.acck = a256((size_t)heads * nk * kHeadDim * sizeof(float));
   L.accv = L.acck;
+  L.doutb = a256((size_t)heads * nq * kHeadDim * sizeof(uint16_t));
   L.bits = a256((size_t)heads * tq * ((tk + 31) / 32) * sizeof(uint32_t));
   L.count = a256((size_t)heads * tk * sizeof(int32_t));
   L.off = a256((size_t)heads * (tk + 1) * sizeof(int32_t));
   L.list = a256((size_t)heads * tq * top_k * sizeof(int32_t));
   L.total = L.fwd + L.dqacc + L.lse + L.dsum + L.lacc + L.dacc + L.dkbar + L.dvbar + L.acck +
-            L.accv + L.bits + L.count + L.off + L.list;
+            L.accv + L.doutb + L.bits + L.count + L.off + L.list;
   return L;
 }
 
@@ -804,13 +1082,19 @@ hipError_t launch_bwd_kernels(BwdParams p, int32_t heads, hipStream_t s) {
       p.q_hi = std::min(p.tq, (c + 1) * qch);
       p.first = c == 0;
       p.last = c == nqc - 1;
-      if (pass == 0) {
-        const int nb = (p.tk + KT - 1) / KT;
-        hipLaunchKernelGGL((bwd_dkdv_kernel<QT, KT, true>), dim3((unsigned)nb, heads),
-                           dim3(KT * 2), 0, s, p);
+      const int nb = pass == 0 ? (p.tk + KT - 1) / KT : p.tk;
+      const dim3 grid((unsigned)nb, heads);
+      // two-stage rings keep two waves per SIMD while QT <= KT (LDS)
+      if constexpr (QT <= KT) {
+        if (pass == 0)
+          hipLaunchKernelGGL((bwd_dkdv_kernel<QT, KT, true>), grid, dim3(KT * 2), 0, s, p);
+        else
+          hipLaunchKernelGGL((bwd_dkdv_kernel<QT, KT, false>), grid, dim3(KT * 2), 0, s, p);
       } else {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<QT, KT, false>), dim3((unsigned)p.tk, heads),
-                           dim3(KT * 2), 0, s, p);
+        if (pass == 0)
+          hipLaunchKernelGGL((bwd_dkdv_sync_kernel<QT, KT, true>), grid, dim3(KT * 2), 0, s, p);
+        else
+          hipLaunchKernelGGL((bwd_dkdv_sync_kernel<QT, KT, false>), grid, dim3(KT * 2), 0, s, p);
       }
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
@@ -851,6 +1135,7 @@ hipError_t launch_tile_sparse_bwd(const uint16_t* q, int64_t nq, int64_t qst, in
   float* dvbar = (float*)take(L.dvbar);
   float* acc_k = (float*)take(L.acck);
   float* acc_v = (float*)take(L.accv);
+  uint16_t* dout_b = (uint16_t*)take(L.doutb);
   uint32_t* bits = (uint32_t*)take(L.bits);
   int32_t* count = (int32_t*)((uint8_t*)bits + L.bits);
   int32_t* off = (int32_t*)((uint8_t*)count + L.count);
@@ -866,6 +1151,14 @@ hipError_t launch_tile_sparse_bwd(const uint16_t* q, int64_t nq, int64_t qst, in
                              k_tile, top_k, scale, dq_acc, kHeadDim, nq * kHeadDim, true, flags, w,
                              s, lse);
     if (err != hipSuccess) return err;
+  }
+  // dout packed as bf16 rows for the dk, dv kernels' direct-to-LDS staging
+  if (nq > 0) {
+    const int64_t pieces = (int64_t)heads * nq * 8;
+    hipLaunchKernelGGL(bwd_pack_dout_kernel,
+                       dim3((unsigned)std::min<int64_t>((pieces + 255) / 256, 1 << 20)), dim3(256),
+                       0, s, dout, dst, dsh, g_f32 ? 1 : 0, nq, pieces, dout_b);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   // kept bits, counts, offsets, lists
   const int64_t nzero = (int64_t)((uint8_t*)off - (uint8_t*)bits) / 4;  // bits and counts
@@ -895,6 +1188,7 @@ hipError_t launch_tile_sparse_bwd(const uint16_t* q, int64_t nq, int64_t qst, in
   p.vbar_b = landmarks ? (const uint16_t*)(w + lm) : nullptr;
   p.sel = sel;
   p.dout = dout;
+  p.dout_b = dout_b;
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
