@@ -316,6 +316,34 @@ __global__ __launch_bounds__(KT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
   const int h = blockIdx.y;
   const int lrow = lane >> 3;
   const bool gf = p.g_f32 != 0;
+  // per-lane operand read offsets within a staged tile (see the dq kernel):
+  // row operands of row kl (+ 32 per query chunk), transposed operands at
+  // rows r0 and r0 + 8 (+ 16 per 16-query step) of channel block db
+  uint32_t roff[4], toff[2][2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) roff[s] = swz(kl, 2 * s + hh);
+  {
+    const int G = lane >> 4, S = lane & 15;
+    const int r0 = 4 * (G >> 1) + (S >> 2);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int col = 32 * db + 16 * (G & 1) + 4 * (S & 3);
+      const int chunk = col >> 3, half = (col & 7) ? 8 : 0;
+      toff[db][0] = swz(r0, chunk) + half;
+      toff[db][1] = swz(r0 + 8, chunk) + half;
+    }
+  }
+  auto row_op = [&](const lds_u8* tile, int qc, int s) -> bf16x8 {
+    return as_bf16x8(*(const __attribute__((address_space(3))) u32x4*)(tile + roff[s] + 4096 * qc));
+  };
+  auto tr_op = [&](const lds_u8* tile, int m, int db) -> bf16x8 {
+    const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(tile + toff[db][0] + 2048 * m));
+    const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(tile + toff[db][1] + 2048 * m));
+    const u32x2 w0 = __builtin_bit_cast(u32x2, t0), w1 = __builtin_bit_cast(u32x2, t1);
+    return as_bf16x8(u32x4{w0.x, w0.y, w1.x, w1.y});
+  };
   for (int cb = blockIdx.x; cb < n_blocks; cb += gridDim.x) {
     // this lane's column (key token or landmark row) and its validity
     const int col = KT * cb + 32 * wave + kl;
@@ -445,8 +473,8 @@ __global__ __launch_bounds__(KT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         f32x16 sacc, pacc;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const bf16x8 aq = row_operand(qtile, 32 * qc + kl, s, hh);
-          const bf16x8 ad = row_operand(dtile, 32 * qc + kl, s, hh);
+          const bf16x8 aq = row_op(qtile, qc, s);
+          const bf16x8 ad = row_op(dtile, qc, s);
           if (s == 0) {
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kop[0], f32x16{}, 0, 0, 0);
             pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vop[0], f32x16{}, 0, 0, 0);
@@ -486,10 +514,10 @@ __global__ __launch_bounds__(KT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         // dV += P^T dout, dK += dS^T Q over these 32 queries (two 16-query chunks)
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
-          const bf16x8 d0 = tr_operand(dtile, 2 * qc, db, lane);
-          const bf16x8 d1 = tr_operand(dtile, 2 * qc + 1, db, lane);
-          const bf16x8 q0 = tr_operand(qtile, 2 * qc, db, lane);
-          const bf16x8 q1 = tr_operand(qtile, 2 * qc + 1, db, lane);
+          const bf16x8 d0 = tr_op(dtile, 2 * qc, db);
+          const bf16x8 d1 = tr_op(dtile, 2 * qc + 1, db);
+          const bf16x8 q0 = tr_op(qtile, 2 * qc, db);
+          const bf16x8 q1 = tr_op(qtile, 2 * qc + 1, db);
           dvacc[db] = mfma32(plo, d0, dvacc[db]);
           dvacc[db] = mfma32(phi, d1, dvacc[db]);
           dkacc[db] = mfma32(slo, q0, dkacc[db]);
@@ -779,6 +807,35 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
   // physical chunk lane % 8, i.e. logical chunk (lane % 8) ^ swz_f(row) of
   // the row (the swizzled layout the operand reads expect)
   const int lrow = lane >> 3;
+  // per-lane byte offsets of the operand reads within a staged block (the
+  // swizzle depends on row bits 1-3 only, so 16- and 32-row steps are plain
+  // offsets): row operands of key row qi, chunk 2 s + hh; transposed
+  // operands at rows r0 and r0 + 8 of the lane's channel block db
+  uint32_t koff[4], toff[2][2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) koff[s] = swz(qi, 2 * s + hh);
+  {
+    const int G = lane >> 4, S = lane & 15;
+    const int r0 = 4 * (G >> 1) + (S >> 2);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int col = 32 * db + 16 * (G & 1) + 4 * (S & 3);
+      const int chunk = col >> 3, half = (col & 7) ? 8 : 0;
+      toff[db][0] = swz(r0, chunk) + half;
+      toff[db][1] = swz(r0 + 8, chunk) + half;
+    }
+  }
+  auto row_op = [&](const lds_u8* tile, int b, int s) -> bf16x8 {
+    return as_bf16x8(*(const __attribute__((address_space(3))) u32x4*)(tile + koff[s] + 4096 * b));
+  };
+  auto tr_op = [&](const lds_u8* tile, int m, int db) -> bf16x8 {
+    const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(tile + toff[db][0] + 2048 * m));
+    const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(tile + toff[db][1] + 2048 * m));
+    const u32x2 w0 = __builtin_bit_cast(u32x2, t0), w1 = __builtin_bit_cast(u32x2, t1);
+    return as_bf16x8(u32x4{w0.x, w0.y, w1.x, w1.y});
+  };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   for (int64_t item = blockIdx.x; item < (int64_t)p.heads * p.tq; item += gridDim.x) {
@@ -896,8 +953,8 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         f32x16 sacc, pacc;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const bf16x8 ak = row_operand(ktile, 32 * b + qi, s, hh);
-          const bf16x8 av = row_operand(vtile, 32 * b + qi, s, hh);
+          const bf16x8 ak = row_op(ktile, b, s);
+          const bf16x8 av = row_op(vtile, b, s);
           if (s == 0) {
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qop[0], f32x16{}, 0, 0, 0);
             pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, dop[0], f32x16{}, 0, 0, 0);
@@ -940,8 +997,8 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
           // dq^T += K^T dS^T over 16-key chunks 2b and 2b + 1
 #pragma unroll
           for (int db = 0; db < 2; ++db) {
-            const bf16x8 k0 = tr_operand(ktile, 2 * b, db, lane);
-            const bf16x8 k1 = tr_operand(ktile, 2 * b + 1, db, lane);
+            const bf16x8 k0 = tr_op(ktile, 2 * b, db);
+            const bf16x8 k1 = tr_op(ktile, 2 * b + 1, db);
             dqacc[db] = mfma32(k0, slo, dqacc[db]);
             dqacc[db] = mfma32(k1, shi, dqacc[db]);
             dqacc[db] = mfma32(k0, slo2, dqacc[db]);
