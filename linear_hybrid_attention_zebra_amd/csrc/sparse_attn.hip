@@ -941,17 +941,32 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
   }
   // direct-to-LDS staging as in tile_sparse_kernel, through buffer
-  // resources: piece v covers rows 8(wave + W v) + lane/8 of a block; W is
-  // even, so the lane's swizzled chunk is the same for every piece. The
-  // resource of a block ends at its last valid row, so the rows past a short
-  // last tile read as zeros (their columns are masked).
+  // resources; the resource of a block ends at its last valid row, so the
+  // rows past a short last tile read as zeros (their columns are masked).
+  // With two waves each wave stages exactly its own key half (pieces
+  // 4 kh .. 4 kh + 3, rows 32 kh ..), so no wave reads what another loaded
+  // and the steps need no workgroup barrier, only the wave's own waits.
+  // With four waves piece v of wave w is w + 4 v and the steps synchronise
+  // the workgroup. Piece u covers rows 8 u + lane / 8, lane chunk
+  // (lane % 8) ^ swz_f(row).
+  constexpr bool kOwnHalf = W == 2;
   const int lrow = lane >> 3;
-  const int r_lane = 8 * wave + lrow;
-  const int lchunk = (lane & 7) ^ swz_f(r_lane);
+  auto piece = [&](int v) { return kOwnHalf ? 4 * kh + v : wave + W * v; };
   // (key/value rows are 128 bytes apart here, like landmark rows)
   uint32_t off_v[NU];
 #pragma unroll
-  for (int v = 0; v < NU; ++v) off_v[v] = (uint32_t)((r_lane + 8 * W * v) * 128 + lchunk * 16);
+  for (int v = 0; v < NU; ++v) {
+    const int r = 8 * piece(v) + lrow;
+    off_v[v] = (uint32_t)(r * 128 + (((lane & 7) ^ swz_f(r)) << 4));
+  }
+  // end of a step's waits: with own-half staging the wave's own loads and
+  // LDS reads; otherwise also every other wave's
+  auto step_sync = [&]() {
+    if constexpr (kOwnHalf)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    else
+      lds_barrier();
+  };
 
   for (int64_t item = blockIdx.x; item < p.n_items; item += gridDim.x) {
     // per-item copies of the argument pointers that lane addresses are formed
@@ -1044,6 +1059,9 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
       if (dense || t_v >= n_kept) return;
       const int hi = min(t_k, n_kept - 1);
       if (t_v >= win_lo && hi < win_lo + kWin) return;
+      // the waves may be at different steps (own-half staging): every wave
+      // has passed its reads of the old window first
+      __syncthreads();
       win_lo = t_v;
       const int nw = min(kWin, n_kept - t_v);
       for (int e = tid; e < nw; e += NT)
@@ -1067,7 +1085,7 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
       return block_rsrc(base, rows * 128);
     };
     auto fire = [&](const Src& src, lds_blk* dst, int v) {
-      buffer_to_lds(src, (__attribute__((address_space(3))) void*)&dst[wave + W * v][0], off_v[v]);
+      buffer_to_lds(src, (__attribute__((address_space(3))) void*)&dst[piece(v)][0], off_v[v]);
     };
     auto block_mask = [&](int t) -> uint64_t {
       if (t < n_kept) return t == n_kept - 1 && last_rows < KT ? ~0ull << last_rows : 0ull;
@@ -1290,7 +1308,7 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
       };
       auto step = [&](int t, auto par, auto masked_c) {
         wait_vmcnt<0>();
-        lds_barrier();
+        step_sync();
         const int tkn = min(t + 2, n_total - 1);
         const int tvn = max(min(t, n_total - 1), 0);
         ensure_window(tvn, tkn);
@@ -1321,7 +1339,7 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
       };
       auto drain = [&](auto par) {  // PV of the last block
         wait_vmcnt<0>();
-        lds_barrier();
+        step_sync();
         u32x4 va[2][2];
         read_v(par, va);
         bf16x8(&pr)[2][2] = pbuf(par);
