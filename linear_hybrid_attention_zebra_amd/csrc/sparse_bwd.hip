@@ -466,6 +466,10 @@ __global__ __launch_bounds__(KT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
             wi < p.bit_words ? p.bits[((int64_t)h * p.tq + qt) * p.bit_words + wi] : 0u;
         masked = masked || ((word >> kl) & 1u);
       }
+      // an excluded landmark column enters with logit bias -inf (probability
+      // zero); key tile columns past the end need no exclusion: a lane adds
+      // only into its own column's dk and dv, which are never stored
+      const float cbias = masked ? -INFINITY : bias;
 #pragma unroll
       for (int qc = 0; qc < QC; ++qc) {
         // S = Q K^T and dP = dout V^T for 32 queries x this wave's 32 columns:
@@ -501,9 +505,9 @@ __global__ __launch_bounds__(KT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 4 * g + r;
-            const float pv = masked ? 0.f
-                                    : __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], p.c, bias) -
-                                                             l4[r]);
+            const float pv =
+                LM ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], p.c, cbias) - l4[r])
+                   : __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], p.c, -l4[r]));
             pr[i] = pv;
             dsr[i] = pv * (pacc[i] - d4[r]);
           }
@@ -922,6 +926,108 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     // float32, and D = sum P dP then matches dP exactly (dP - D cancels, which
     // would amplify any mismatch). sweep 1: dS and dq.
     float dpart = 0.f, lpart = 0.f;
+    // A 64-key block without excluded columns, in a fixed instruction order
+    // (scheduling fences between MFMA slots) so that each wave's VALU work
+    // runs beside its own MFMAs: slots 1-8 S and dP of key half 0 (operand
+    // reads of half 1 beside them), slots 9-16 S and dP of half 1 beside the
+    // probabilities of half 0 (sweep 1: their dS split into bf16 pairs, and
+    // the K^T operand reads of half 0), slots 17-24 dq of half 0 beside the
+    // probabilities of half 1, slots 25-32 dq of half 1. Per accumulator the
+    // summation order is that of the plain block loop below.
+    auto fast_block = [&](const lds_u8* ktile, const lds_u8* vtile, float nb) {
+      bf16x8 ka0[4], va0[4], ka1[4], va1[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        ka0[s] = row_op(ktile, 0, s);
+        va0[s] = row_op(vtile, 0, s);
+      }
+      f32x16 sa0, pa0, sa1, pa1;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {  // slots 1-8
+        sa0 = s == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0[0], qop[0], f32x16{}, 0, 0, 0)
+                     : mfma32(ka0[s], qop[s], sa0);
+        ka1[s] = row_op(ktile, 1, s);
+        __builtin_amdgcn_sched_barrier(0);
+        pa0 = s == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0[0], dop[0], f32x16{}, 0, 0, 0)
+                     : mfma32(va0[s], dop[s], pa0);
+        va1[s] = row_op(vtile, 1, s);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // probabilities (and, in sweep 1, the split dS) of keys 2 j, 2 j + 1
+      uint32_t w[8], r[8];
+      auto job = [&](const f32x16& sa, const f32x16& pa, int j) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[2 * j], p.c, nb));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[2 * j + 1], p.c, nb));
+        if constexpr (kGrad) {
+          const float d0 = p0 * (pa[2 * j] - dsum), d1 = p1 * (pa[2 * j + 1] - dsum);
+          w[j] = pack_bf16x2(d0, d1);
+          r[j] = pack_bf16x2(d0 - bf16lo(w[j]), d1 - bf16hi(w[j]));
+        } else {
+          dpart = __builtin_fmaf(p0, pa[2 * j], dpart);
+          lpart += p0;
+          dpart = __builtin_fmaf(p1, pa[2 * j + 1], dpart);
+          lpart += p1;
+        }
+      };
+      bf16x8 kt[2][2];  // K^T operands [16-key chunk][channel block]
+      auto dq_slot = [&](int j) {  // dq^T += K^T dS^T: (lo, hi, small lo, small hi) per block
+        const int db = j & 1, part = j >> 1;
+        const int m = part & 1;
+        const bf16x8 op = part == 0   ? as_bf16x8(u32x4{w[0], w[1], w[2], w[3]})
+                          : part == 1 ? as_bf16x8(u32x4{w[4], w[5], w[6], w[7]})
+                          : part == 2 ? as_bf16x8(u32x4{r[0], r[1], r[2], r[3]})
+                                      : as_bf16x8(u32x4{r[4], r[5], r[6], r[7]});
+        dqacc[db] = mfma32(kt[m][db], op, dqacc[db]);
+      };
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {  // slots 9-16
+        const int s = j >> 1;
+        if ((j & 1) == 0)
+          sa1 = s == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1[0], qop[0], f32x16{}, 0, 0, 0)
+                       : mfma32(ka1[s], qop[s], sa1);
+        else
+          pa1 = s == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1[0], dop[0], f32x16{}, 0, 0, 0)
+                       : mfma32(va1[s], dop[s], pa1);
+        job(sa0, pa0, j);
+        if constexpr (kGrad) {
+          if (j < 4) kt[j >> 1][j & 1] = tr_op(ktile, j >> 1, j & 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (kGrad) {
+        // w, r of half 0 are complete; half 1's reuse them after its dq slots
+        uint32_t w0[8], r0[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          w0[j] = w[j];
+          r0[j] = r[j];
+        }
+        bf16x8 kt1[2][2];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {  // slots 17-24
+          const int db = j & 1, part = j >> 1, m = part & 1;
+          const bf16x8 op = part == 0   ? as_bf16x8(u32x4{w0[0], w0[1], w0[2], w0[3]})
+                            : part == 1 ? as_bf16x8(u32x4{w0[4], w0[5], w0[6], w0[7]})
+                            : part == 2 ? as_bf16x8(u32x4{r0[0], r0[1], r0[2], r0[3]})
+                                        : as_bf16x8(u32x4{r0[4], r0[5], r0[6], r0[7]});
+          dqacc[db] = mfma32(kt[m][db], op, dqacc[db]);
+          job(sa1, pa1, j);
+          if (j < 4) kt1[j >> 1][j & 1] = tr_op(ktile, 2 + (j >> 1), j & 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kt[j >> 2][(j >> 1) & 1] = kt1[j >> 2][(j >> 1) & 1];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {  // slots 25-32
+          dq_slot(j);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) job(sa1, pa1, j);
+      }
+    };
     auto step = [&](int t, auto stc) {
       __syncthreads();  // block t has landed for every wave; the other stage is free
       if (t + 1 < n_total) {
@@ -946,6 +1052,12 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
       }
       if (bk.rows < KT) cmask |= ~0ull << bk.rows;
+      if constexpr (NB == 2) {
+        if (cmask == 0ull && tail_col < 0) {
+          fast_block(ktile, vtile, bias - lse);
+          return;
+        }
+      }
       // S^T = K Q^T, dP^T = V dout^T: lane = query, register = key
       // 32 b + 8 (v / 4) + 4 hh + v % 4
 #pragma unroll
