@@ -926,6 +926,28 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     // float32, and D = sum P dP then matches dP exactly (dP - D cancels, which
     // would amplify any mismatch). sweep 1: dS and dq.
     float dpart = 0.f, lpart = 0.f;
+    // sweep 0: the probabilities of key half 1 of the last fast block, done
+    // beside the next block's first MFMAs (or before any other block)
+    f32x16 pend_s, pend_p;
+    float pend_nb = 0.f;
+    bool pending = false;
+    auto pend_job = [&](int j) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(pend_s[2 * j], p.c, pend_nb));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(pend_s[2 * j + 1], p.c, pend_nb));
+      dpart = __builtin_fmaf(p0, pend_p[2 * j], dpart);
+      lpart += p0;
+      dpart = __builtin_fmaf(p1, pend_p[2 * j + 1], dpart);
+      lpart += p1;
+    };
+    auto flush = [&]() {
+      if constexpr (!kGrad) {
+        if (pending) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pend_job(j);
+          pending = false;
+        }
+      }
+    };
     // A 64-key block without excluded columns, in a fixed instruction order
     // (scheduling fences between MFMA slots) so that each wave's VALU work
     // runs beside its own MFMAs: slots 1-8 S and dP of key half 0 (operand
@@ -934,7 +956,8 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     // the K^T operand reads of half 0), slots 17-24 dq of half 0 beside the
     // probabilities of half 1, slots 25-32 dq of half 1. Per accumulator the
     // summation order is that of the plain block loop below.
-    auto fast_block = [&](const lds_u8* ktile, const lds_u8* vtile, float nb) {
+    auto fast_block = [&](auto pend_c, const lds_u8* ktile, const lds_u8* vtile, float nb) {
+      constexpr bool pend_here = decltype(pend_c)::value;  // (sweep 0 only)
       bf16x8 ka0[4], va0[4], ka1[4], va1[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -942,16 +965,19 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         va0[s] = row_op(vtile, 0, s);
       }
       f32x16 sa0, pa0, sa1, pa1;
+      // sweep 0: a pending half of the previous block goes beside slots 1-8
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {  // slots 1-8
         sa0 = s == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0[0], qop[0], f32x16{}, 0, 0, 0)
                      : mfma32(ka0[s], qop[s], sa0);
         ka1[s] = row_op(ktile, 1, s);
+        if constexpr (pend_here) pend_job(2 * s);
         __builtin_amdgcn_sched_barrier(0);
         pa0 = s == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0[0], dop[0], f32x16{}, 0, 0, 0)
                      : mfma32(va0[s], dop[s], pa0);
         va1[s] = row_op(vtile, 1, s);
+        if constexpr (pend_here) pend_job(2 * s + 1);
         __builtin_amdgcn_sched_barrier(0);
       }
       // probabilities (and, in sweep 1, the split dS) of keys 2 j, 2 j + 1
@@ -1023,9 +1049,11 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
           dq_slot(j);
           __builtin_amdgcn_sched_barrier(0);
         }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) job(sa1, pa1, j);
+      } else {  // half 1's probabilities wait for the next block's first slots
+        pend_s = sa1;
+        pend_p = pa1;
+        pend_nb = nb;
+        pending = true;
       }
     };
     auto step = [&](int t, auto stc) {
@@ -1054,10 +1082,14 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
       if (bk.rows < KT) cmask |= ~0ull << bk.rows;
       if constexpr (NB == 2) {
         if (cmask == 0ull && tail_col < 0) {
-          fast_block(ktile, vtile, bias - lse);
+          if (!kGrad && pending)
+            fast_block(std::true_type{}, ktile, vtile, bias - lse);
+          else
+            fast_block(std::false_type{}, ktile, vtile, bias - lse);
           return;
         }
       }
+      flush();
       // S^T = K Q^T, dP^T = V dout^T: lane = query, register = key
       // 32 b + 8 (v / 4) + 4 hh + v % 4
 #pragma unroll
@@ -1127,6 +1159,7 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
       step(t + 1, S1{});
     }
     if (t < n_total) step(t, S0{});
+    flush();
     if constexpr (!kGrad) {  // add this launch's sums over both lane halves
       const auto sd = __builtin_amdgcn_permlane32_swap(__float_as_uint(dpart),
                                                        __float_as_uint(dpart), false, false);
