@@ -422,7 +422,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path "
-              "shards by head across GPUs, which this build does not run.", file=sys.stderr)
+              "would shard by head across GPUs; this implementation runs on one GPU.", file=sys.stderr)
         sys.exit(2)
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     import torch
