@@ -1518,20 +1518,41 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if (r >= rows) return;
   const int sub = threadIdx.x & 15;
   const float2* ml = part_ml + r * n_chunks;
+  // loads go out kB chunks at a time (the sums still run in chunk order)
+  constexpr int kB = 8;
   float ref = -INFINITY;  // over the chunks with columns (l > 0)
-  for (int ch = 0; ch < n_chunks; ++ch)
+  int ch = 0;
+  for (; ch + kB <= n_chunks; ch += kB) {
+    float2 m[kB];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) m[j] = ml[ch + j];
+#pragma unroll
+    for (int j = 0; j < kB; ++j)
+      if (m[j].y > 0.f) ref = fmaxf(ref, m[j].x);
+  }
+  for (; ch < n_chunks; ++ch)
     if (ml[ch].y > 0.f) ref = fmaxf(ref, ml[ch].x);
   const float* po = part_o + r * n_chunks * kHeadDim + 4 * sub;
   float l = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int ch = 0; ch < n_chunks; ++ch) {
-    const float2 m = ml[ch];
+  auto add = [&](float2 m, f32x4 x) {
     const float w = m.y > 0.f ? __builtin_amdgcn_exp2f(m.x - ref) : 0.f;
-    const f32x4 x = *(const f32x4*)(po + (int64_t)ch * kHeadDim);
     l = __builtin_fmaf(m.y, w, l);
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(x[i], w, acc[i]);
+  };
+  for (ch = 0; ch + kB <= n_chunks; ch += kB) {
+    float2 m[kB];
+    f32x4 x[kB];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      m[j] = ml[ch + j];
+      x[j] = *(const f32x4*)(po + (int64_t)(ch + j) * kHeadDim);
+    }
+#pragma unroll
+    for (int j = 0; j < kB; ++j) add(m[j], x[j]);
   }
+  for (; ch < n_chunks; ++ch) add(ml[ch], *(const f32x4*)(po + (int64_t)ch * kHeadDim));
   const float inv = l > 0.f ? 1.0f / l : 0.f;  // l == 0 only without any column
   const int64_t h = r / nq, q = r - h * nq;
   if (lse != nullptr && sub == 0) lse[r] = ref + __builtin_log2f(l);
