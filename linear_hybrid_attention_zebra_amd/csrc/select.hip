@@ -142,6 +142,26 @@ struct RowReader {
   }
 };
 
+// Visits chunks 0 .. n-1 in order; the loads of kB chunks go out together
+// (a pass over a row is otherwise one load latency per chunk).
+template <class F>
+__device__ __forceinline__ void for_chunks(const RowReader& rd, int nchunks, int lane, F&& f) {
+  constexpr int kB = 4;
+  int c = 0;
+  for (; c + kB <= nchunks; c += kB) {
+    float x[kB][4];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) rd.load(c + j, lane, x[j]);
+#pragma unroll
+    for (int j = 0; j < kB; ++j) f(c + j, x[j]);
+  }
+  for (; c < nchunks; ++c) {
+    float x[4];
+    rd.load(c, lane, x);
+    f(c, x);
+  }
+}
+
 // One wave per (head, query tile) row; no workgroup barriers. Passes over the
 // row (re-read from L2): value range; a 2048-bin monotone histogram in LDS;
 // the bin where the count from the top reaches top_k; the exact threshold tau
@@ -165,29 +185,25 @@ __global__ __launch_bounds__(kRowsPerGroup * kWave) void select_kernel(
 
   // 1. value range
   float lmax = -INFINITY, lmin = INFINITY;
-    for (int c = 0; c < nchunks; ++c) {
-    float x[4];
-    rd.load(c, lane, x);
+  for_chunks(rd, nchunks, lane, [&](int c, const float (&x)[4]) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       if (valid(c, u)) {
         lmax = fmaxf(lmax, x[u]);
         lmin = fminf(lmin, x[u]);
       }
-  }
+  });
   const float vmax = wave_max(lmax), vmin = wave_min(lmin);
 
   // 2. histogram; bin() is monotone non-decreasing in the value
   for (int b = lane; b < kBins; b += kWave) hist[b] = 0u;
   const float inv = (vmax > vmin) ? (float)kBins / (vmax - vmin) : 0.f;
   auto bin_of = [&](float x) { return min(kBins - 1, (int)((x - vmin) * inv)); };
-    for (int c = 0; c < nchunks; ++c) {
-    float x[4];
-    rd.load(c, lane, x);
+  for_chunks(rd, nchunks, lane, [&](int c, const float (&x)[4]) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       if (valid(c, u)) atomicAdd(&hist[bin_of(x[u])], 1u);
-  }
+  });
 
   // 3. the bin where the count from the top reaches top_k: lane l owns bins
   // 32(63-l) .. 32(63-l)+31, so lane order is descending value order
@@ -223,16 +239,14 @@ __global__ __launch_bounds__(kRowsPerGroup * kWave) void select_kernel(
   float tau;
   if (n_in_bin <= (uint32_t)kMaxCand) {
     if (lane == 0) ncand_all[wave] = 0u;
-    for (int c = 0; c < nchunks; ++c) {
-      float x[4];
-      rd.load(c, lane, x);
+    for_chunks(rd, nchunks, lane, [&](int c, const float (&x)[4]) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         if (valid(c, u) && bin_of(x[u]) == bstar) {
           const uint32_t slot = atomicAdd(&ncand_all[wave], 1u);
           cand[slot] = x[u];
         }
-    }
+    });
     float t = -INFINITY;
     bool found = false;
     for (uint32_t i = lane; i < n_in_bin; i += kWave) {
@@ -288,9 +302,7 @@ __global__ __launch_bounds__(kRowsPerGroup * kWave) void select_kernel(
   const uint32_t need_eq = n_gt < (uint32_t)top_k ? (uint32_t)top_k - n_gt : 0u;
   int32_t* out = sel + row * top_k;
   uint32_t base = 0, ties = 0;  // kept so far, ties seen so far (uniform)
-    for (int c = 0; c < nchunks; ++c) {
-    float x[4];
-    rd.load(c, lane, x);
+  for_chunks(rd, nchunks, lane, [&](int c, const float (&x)[4]) {
     uint32_t g = 0, e = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -325,7 +337,7 @@ __global__ __launch_bounds__(kRowsPerGroup * kWave) void select_kernel(
     const uint32_t tg = tot >> 16, te = tot & 0xffffu;
     base += tg + min(ties + te, need_eq) - min(ties, need_eq);
     ties += te;
-  }
+  });
 }
 
 }  // namespace
