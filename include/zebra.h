@@ -89,7 +89,7 @@ zebra_status zebra_pool_landmarks(const void* x, zebra_seq xs, int32_t tile, flo
  * top_k    1..t_k; t_k at most 32768.
  * sel_out  int32 [H][t_q][top_k], each row in ascending tile order.
  * workspace at least zebra_select_tiles_workspace(H, t_q, t_k) bytes (the
- *          float32 score matrix).
+ *          float32 score matrix, rows padded to a multiple of 32 scores).
  */
 size_t zebra_select_tiles_workspace(int32_t n_heads, int32_t t_q, int32_t t_k);
 zebra_status zebra_select_tiles(const float* qbar, const float* kbar, int32_t n_heads,

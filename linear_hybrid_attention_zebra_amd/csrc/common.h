@@ -67,6 +67,9 @@ struct SeqDesc {
 
 hipError_t launch_pool(const uint16_t* x, int64_t n, int32_t heads, int64_t st, int64_t sh,
                        int32_t tile, float* out, hipStream_t s);
+// Row stride (floats) of the select workspace's score matrix: t_k rounded up
+// to a multiple of 32, so every row starts on a 128-byte line.
+inline int32_t score_row_stride(int32_t tk) { return (tk + 31) & ~31; }
 hipError_t launch_select(const float* qbar, const float* kbar, int32_t heads, int32_t tq,
                          int32_t tk, int32_t top_k, int32_t* sel, float* scores,
                          hipStream_t s);

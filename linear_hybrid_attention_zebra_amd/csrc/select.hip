@@ -7,9 +7,9 @@
 // (s_ij descending, j ascending) and emits them in ascending order.
 //
 // Two kernels:
-//  1. score_kernel: a K=64 float32 GEMM, 128x128 output tile per workgroup
-//     and 8x8 per thread, operands staged transposed in LDS, sequential FMA
-//     over the 64 channels (the same summation order for every element).
+//  1. score_kernel: a K=64 float32 GEMM on float32 MFMAs, 128x128 output
+//     tile per workgroup, operands staged in LDS; every element has the same
+//     fixed summation order. Score rows are padded to 32 floats.
 //  2. select_kernel: one wave per (head, query tile), no workgroup barriers.
 //     The k-th largest value tau is found exactly: min/max, a 2048-bin
 //     histogram on the value range (a monotone binning, so equal scores share
@@ -26,17 +26,21 @@ namespace {
 
 constexpr int kScoreTile = 128;  // output tile edge of score_kernel
 
-// One 128x128 tile of s = qbar kbar^T per workgroup; thread (ty, tx) owns rows
-// 8ty .. 8ty+7 and columns 4tx .. 4tx+3, 64+4tx .. 64+4tx+3. Both operand
-// tiles sit transposed in LDS ([channel][row]), so each channel step is four
-// 16-byte reads and 64 FMAs per thread; every output element is the same
-// sequential FMA chain over the 64 channels.
+// One 128x128 tile of s = qbar kbar^T per workgroup, a 64x64 quarter per
+// wave, on float32 MFMAs (32x32x2: exact float32 products, float32 sums).
+// Both operand tiles sit row-major in LDS (rows padded to 68 floats, so the
+// 16-byte reads of 16 consecutive rows hit distinct banks). MFMA step t
+// contracts channels t (lane half 0) and 32 + t (lane half 1), t = 0..31 in
+// order: every output element has the same fixed summation order, and
+// integer-valued inputs give exact scores. Score rows are ld floats apart, ld
+// a multiple of 32, so each 32-lane store fills one 128-byte line.
 __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qbar,
                                                     const float* __restrict__ kbar, int32_t tq,
-                                                    int32_t tk, float* __restrict__ scores) {
-  constexpr int T = kScoreTile, P = T + 4;  // padded rows of the transposed tiles
-  __shared__ __attribute__((aligned(16))) float qs[kHeadDim][P];
-  __shared__ __attribute__((aligned(16))) float ks[kHeadDim][P];
+                                                    int32_t tk, int32_t ld,
+                                                    float* __restrict__ scores) {
+  constexpr int T = kScoreTile, LD = kHeadDim + 4;
+  __shared__ __attribute__((aligned(16))) float qs[T * LD];
+  __shared__ __attribute__((aligned(16))) float ks[T * LD];
   const int h = blockIdx.z;
   const int i0 = blockIdx.y * T;
   const int j0 = blockIdx.x * T;
@@ -51,55 +55,50 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qb
     f32x4 qv = {0.f, 0.f, 0.f, 0.f}, kv = {0.f, 0.f, 0.f, 0.f};
     if (i0 + r < tq) qv = *(const f32x4*)(qh + (int64_t)(i0 + r) * kHeadDim + 4 * c4);
     if (j0 + r < tk) kv = *(const f32x4*)(kh + (int64_t)(j0 + r) * kHeadDim + 4 * c4);
-    qs[4 * c4][r] = qv.x;
-    qs[4 * c4 + 1][r] = qv.y;
-    qs[4 * c4 + 2][r] = qv.z;
-    qs[4 * c4 + 3][r] = qv.w;
-    ks[4 * c4][r] = kv.x;
-    ks[4 * c4 + 1][r] = kv.y;
-    ks[4 * c4 + 2][r] = kv.z;
-    ks[4 * c4 + 3][r] = kv.w;
+    *(f32x4*)&qs[r * LD + 4 * c4] = qv;
+    *(f32x4*)&ks[r * LD + 4 * c4] = kv;
   }
   __syncthreads();
-  const int tx = tid & 15, ty = tid >> 4;
-  float acc[8][8];
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int wr = 64 * (wave >> 1), wc = 64 * (wave & 1);  // the wave's quarter
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) acc[a][b] = 0.f;
-#pragma unroll 4
-  for (int c = 0; c < kHeadDim; ++c) {
-    const f32x4 q0 = *(const f32x4*)&qs[c][8 * ty];
-    const f32x4 q1 = *(const f32x4*)&qs[c][8 * ty + 4];
-    const f32x4 k0 = *(const f32x4*)&ks[c][4 * tx];
-    const f32x4 k1 = *(const f32x4*)&ks[c][64 + 4 * tx];
-    const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-    const float kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
 #pragma unroll
-      for (int b = 0; b < 8; ++b) acc[a][b] = __builtin_fmaf(qv[a], kv[b], acc[a][b]);
+  for (int u = 0; u < 8; ++u) {  // channels 32 hh + 4 u .. +3: steps t = 4u .. 4u+3
+    f32x4 qa[2], kb[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      qa[a] = *(const f32x4*)&qs[(wr + 32 * a + l32) * LD + 32 * hh + 4 * u];
+      kb[a] = *(const f32x4*)&ks[(wc + 32 * a + l32) * LD + 32 * hh + 4 * u];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[a][e], kb[b][e], acc[a][b], 0, 0, 0);
   }
-  float* out = scores + (int64_t)h * tq * tk;
-  const bool vec = (tk & 3) == 0;
+  // lane l holds column l % 32 and rows 8 (v / 4) + 4 (l / 32) + v % 4 of a block
+  float* out = scores + (int64_t)h * tq * ld;
 #pragma unroll
-  for (int a = 0; a < 8; ++a) {
-    const int i = i0 + 8 * ty + a;
-    if (i >= tq) continue;
-    float* orow = out + (int64_t)i * tk;
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int j = j0 + 64 * half + 4 * tx;
-      const float* src = &acc[a][4 * half];
-      if (vec && j + 3 < tk) {
-        *(f32x4*)(orow + j) = f32x4{src[0], src[1], src[2], src[3]};
-      } else {
+    for (int b = 0; b < 2; ++b) {
+      const int j = j0 + wc + 32 * b + l32;
+      if (j >= tk) continue;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-          if (j + b < tk) orow[j + b] = src[b];
+      for (int v = 0; v < 16; ++v) {
+        const int i = i0 + wr + 32 * a + 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (i < tq) out[(int64_t)i * ld + j] = acc[a][b][v];
       }
     }
-  }
 }
 
 constexpr int kBins = 2048;
@@ -169,7 +168,7 @@ __device__ __forceinline__ void for_chunks(const RowReader& rd, int nchunks, int
 // bin holds more than kMaxCand values, e.g. many equal scores); then an
 // ordered compaction of {s > tau} plus the lowest-indexed ties at tau.
 __global__ __launch_bounds__(kRowsPerGroup * kWave) void select_kernel(
-    const float* __restrict__ scores, int64_t n_rows, int32_t tk, int32_t top_k,
+    const float* __restrict__ scores, int64_t n_rows, int32_t tk, int32_t ld, int32_t top_k,
     int32_t* __restrict__ sel) {
   __shared__ uint32_t hist_all[kRowsPerGroup][kBins];
   __shared__ float cand_all[kRowsPerGroup][kMaxCand];
@@ -179,7 +178,7 @@ __global__ __launch_bounds__(kRowsPerGroup * kWave) void select_kernel(
   if (row >= n_rows) return;  // whole wave; no barriers follow
   uint32_t* hist = hist_all[wave];
   float* cand = cand_all[wave];
-  const RowReader rd{scores + row * tk, tk, (tk & 3) == 0};
+  const RowReader rd{scores + row * ld, tk, true};  // rows start 128-byte aligned
   const int nchunks = (tk + 255) / 256;
   auto valid = [&](int c, int u) { return 256 * c + 4 * lane + u < tk; };
 
@@ -347,12 +346,13 @@ hipError_t launch_select(const float* qbar, const float* kbar, int32_t heads, in
                          hipStream_t s) {
   if (heads == 0 || tq == 0) return hipSuccess;
   dim3 sgrid((tk + kScoreTile - 1) / kScoreTile, (tq + kScoreTile - 1) / kScoreTile, heads);
-  hipLaunchKernelGGL(score_kernel, sgrid, dim3(256), 0, s, qbar, kbar, tq, tk, scores);
+  const int32_t ld = score_row_stride(tk);
+  hipLaunchKernelGGL(score_kernel, sgrid, dim3(256), 0, s, qbar, kbar, tq, tk, ld, scores);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t rows = (int64_t)heads * tq;
   hipLaunchKernelGGL(select_kernel, dim3((unsigned)((rows + kRowsPerGroup - 1) / kRowsPerGroup)),
-                     dim3(kRowsPerGroup * kWave), 0, s, scores, rows, tk, top_k, sel);
+                     dim3(kRowsPerGroup * kWave), 0, s, scores, rows, tk, ld, top_k, sel);
   return hipGetLastError();
 }
 

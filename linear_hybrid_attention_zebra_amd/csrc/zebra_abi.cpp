@@ -120,7 +120,7 @@ zebra_status zebra_pool_landmarks(const void* x, zebra_seq xs, int32_t tile, flo
 
 size_t zebra_select_tiles_workspace(int32_t n_heads, int32_t t_q, int32_t t_k) {
   if (n_heads <= 0 || t_q <= 0 || t_k <= 0) return 0;
-  return (size_t)n_heads * (size_t)t_q * (size_t)t_k * sizeof(float);
+  return (size_t)n_heads * (size_t)t_q * (size_t)zebra::score_row_stride(t_k) * sizeof(float);
 }
 
 zebra_status zebra_select_tiles(const float* qbar, const float* kbar, int32_t n_heads,

@@ -78,7 +78,7 @@ def test_pool_validation(lib):
 def test_select_validation(lib):
     f = lib.zebra_select_tiles
     ws = lib.zebra_select_tiles_workspace(2, 10, 20)
-    assert ws == 2 * 10 * 20 * 4
+    assert ws == 2 * 10 * 32 * 4  # rows padded to 32 scores
     args = lambda top_k=5, hd=64, ws_ptr=P(1 << 30), ws_b=ws, tk=20: (
         P(1 << 16), P(1 << 20), 2, 10, tk, hd, top_k, P(1 << 24), ws_ptr, ws_b, None)
     assert f(*args(top_k=0)) == zb.ZEBRA_ERR_INVALID_ARG
