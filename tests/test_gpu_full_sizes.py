@@ -61,6 +61,24 @@ def test_full_size_sparse_stage_sampled(name, stage):
     print(f"[parity] near-tie swaps {swaps} of {len(rows)} sampled rows", flush=True)
 
 
+def test_full_size_sparse_stage_is_deterministic():
+    """Stage 9 of the 512-view stack, twice: selection and output bitwise equal.
+    Every sum runs in a fixed order (no float atomics), so any difference is a
+    race in staging; some show only at full size, where the waves of a
+    workgroup drift furthest apart."""
+    w = synth.WORKLOADS["stack24-512v"]
+    print(f"[case] full-size sparse determinism stack24-512v stage 9: N={w.n_tokens}", flush=True)
+    q, k, v = synth.stage_inputs(w, 9, DEV)
+    bufs = stage_mod.SparseBuffers.allocate(w.heads, w.n_tokens, w.n_tokens, w.q_tile, w.k_tile,
+                                            w.k, DEV)
+    stage_mod.sparse_stage(q, k, v, w.q_tile, w.k_tile, w.k, SCALE, bufs)
+    first_out, first_sel = bufs.out.clone(), bufs.sel.clone()
+    stage_mod.sparse_stage(q, k, v, w.q_tile, w.k_tile, w.k, SCALE, bufs)
+    torch.cuda.synchronize()
+    assert torch.equal(first_sel, bufs.sel)
+    assert torch.equal(first_out, bufs.out)
+
+
 LINEAR_STAGES = [("linear-128v", 0), ("stack24-512v", 0)]
 
 
