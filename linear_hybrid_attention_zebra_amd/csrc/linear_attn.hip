@@ -100,7 +100,8 @@ __global__ __launch_bounds__(256) void linear_state_kernel(const uint16_t* __res
   float z8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
   // this thread's two 16-byte pieces of a 64-token block: row e/8, chunk e%8;
-  // the next block's loads are in flight while one block is used
+  // the next block's loads are in flight while one block is used. K and V
+  // are read once: non-temporal loads keep them from displacing L2 lines.
   u32x4 kn[2], vn[2];
   auto load_block = [&](int64_t b0) {
 #pragma unroll
@@ -110,8 +111,8 @@ __global__ __launch_bounds__(256) void linear_state_kernel(const uint16_t* __res
       kn[u] = u32x4{0u, 0u, 0u, 0u};
       vn[u] = u32x4{0u, 0u, 0u, 0u};
       if (tok < t1) {
-        kn[u] = *(const u32x4*)(kh + tok * kst + 8 * (e & 7));
-        vn[u] = *(const u32x4*)(vh + tok * kst + 8 * (e & 7));
+        kn[u] = __builtin_nontemporal_load((const u32x4*)(kh + tok * kst + 8 * (e & 7)));
+        vn[u] = __builtin_nontemporal_load((const u32x4*)(vh + tok * kst + 8 * (e & 7)));
       }
     }
   };
