@@ -412,8 +412,9 @@ def cpu_baseline(args, w, torch, inputs, synth):
         cal_part = time.perf_counter() - t0
         est["linear_stage_s"] = heads * lin_head
         est["calibration_s"] = heads * cal_part * (w.fit_samples / m_sub)
-        sample.append(f"linear stage {s}: head 0 in full; calibration of head 0 on "
-                      f"{m_sub} of {w.fit_samples} sampled queries")
+        sample.append(f"linear stage {s}: head 0 in full (calibration of head 0 on "
+                      f"{m_sub} of {w.fit_samples} sampled queries timed too, reported in "
+                      f"per_stage_s, outside the step)")
     # the step's work: the affine fit is a one-off calibration, as on the GPU side
     total = (len(sparse_s) * est.get("sparse_stage_s", 0.0)
              + len(linear_s) * est.get("linear_stage_s", 0.0))
