@@ -201,19 +201,39 @@ __global__ __launch_bounds__(256) void bwd_pack_dout_kernel(const void* __restri
   }
 }
 
+// Kept-tile bit matrix and per-key-tile counts. One workgroup per (head,
+// rows_per_wg query tiles, at most kBitsRows): each row's bits are set in LDS and stored whole, and the
+// counts of the workgroup's rows gather in an LDS histogram that is added to
+// the global counts once (integer sums, so the result does not depend on
+// the order). Dynamic LDS: tk counters, then bit_words words.
+constexpr int kBitsRows = 64;
 __global__ __launch_bounds__(256) void bwd_bits_kernel(const int32_t* __restrict__ sel,
-                                                       int64_t rows, int32_t tq, int32_t tk,
-                                                       int32_t top_k, int32_t bit_words,
+                                                       int32_t tq, int32_t tk, int32_t top_k,
+                                                       int32_t bit_words, int32_t rows_per_wg,
                                                        uint32_t* __restrict__ bits,
                                                        int32_t* __restrict__ count) {
-  const int64_t row = blockIdx.x;  // (head, query tile)
-  if (row >= rows) return;
-  const int64_t h = row / tq;
-  for (int e = threadIdx.x; e < top_k; e += 256) {
-    const int j = min(max(sel[row * top_k + e], 0), tk - 1);
-    atomicOr(&bits[row * bit_words + (j >> 5)], 1u << (j & 31));
-    atomicAdd(&count[h * tk + j], 1);
+  extern __shared__ uint32_t bits_lds[];
+  uint32_t* cnt = bits_lds;
+  uint32_t* wb = bits_lds + tk;
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y;
+  const int i0 = blockIdx.x * rows_per_wg, i1 = min(tq, i0 + rows_per_wg);
+  for (int j = tid; j < tk; j += 256) cnt[j] = 0u;
+  for (int i = i0; i < i1; ++i) {
+    const int64_t row = (int64_t)h * tq + i;
+    for (int e = tid; e < bit_words; e += 256) wb[e] = 0u;
+    __syncthreads();  // (also: the histogram is cleared)
+    for (int e = tid; e < top_k; e += 256) {
+      const int j = min(max(sel[row * top_k + e], 0), tk - 1);
+      atomicOr(&wb[j >> 5], 1u << (j & 31));
+      atomicAdd(&cnt[j], 1u);
+    }
+    __syncthreads();
+    for (int e = tid; e < bit_words; e += 256) bits[row * bit_words + e] = wb[e];
+    __syncthreads();  // the row is stored before the next one clears it
   }
+  for (int j = tid; j < tk; j += 256)
+    if (cnt[j] != 0u) atomicAdd(&count[(int64_t)h * tk + j], (int)cnt[j]);
 }
 
 // exclusive scan of the counts of one head -> list offsets (head h starts at
@@ -1371,8 +1391,16 @@ hipError_t launch_tile_sparse_bwd(const uint16_t* q, int64_t nq, int64_t qst, in
                      dim3(256), 0, s, bits, nzero);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (tq > 0) {
-    hipLaunchKernelGGL(bwd_bits_kernel, dim3((unsigned)((int64_t)heads * tq)), dim3(256), 0, s,
-                       sel, (int64_t)heads * tq, tq, tk, top_k, bit_words, bits, count);
+    const size_t lds = (size_t)(tk + bit_words) * sizeof(uint32_t);  // at most 132 KB
+    if ((err = hipFuncSetAttribute((const void*)bwd_bits_kernel,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) !=
+        hipSuccess)
+      return err;
+    // about 2,048 workgroups, at most kBitsRows rows each
+    const int32_t rpw = (int32_t)std::min<int64_t>(
+        kBitsRows, std::max<int64_t>(1, (int64_t)heads * tq / 2048));
+    hipLaunchKernelGGL(bwd_bits_kernel, dim3((unsigned)((tq + rpw - 1) / rpw), heads), dim3(256),
+                       lds, s, sel, tq, tk, top_k, bit_words, rpw, bits, count);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   hipLaunchKernelGGL(bwd_scan_kernel, dim3(heads), dim3(256), 0, s, count, tk,
