@@ -1391,11 +1391,13 @@ hipError_t launch_tile_sparse_bwd(const uint16_t* q, int64_t nq, int64_t qst, in
                      dim3(256), 0, s, bits, nzero);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (tq > 0) {
-    const size_t lds = (size_t)(tk + bit_words) * sizeof(uint32_t);  // at most 132 KB
-    if ((err = hipFuncSetAttribute((const void*)bwd_bits_kernel,
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) !=
-        hipSuccess)
-      return err;
+    const size_t lds = (size_t)(tk + bit_words) * sizeof(uint32_t);
+    // the kernel's dynamic LDS limit, raised once per process to what the
+    // largest key range (32,768 tiles) needs: 132 KB
+    static const hipError_t lds_limit = hipFuncSetAttribute(
+        (const void*)bwd_bits_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)((32768 + 32768 / 32) * sizeof(uint32_t)));
+    if (lds_limit != hipSuccess) return lds_limit;
     // about 2,048 workgroups, at most kBitsRows rows each
     const int32_t rpw = (int32_t)std::min<int64_t>(
         kBitsRows, std::max<int64_t>(1, (int64_t)heads * tq / 2048));
