@@ -45,6 +45,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=1)
     p.add_argument("--workload", default="stack24-512v")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the per-workload stages timed after the stack")
+    p.add_argument("--extra-launches", type=int, default=20,
+                   help="timed launches per workload in the per-workload section")
     p.add_argument("--cpu-rows", type=int, default=8,
                    help="sampled (head, query tile) rows for the oracle's attention step")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -216,22 +220,16 @@ def run_gpu(args, w, torch, zb, stage_mod, synth):
             q, k, v = inputs[s]
             if kinds[s] == "sparse":
                 timer.start("sparse_stage")
-                zb.zebra_pool_landmarks(q, w.q_tile, out=sparse_bufs.qbar)
-                zb.zebra_pool_landmarks(k, w.k_tile, out=sparse_bufs.kbar)
-                zb.zebra_pool_landmarks(v, w.k_tile, out=sparse_bufs.vbar)
-                zb.zebra_select_tiles(sparse_bufs.qbar, sparse_bufs.kbar, top_k,
-                                      out=sparse_bufs.sel, workspace=sparse_bufs.select_ws)
+                stage_mod.sparse_select(q, k, v, w.q_tile, w.k_tile, top_k, sparse_bufs)
                 timer.start("sparse_attn")
-                zb.zebra_tile_sparse_attn(q, k, v, sparse_bufs.kbar, sparse_bufs.vbar,
-                                          sparse_bufs.sel, w.q_tile, w.k_tile, top_k, SCALE,
-                                          out=sparse_bufs.out, workspace=sparse_bufs.attn_ws)
+                stage_mod.sparse_attend(q, k, v, w.q_tile, w.k_tile, top_k, SCALE, sparse_bufs)
                 timer.stop("sparse_attn")
                 timer.stop("sparse_stage")
             else:
                 cal = cals[s]
                 timer.start("linear_stage")
-                zb.zebra_linear_attn(q, k, v, cal.aff_scale, cal.aff_bias, out=lin_out,
-                                     workspace=lin_ws)
+                stage_mod.linear_stage(q, k, v, cal.aff_scale, cal.aff_bias, out=lin_out,
+                                       workspace=lin_ws)
                 timer.stop("linear_stage")
 
     for _ in range(args.warmup):
@@ -258,8 +256,100 @@ def run_gpu(args, w, torch, zb, stage_mod, synth):
             n, n, w.q_tile, w.k_tile, top_k, sel)
         res["top_k"] = top_k
         res["t_k"] = t_k
+        # the first sparse stage's selection, for the parity report (outside timing)
+        s0 = min(s for s in stages if kinds[s] == "sparse")
+        stage_mod.sparse_select(*inputs[s0], w.q_tile, w.k_tile, top_k, sparse_bufs)
+        res["report_sel"] = (s0, sparse_bufs.sel.cpu().numpy())
     res["linear_bytes"] = heads * 64 * 4 * n * 2  # Q, K, V in and O out, bf16
     return res, inputs
+
+
+def _timed_launches(torch, fn, warmup, launches, flush=None):
+    """Mean and median HIP-event time (ms) of fn over `launches` calls after
+    `warmup` untimed ones; flush() (if given) runs before each call, outside
+    the events (it evicts the inputs from the 256 MB Infinity Cache)."""
+    for _ in range(warmup):
+        fn()
+    pairs = []
+    for _ in range(launches):
+        if flush is not None:
+            flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    ms = [x.elapsed_time(y) for x, y in pairs]
+    return float(np.mean(ms)), float(np.median(ms))
+
+
+def per_workload(args, torch, zb, stage_mod, synth):
+    """One stage of each single-stage workload (16 and 1,024 views sparse, 128
+    views linear) and stage 9 of the 512-view stack on the running-maximum
+    softmax path: pool+select and attention timed apart, with their rooflines.
+    Outside the step and its value."""
+    dev = torch.device("cuda", 0)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = lambda: scratch.zero_()
+    out = {}
+    for name, stage, q_mul in (("sparse-16v", 0, 1.0), ("linear-128v", 0, 1.0),
+                               ("sparse-1024v", 0, 1.0), ("stack24-512v", 9, 8.0)):
+        w = synth.WORKLOADS[name]
+        n, heads = w.n_tokens, w.heads
+        q, k, v = synth.stage_inputs(w, stage, dev)
+        key = f"{name}:{stage}" + (":fallback" if q_mul != 1.0 else "")
+        # the running-maximum leg is a comparison point: a few launches suffice
+        launches = args.extra_launches if q_mul == 1.0 else max(3, args.extra_launches // 4)
+        if w.stage_kind(stage) == "linear":
+            idx = torch.from_numpy(synth.fit_sample_indices(n, w.fit_samples,
+                                                            w.stage_seed(stage))).to(dev)
+            cal = stage_mod.calibrate_linear(q, k, v, idx, SCALE, w.k_tile)
+            o = torch.empty((heads, n, 64), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(zb.library().zebra_linear_attn_workspace(n, heads, 64),
+                             dtype=torch.uint8, device=dev)
+            mean, med = _timed_launches(
+                torch, lambda: stage_mod.linear_stage(q, k, v, cal.aff_scale, cal.aff_bias,
+                                                      out=o, workspace=ws),
+                2, launches, flush)
+            by = heads * 64 * 4 * n * 2
+            out[key] = {"views": w.n_views, "tokens": n, "stage_ms": mean, "stage_ms_median": med,
+                        "launches": launches, "bound": "hbm", "bytes_per_launch": by,
+                        "achieved": by / (mean * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": by / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS}
+            del o, ws, cal
+        else:
+            if q_mul != 1.0:
+                q = q * q_mul  # a power of two: exact in bf16, selection unchanged
+            bufs = stage_mod.SparseBuffers.allocate(heads, n, n, w.q_tile, w.k_tile, w.k, dev)
+            sel_ms, _ = _timed_launches(
+                torch, lambda: stage_mod.sparse_select(q, k, v, w.q_tile, w.k_tile, w.k, bufs),
+                2, launches, flush)
+            att_ms, att_med = _timed_launches(
+                torch, lambda: stage_mod.sparse_attend(q, k, v, w.q_tile, w.k_tile, w.k, SCALE,
+                                                       bufs),
+                1, launches, flush)
+            sel_fl, lm_fl = sparse_flops(n, n, w.q_tile, w.k_tile, w.k, bufs.sel.cpu().numpy())
+            ach = sel_fl / (att_ms * 1e-3) / 1e12
+            pool_bytes = 3 * heads * n * 64 * 2
+            out[key] = {"views": w.n_views, "tokens": n, "q_tile": w.q_tile, "k_tile": w.k_tile,
+                        "top_k": w.k, "t_k": w.t_k, "launches": launches,
+                        "stage_ms": sel_ms + att_ms, "pool_select_ms": sel_ms,
+                        "attn_ms": att_ms, "attn_ms_median": att_med, "bound": "mfma",
+                        "selected_flops": sel_fl, "landmark_flops": lm_fl, "achieved": ach,
+                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": ach / PEAK_BF16_TFLOPS,
+                        "achieved_with_landmarks": (sel_fl + lm_fl) / (att_ms * 1e-3) / 1e12,
+                        "pool_bytes": pool_bytes}
+            if q_mul != 1.0:
+                out[key]["softmax"] = (f"running maximum (queries x{q_mul:g}: every item's "
+                                       "logit bound exceeds the fixed-reference limit)")
+            del bufs
+        del q, k, v
+        torch.cuda.synchronize()
+        print(f"[bench] {key}: {json.dumps(out[key])}", file=sys.stderr, flush=True)
+    del scratch
+    return out
 
 
 def selection_quality(args, w, torch, zb, synth):
@@ -366,8 +456,10 @@ def backward(args, w, torch, zb, stage_mod, synth):
 # CPU oracle baseline on a bounded sample of the same workload
 # ----------------------------------------------------------------------------
 
-def cpu_baseline(args, w, torch, inputs, synth):
+def cpu_baseline(args, w, torch, inputs, synth, report_sel=None):
     import oracle.zebra_oracle as zo
+    sys.path.insert(0, os.path.join(os.path.dirname(os.path.abspath(__file__)), "tests"))
+    from parity_util import selection_report
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -388,6 +480,13 @@ def cpu_baseline(args, w, torch, inputs, synth):
         zo.pool_tiles(v, w.k_tile)
         sel = zo.select_tiles(qbar, kbar, w.k)
         per_head = time.perf_counter() - t0
+        if report_sel is not None and report_sel[0] == s:
+            rep = selection_report(report_sel[1][0], zo.block_scores(qbar, kbar), w.k)
+            rep.update({"stage": s, "head": 0, "top_k": w.k, "t_k": kbar.shape[0],
+                        "rule": "bit-exact except near ties (k-th and (k+1)-th oracle float64 "
+                                "scores within 1e-4 relative), where only tiles inside the "
+                                "band may swap"})
+            est["selection"] = rep
         rows = synth.sample_rows(1, qbar.shape[0], args.cpu_rows, 17)[:, 1]
         t0 = time.perf_counter()
         for i in rows:
@@ -418,11 +517,12 @@ def cpu_baseline(args, w, torch, inputs, synth):
     # the step's work: the affine fit is a one-off calibration, as on the GPU side
     total = (len(sparse_s) * est.get("sparse_stage_s", 0.0)
              + len(linear_s) * est.get("linear_stage_s", 0.0))
+    selection = est.pop("selection", None)
     return {"value": 1000.0 * total / len(stages), "unit": "ms/stage", "cores": int(threads),
             "kind": "oracle",
             "sample": "; ".join(sample) + "; scaled to all heads, query tiles and samples "
                       "(extrapolated)",
-            "per_stage_s": est}
+            "per_stage_s": est}, selection
 
 
 def main():
@@ -499,8 +599,20 @@ def main():
                            "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": achieved / PEAK_HBM_GBS, "traffic": None,
                            "bytes_per_launch": res["linear_bytes"]}
+    report_sel = res.pop("report_sel", None)
+    if w.kind == "stack" and not args.no_extra:
+        # free the stages the CPU leg does not read, then the single-stage workloads
+        keep = {min(s for s in inputs if w.stage_kind(s) == k)
+                for k in ("sparse", "linear") if any(w.stage_kind(s) == k for s in inputs)}
+        for s in list(inputs):
+            if s not in keep:
+                del inputs[s]
+        torch.cuda.empty_cache()
+        out["per_workload"] = per_workload(args, torch, zb, stage_mod, synth)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args, w, torch, inputs, synth)
+        out["cpu_baseline"], selection = cpu_baseline(args, w, torch, inputs, synth, report_sel)
+        if selection is not None:
+            out["selection"] = selection
     print(json.dumps(out), flush=True)
 
 

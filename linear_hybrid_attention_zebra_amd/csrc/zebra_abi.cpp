@@ -46,7 +46,9 @@ bool overlaps(Range a, Range b) {
 }
 
 // An output sequence must not write one element twice: the (stride, extent)
-// pairs of its three dimensions, sorted by stride, must nest.
+// pairs of its three dimensions, sorted by stride, must nest. Only dimensions
+// of extent > 1 are listed, so a zero stride among them always repeats
+// elements (it sorts first, where the nesting test alone would pass it).
 bool seq_self_disjoint(const zebra_seq& s) {
   if (seq_empty(s)) return true;
   std::vector<std::pair<int64_t, int64_t>> dims = {{1, s.head_dim}};
@@ -55,7 +57,7 @@ bool seq_self_disjoint(const zebra_seq& s) {
   std::sort(dims.begin(), dims.end());
   int64_t extent = 0;
   for (auto& d : dims) {
-    if (d.first < extent) return false;
+    if (d.first == 0 || d.first < extent) return false;
     extent = d.first * d.second;
   }
   return true;

@@ -52,6 +52,25 @@ class SparseBuffers:
         )
 
 
+def sparse_select(q, k, v, q_tile: int, k_tile: int, top_k: int,
+                  bufs: SparseBuffers) -> SparseBuffers:
+    """The first half of a tile-sparse stage: pool Q, K and V into tile means,
+    score pooled query tiles against pooled key tiles and keep top_k per row."""
+    zebra_pool_landmarks(q, q_tile, out=bufs.qbar)
+    zebra_pool_landmarks(k, k_tile, out=bufs.kbar)
+    zebra_pool_landmarks(v, k_tile, out=bufs.vbar)
+    zebra_select_tiles(bufs.qbar, bufs.kbar, top_k, out=bufs.sel, workspace=bufs.select_ws)
+    return bufs
+
+
+def sparse_attend(q, k, v, q_tile: int, k_tile: int, top_k: int, scale: float,
+                  bufs: SparseBuffers, flags: int = 0) -> SparseBuffers:
+    """The second half: tile-sparse attention over the kept tiles plus landmarks."""
+    zebra_tile_sparse_attn_ex(q, k, v, bufs.kbar, bufs.vbar, bufs.sel, q_tile, k_tile, top_k,
+                              scale, flags, out=bufs.out, workspace=bufs.attn_ws)
+    return bufs
+
+
 def sparse_stage(q, k, v, q_tile: int, k_tile: int, top_k: int, scale: float,
                  bufs: Optional[SparseBuffers] = None, flags: int = 0) -> SparseBuffers:
     """One tile-sparse stage; returns the buffers (out, sel, means) it filled.
@@ -62,13 +81,8 @@ def sparse_stage(q, k, v, q_tile: int, k_tile: int, top_k: int, scale: float,
     if bufs is None:
         bufs = SparseBuffers.allocate(q.shape[0], q.shape[1], k.shape[1], q_tile, k_tile, top_k,
                                       q.device)
-    zebra_pool_landmarks(q, q_tile, out=bufs.qbar)
-    zebra_pool_landmarks(k, k_tile, out=bufs.kbar)
-    zebra_pool_landmarks(v, k_tile, out=bufs.vbar)
-    zebra_select_tiles(bufs.qbar, bufs.kbar, top_k, out=bufs.sel, workspace=bufs.select_ws)
-    zebra_tile_sparse_attn_ex(q, k, v, bufs.kbar, bufs.vbar, bufs.sel, q_tile, k_tile, top_k,
-                              scale, flags, out=bufs.out, workspace=bufs.attn_ws)
-    return bufs
+    sparse_select(q, k, v, q_tile, k_tile, top_k, bufs)
+    return sparse_attend(q, k, v, q_tile, k_tile, top_k, scale, bufs, flags)
 
 
 def spatial_sparse_stage(q, k, v, order: torch.Tensor, q_tile: int, k_tile: int, top_k: int,

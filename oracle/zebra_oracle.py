@@ -58,9 +58,10 @@ means, so each token of tile j receives 1/n_j of its landmark's gradient.
 
 Parity status: every function on the attention path is pinned by
 ``tests/oracle_pins.py`` against closed forms, library routines or brute
-force. ``mean_attention_sparsity`` is bookkeeping, not part of the path; the
-pages' "about 79%" and "about 94%" figures pin it only weakly (leaving out
-the landmark columns also lands within one point of both).
+force. ``mean_attention_sparsity`` (bookkeeping outside the path) is pinned
+by a column-by-column count over small stacks through ``attention_columns``,
+by the paper page's Table 6 layer roles, and by the pages' "about 79%" and
+"about 94%" figures.
 """
 
 from __future__ import annotations

@@ -330,6 +330,81 @@ def pin_mean_sparsity_pages():
         assert abs(100.0 * s - p["about_percent"]) <= 1.0, f"{p}: {100 * s:.2f}%"
 
 
+def _stack_sparsity_by_count(roles, k_tile, t_k, top_k, rng, q_tiles=3):
+    """Mean over the stages of a stack of the fraction of key columns a query does
+    not attend to exactly, counted column by column. A linear stage ("L")
+    attends to no softmax column; for a tile-sparse stage ("S") every query tile
+    draws a random kept set of top_k tiles and its columns are those
+    attention_columns lists (kept tokens, then one landmark per omitted tile)."""
+    n = t_k * k_tile
+    k = rng.standard_normal((n, 4))
+    v = rng.standard_normal((n, 4))
+    per_stage = []
+    for role in roles:
+        if role == "L":
+            per_stage.append(1.0)
+            continue
+        fr = []
+        for _ in range(q_tiles):
+            kept = rng.choice(t_k, size=top_k, replace=False)
+            ck, _, _ = zo.attention_columns(k, v, k_tile, kept)
+            fr.append(1.0 - ck.shape[0] / n)
+        per_stage.append(float(np.mean(fr)))
+    return float(np.mean(per_stage))
+
+
+def pin_mean_sparsity_brute_force():
+    """The closed form equals a column-by-column count over small stacks: linear
+    stages count as fully sparse, sparse stages miss all but the kept tokens and
+    one landmark column per omitted tile."""
+    rng = np.random.default_rng(61)
+    for roles, k_tile, t_k, top_k in ((["L", "S", "S", "L"], 4, 10, 2),
+                                      (["S", "L", "L", "L", "S"], 8, 5, 3),
+                                      (["S", "S", "S"], 2, 6, 1),
+                                      (["L", "S"], 64, 10, 4)):
+        got = _stack_sparsity_by_count(roles, k_tile, t_k, top_k, rng)
+        x = roles.count("L") / len(roles)
+        ref = zo.mean_attention_sparsity(x, top_k / t_k, k_tile)
+        _close(ref, got, 1e-12, f"mean sparsity of {''.join(roles)}, tile {k_tile}, "
+                                f"{top_k} of {t_k} kept")
+
+
+def _stage_set(spec: str):
+    out = set()
+    for part in spec.split(","):
+        a, _, b = part.partition("-")
+        out.update(range(int(a), int(b or a) + 1))
+    return out
+
+
+def pin_mean_sparsity_table6_roles():
+    """The layer roles of the paper page's Table 6 partition each backbone's stages,
+    their linear fraction matches the variant's xL label, and the mean sparsity
+    counted over those actual roles (64-key tiles; 0.5L paired with 0.6S and 0.7L
+    with 0.8S, the training-free and refined settings of the synopsis) equals the
+    closed form and lands on the pages' 'about 79%' and 'about 94%'."""
+    with open(os.path.join(GOLDEN, "table6_layer_roles.json")) as f:
+        table = json.load(f)
+    about = {"0.5L": (0.6, 79), "0.7L": (0.8, 94)}
+    rng = np.random.default_rng(62)
+    for row in table["variants"]:
+        lin, sp = _stage_set(row["linear"]), _stage_set(row["sparse"])
+        n = row["n_stages"]
+        assert not (lin & sp), f"{row['backbone']} {row['variant']}: a stage has two roles"
+        assert lin | sp == set(range(n)), f"{row['backbone']} {row['variant']}: stages missing"
+        x = len(lin) / n
+        label = float(row["variant"].rstrip("L"))
+        assert abs(x - label) <= 0.05, f"{row['backbone']} {row['variant']}: linear fraction {x}"
+        y, percent = about[row["variant"]]
+        t_k = 10
+        top_k = round((1.0 - y) * t_k)
+        roles = ["L" if s in lin else "S" for s in range(n)]
+        got = _stack_sparsity_by_count(roles, 64, t_k, top_k, rng, q_tiles=2)
+        ref = zo.mean_attention_sparsity(x, top_k / t_k, 64)
+        _close(ref, got, 1e-12, f"{row['backbone']} {row['variant']} by count")
+        assert abs(100.0 * ref - percent) <= 1.0, f"{row['backbone']} {row['variant']}: {ref}"
+
+
 # ----------------------------------------------------------------------------
 # selection-quality diagnostic
 # ----------------------------------------------------------------------------
@@ -574,7 +649,8 @@ ALL_PINS = [
     pin_convexity_and_constant_values, pin_permutation_within_tile,
     pin_tiny_workload_hot_tile, pin_elu_plus_one_vs_torch, pin_linear_brute_force,
     pin_linear_closed_forms, pin_fit_vs_lstsq, pin_fit_exact_and_degenerate,
-    pin_mean_sparsity_pages, pin_block_mass_tile_one_is_softmax,
+    pin_mean_sparsity_pages, pin_mean_sparsity_brute_force, pin_mean_sparsity_table6_roles,
+    pin_block_mass_tile_one_is_softmax,
     pin_block_mass_rows_sum_to_one_and_by_hand, pin_block_mass_constant_keys,
     pin_retained_and_top_mass, pin_no_landmarks_is_attention_over_kept_tokens,
     pin_log_count_constant_tiles_is_dense, pin_log_count_unit_tiles_by_hand,

@@ -83,6 +83,49 @@ def check_selection(gpu_sel, scores, top_k: int) -> int:
     return sum(check_selection_row(g2[i], s2[i], top_k) for i in range(g2.shape[0]))
 
 
+def oracle_kept_mask(scores, top_k: int) -> np.ndarray:
+    """[R][T] boolean mask of the oracle's kept tiles for every row of scores:
+    all tiles above the k-th largest score, then the lowest-indexed tiles
+    equal to it (the tie rule of the selection)."""
+    s = np.asarray(scores, dtype=np.float64)
+    t = s.shape[1]
+    tau = np.partition(s, t - top_k, axis=1)[:, t - top_k]
+    above = s > tau[:, None]
+    ties = s == tau[:, None]
+    room = top_k - above.sum(axis=1)
+    return above | (ties & (np.cumsum(ties, axis=1) <= room[:, None]))
+
+
+def selection_report(gpu_sel, scores, top_k: int, chunk: int = 1024) -> dict:
+    """Every row of a GPU selection ([..][k]) against the oracle's float64 scores
+    ([..][T]), vectorised over rows. Returns the row count, the rows identical to
+    the oracle's, the near-tie swaps (rows that differ only inside the tie band)
+    and the mismatches (rows that differ anywhere else: a parity failure)."""
+    g = np.asarray(gpu_sel).reshape(-1, top_k).astype(np.int64)
+    s = np.asarray(scores, dtype=np.float64)
+    s = s.reshape(-1, s.shape[-1])
+    rows, t = s.shape
+    assert g.shape[0] == rows, f"{g.shape[0]} selection rows for {rows} score rows"
+    if top_k > 1:
+        assert np.all(np.diff(g, axis=1) > 0), "a selection row is not strictly ascending"
+    assert g.min() >= 0 and g.max() < t, "selection index out of range"
+    exact = near = bad = 0
+    for r0 in range(0, rows, chunk):
+        r1 = min(rows, r0 + chunk)
+        ref = oracle_kept_mask(s[r0:r1], top_k)
+        got = np.zeros_like(ref)
+        np.put_along_axis(got, g[r0:r1], True, axis=1)
+        same = (got == ref).all(axis=1)
+        exact += int(same.sum())
+        for r in np.nonzero(~same)[0]:
+            try:
+                check_selection_row(g[r0 + r], s[r0 + r], top_k)
+                near += 1
+            except AssertionError:
+                bad += 1
+    return {"rows": rows, "exact": exact, "near_tie_swaps": near, "mismatches": bad}
+
+
 def assert_grad_close(gpu, ref, what: str):
     """Gradients: relative Frobenius error <= 5e-3 and max |gpu - ref| <= 2e-2 of
     max(1, max |ref|) (their scale grows with the sequence length)."""

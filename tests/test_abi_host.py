@@ -116,6 +116,23 @@ def test_sparse_validation(lib):
     assert call(os_=seq(256, st=32)) == zb.ZEBRA_ERR_UNSUPPORTED or \
         call(os_=seq(256, st=32)) == zb.ZEBRA_ERR_INVALID_ARG  # rows overlap themselves
     assert call(dtype=7) == zb.ZEBRA_ERR_INVALID_ARG
+    # a zero stride over more than one token or head writes rows onto each other
+    assert call(os_=seq(256, st=0)) == zb.ZEBRA_ERR_INVALID_ARG
+    assert call(os_=seq(256, sh=0)) == zb.ZEBRA_ERR_INVALID_ARG
+    assert call(os_=seq(256, st=0, sh=0)) == zb.ZEBRA_ERR_INVALID_ARG
+
+
+def test_zero_stride_outputs_rejected_everywhere(lib):
+    """Every entry point that writes a token sequence rejects an output whose
+    token or head stride is zero over an extent above one (rows would collide)."""
+    s = seq(300)
+    lin_ws = lib.zebra_linear_attn_workspace(300, 2, 64)
+    for bad in (seq(300, st=0), seq(300, sh=0)):
+        assert lib.zebra_linear_attn(P(1 << 16), s, P(1 << 18), P(1 << 20), s, None, None,
+                                     P(1 << 28), bad, 0, P(1 << 30), lin_ws, None) == \
+            zb.ZEBRA_ERR_INVALID_ARG
+        assert lib.zebra_permute_tokens(P(1 << 16), s, P(1 << 24), 0, 0, P(1 << 28), bad,
+                                        None) == zb.ZEBRA_ERR_INVALID_ARG
 
 
 def test_sparse_variant_flags_validation(lib):

@@ -20,7 +20,7 @@ import oracle.zebra_oracle as zo
 import linear_hybrid_attention_zebra_amd as zb
 from linear_hybrid_attention_zebra_amd import stage as stage_mod
 from linear_hybrid_attention_zebra_amd import synth
-from parity_util import assert_close, check_selection_row, to_f64
+from parity_util import assert_close, check_selection_row, selection_report, to_f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -59,6 +59,49 @@ def test_full_size_sparse_stage_sampled(name, stage):
             ref = zo.tile_sparse_attention_tile(qh[s0:e0], kh, vh, w.k_tile, gsel, SCALE)
             assert_close(bufs.out[h, s0:e0], ref, f"{name} stage {stage} head {h} tile {i}")
     print(f"[parity] near-tie swaps {swaps} of {len(rows)} sampled rows", flush=True)
+
+
+def test_whole_16_view_stage_every_row_and_element():
+    """The whole 16-view sparse stage (21,984 tokens, 16 heads, 344 query tiles
+    with a 32-token last tile): every selection row of every head against the
+    oracle's float64 pooled scores, and every output element against the oracle
+    run on the GPU's selection."""
+    w = synth.WORKLOADS["sparse-16v"]
+    print(f"[case] whole sparse-16v stage: N={w.n_tokens} H={w.heads} top_k={w.k}", flush=True)
+    q, k, v = synth.stage_inputs(w, 0, DEV)
+    bufs = stage_mod.sparse_stage(q, k, v, w.q_tile, w.k_tile, w.k, SCALE)
+    torch.cuda.synchronize()
+    sel = bufs.sel.cpu().numpy()
+    qn, kn, vn = (t.to("cpu", torch.float64).numpy() for t in (q, k, v))
+    scores = np.stack([zo.block_scores(zo.pool_tiles(qn[h], w.q_tile),
+                                       zo.pool_tiles(kn[h], w.k_tile)) for h in range(w.heads)])
+    rep = selection_report(sel, scores, w.k)
+    print(f"[parity] sparse-16v selection: {rep}", flush=True)
+    assert rep["rows"] == w.heads * w.t_q and rep["mismatches"] == 0
+    ref, _ = zo.tile_sparse_attention(qn, kn, vn, w.q_tile, w.k_tile, w.k, SCALE, sel=sel)
+    assert_close(bufs.out, ref, "sparse-16v, every element of every head")
+
+
+WHOLE_HEAD = [("stack24-512v", 9, 3), ("sparse-1024v", 0, 12)]
+
+
+@pytest.mark.parametrize("name,stage,head", WHOLE_HEAD, ids=[f"{n}:{s}" for n, s, _ in WHOLE_HEAD])
+def test_full_size_selection_whole_head(name, stage, head):
+    """Every selection row of one whole head at full size against the oracle's
+    float64 pooled scores of that head (10,992 rows of 10,992 or 21,984 scores)."""
+    w = synth.WORKLOADS[name]
+    print(f"[case] whole-head selection {name} stage {stage} head {head}: T_q={w.t_q} "
+          f"T_k={w.t_k} top_k={w.k}", flush=True)
+    q, k, v = synth.stage_inputs(w, stage, DEV)
+    bufs = stage_mod.SparseBuffers.allocate(w.heads, w.n_tokens, w.n_tokens, w.q_tile, w.k_tile,
+                                            w.k, DEV)
+    stage_mod.sparse_select(q, k, v, w.q_tile, w.k_tile, w.k, bufs)
+    torch.cuda.synchronize()
+    qbar = zo.pool_tiles(_head(q, head), w.q_tile)
+    kbar = zo.pool_tiles(_head(k, head), w.k_tile)
+    rep = selection_report(bufs.sel[head].cpu().numpy(), zo.block_scores(qbar, kbar), w.k)
+    print(f"[parity] {name} stage {stage} head {head} selection: {rep}", flush=True)
+    assert rep["rows"] == w.t_q and rep["mismatches"] == 0
 
 
 def test_full_size_sparse_stage_is_deterministic():

@@ -608,6 +608,33 @@ def test_sparse_backward_parity(case, g_dtype):
     assert_grad_close(dv, rv, f"sparse dv {case}")
 
 
+def test_sparse_backward_multirow_bits_partial_group():
+    """dk and dv through the kept-tile bit matrix built several query tiles per
+    workgroup: 16 heads x 283 query tiles of 32 (4,528 rows) give 2 rows per
+    workgroup with a last group of one row, and an LDS histogram of per-key-tile
+    counts per workgroup. One whole head against the oracle, all three gradients."""
+    heads, q_tile, k_tile, n, top_k = 16, 32, 64, 9050, 29
+    print(f"[case] sparse backward multirow bits: H={heads} N={n} tiles {q_tile}x{k_tile} "
+          f"top_k={top_k}", flush=True)
+    q, k, v = _clustered(9050, heads, n, n, q_tile, k_tile, 3)
+    rng = np.random.default_rng(9051)
+    dout = synth.bf16_round(rng.standard_normal((heads, n, 64)).astype(np.float32))
+    qg, kg, vg = bf16_gpu(q), bf16_gpu(k), bf16_gpu(v)
+    bufs = stage.sparse_stage(qg, kg, vg, q_tile, k_tile, top_k, 0.125)
+    dq, dk, dv = zb.zebra_tile_sparse_attn_backward(
+        qg, kg, vg, bufs.kbar, bufs.vbar, bufs.sel, q_tile, k_tile, top_k, 0.125,
+        torch.from_numpy(dout).to(DEV))
+    torch.cuda.synchronize()
+    sel = bufs.sel.cpu().numpy()
+    for h in (0, 11):
+        rq, rk, rv = zo.tile_sparse_attention_backward(q[h:h + 1], k[h:h + 1], v[h:h + 1],
+                                                       q_tile, k_tile, sel[h:h + 1], 0.125,
+                                                       dout[h:h + 1])
+        assert_grad_close(dq[h], rq[0], f"multirow bits dq head {h}")
+        assert_grad_close(dk[h], rk[0], f"multirow bits dk head {h}")
+        assert_grad_close(dv[h], rv[0], f"multirow bits dv head {h}")
+
+
 def test_sparse_backward_running_max_path_and_determinism():
     """Query tiles with a loose logit bound (the forward's running-maximum path)
     and bitwise-equal gradients on a second call."""

@@ -228,6 +228,19 @@ def _linear_bwd_with(no_dphi=False, dden_sign=False, no_db=False):
     return bwd
 
 
+def _sparsity_without_landmarks(linear_frac, keep_frac, k_tile):
+    return linear_frac + (1.0 - linear_frac) * (1.0 - keep_frac)
+
+
+def _sparsity_linear_as_dense(linear_frac, keep_frac, k_tile):
+    return (1.0 - linear_frac) * (1.0 - keep_frac - (1.0 - keep_frac) / k_tile)
+
+
+def _sparsity_landmark_per_key(linear_frac, keep_frac, k_tile):
+    dense = keep_frac + (1.0 - keep_frac)
+    return linear_frac + (1.0 - linear_frac) * (1.0 - dense)
+
+
 def _top_mass_lowest(mass, top_k):
     m = np.asarray(mass, np.float64)
     return np.sort(m, axis=1)[:, :top_k].sum(axis=1)
@@ -254,6 +267,12 @@ MUTATIONS = {
     "block mass drops the last key tile": ("block_attention_mass",
                                            _mass_with(skip_last_tile=True)),
     "top mass takes the lowest blocks": ("top_mass", _top_mass_lowest),
+    "mean sparsity drops the landmark columns": ("mean_attention_sparsity",
+                                                  _sparsity_without_landmarks),
+    "mean sparsity counts linear stages as dense": ("mean_attention_sparsity",
+                                                     _sparsity_linear_as_dense),
+    "mean sparsity counts a landmark per key": ("mean_attention_sparsity",
+                                                _sparsity_landmark_per_key),
     "landmark switch ignored": ("attention_columns", _columns_with(ignore_switch=True)),
     "landmark count in base 2": ("attention_columns", _columns_with(count_base2=True)),
     "landmark count ignores the short last tile": ("attention_columns",
