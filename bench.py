@@ -553,6 +553,7 @@ def main():
         backward(args, w, torch, zb, stage_mod, synth)
         return
     res, inputs = run_gpu(args, w, torch, zb, stage_mod, synth)
+    report_sel = res.pop("report_sel", None)
     print(f"[bench] gpu done: {json.dumps(res)}", file=sys.stderr, flush=True)
 
     ms_per_step = 1000.0 * res["wall_s"] / args.steps
@@ -599,7 +600,6 @@ def main():
                            "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": achieved / PEAK_HBM_GBS, "traffic": None,
                            "bytes_per_launch": res["linear_bytes"]}
-    report_sel = res.pop("report_sel", None)
     if w.kind == "stack" and not args.no_extra:
         # free the stages the CPU leg does not read, then the single-stage workloads
         keep = {min(s for s in inputs if w.stage_kind(s) == k)
