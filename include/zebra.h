@@ -184,6 +184,30 @@ zebra_status zebra_linear_attn(const void* q, zebra_seq qs, const void* k, const
                                size_t workspace_bytes, void* stream);
 
 /*
+ * zebra_linear_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops or
+ * harnesses that forbid hipMalloc). Same arguments, kernels and results as
+ * zebra_linear_attn (bitwise), except that the partial and folded states live
+ * in a fixed device array of zebra_linear_attn_noalloc_max_bytes() bytes
+ * (40 MiB) that the library holds on each GPU it runs on until the process
+ * ends; its device address is taken once per device on the first call there.
+ * The call allocates nothing and frees nothing.
+ *
+ * Limit: zebra_linear_attn_workspace(Nk, H, 64) must not exceed that size
+ * (true for up to 64 heads at any length); otherwise ZEBRA_ERR_WORKSPACE,
+ * before any HIP call. Every call on one GPU shares that GPU's array and the
+ * kernels overwrite it entirely (nothing must start at zero); calls that
+ * overlap in time on one GPU (two streams, two threads) race on it and must
+ * be serialised by the caller. ZEBRA_ERR_HIP if the array's address cannot be
+ * taken on the current device.
+ */
+size_t zebra_linear_attn_noalloc_max_bytes(void);
+zebra_status zebra_linear_attn_noalloc(const void* q, zebra_seq qs, const void* k, const void* v,
+                                       zebra_seq kvs, const float* aff_scale,
+                                       const float* aff_bias, void* o, zebra_seq os,
+                                       zebra_dtype o_dtype, void* stream);
+
+/*
  * Closed-form affine fit (news.hamidun.com article, "How Zebra3D works": the
  * linear components are fitted by a closed-form affine map, no gradient
  * descent). Per (head h, channel c), over the m samples:

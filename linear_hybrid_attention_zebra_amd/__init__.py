@@ -77,6 +77,9 @@ def _declare(lib):
         "zebra_linear_attn_workspace": (c_sz, [c_i64, c_i32, c_i32]),
         "zebra_linear_attn": (c_i32, [c_p, ZebraSeq, c_p, c_p, ZebraSeq, c_p, c_p, c_p, ZebraSeq,
                                       c_i32, c_p, c_sz, c_p]),
+        "zebra_linear_attn_noalloc_max_bytes": (c_sz, []),
+        "zebra_linear_attn_noalloc": (c_i32, [c_p, ZebraSeq, c_p, c_p, ZebraSeq, c_p, c_p, c_p,
+                                              ZebraSeq, c_i32, c_p]),
         "zebra_fit_affine": (c_i32, [c_p, c_p, c_i32, c_i32, c_i32, c_p, c_p, c_p, c_p]),
         "zebra_fit_scale_only": (c_i32, [c_p, c_p, c_i32, c_i32, c_i32, c_p, c_p, c_p, c_p]),
         "zebra_block_mass_workspace": (c_sz, [c_i64, c_i32]),
@@ -280,6 +283,31 @@ def zebra_linear_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _ptr(q), seq_of(q), _ptr(k), _ptr(v), seq_of(k), _ptr(aff_scale), _ptr(aff_bias),
         _ptr(out), seq_of(out), ZEBRA_F32 if out.dtype == torch.float32 else ZEBRA_BF16,
         _ptr(workspace), nbytes, _stream(q.device)))
+    return out
+
+
+def zebra_linear_attn_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                              aff_scale: Optional[torch.Tensor] = None,
+                              aff_bias: Optional[torch.Tensor] = None,
+                              out: Optional[torch.Tensor] = None,
+                              out_dtype=torch.bfloat16) -> torch.Tensor:
+    """zebra_linear_attn with the library's fixed device scratch instead of a
+    workspace (the C call allocates nothing; pass `out` to allocate nothing here)."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, name)
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k and v must share shape and strides")
+    for t, name in ((aff_scale, "aff_scale"), (aff_bias, "aff_bias")):
+        if t is not None:
+            _need(t, torch.float32, name)
+            if not t.is_contiguous() or t.numel() != q.shape[0] * HEAD_DIM:
+                raise ValueError(f"{name} must be a contiguous [H][64] float32 tensor")
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    _check("zebra_linear_attn_noalloc", library().zebra_linear_attn_noalloc(
+        _ptr(q), seq_of(q), _ptr(k), _ptr(v), seq_of(k), _ptr(aff_scale), _ptr(aff_bias),
+        _ptr(out), seq_of(out), ZEBRA_F32 if out.dtype == torch.float32 else ZEBRA_BF16,
+        _stream(q.device)))
     return out
 
 

@@ -313,6 +313,43 @@ zebra_status zebra_linear_attn(const void* q, zebra_seq qs, const void* k, const
       (hipStream_t)stream));
 }
 
+size_t zebra_linear_attn_noalloc_max_bytes(void) { return zebra::kNoAllocScratchBytes; }
+
+zebra_status zebra_linear_attn_noalloc(const void* q, zebra_seq qs, const void* k, const void* v,
+                                       zebra_seq kvs, const float* aff_scale,
+                                       const float* aff_bias, void* o, zebra_seq os,
+                                       zebra_dtype o_dtype, void* stream) {
+  zebra_status st;
+  if ((st = check_seq(q, qs, false)) != ZEBRA_OK) return st;
+  if ((st = check_seq(k, kvs, false)) != ZEBRA_OK) return st;
+  if ((st = check_seq(v, kvs, false)) != ZEBRA_OK) return st;
+  if ((st = check_seq(o, os, true)) != ZEBRA_OK) return st;
+  if (o_dtype != ZEBRA_BF16 && o_dtype != ZEBRA_F32) return ZEBRA_ERR_INVALID_ARG;
+  if (qs.n_heads != kvs.n_heads || os.n_heads != qs.n_heads || os.n_tokens != qs.n_tokens)
+    return ZEBRA_ERR_INVALID_ARG;
+  if (seq_empty(qs)) return ZEBRA_OK;
+  if (kvs.n_tokens == 0) return ZEBRA_ERR_INVALID_ARG;
+  const size_t need = zebra::linear_workspace_bytes(kvs.n_tokens, kvs.n_heads);
+  if (need > zebra::kNoAllocScratchBytes) return ZEBRA_ERR_WORKSPACE;  // too many heads
+  if (((uintptr_t)aff_scale % 4) != 0 || ((uintptr_t)aff_bias % 4) != 0)
+    return ZEBRA_ERR_INVALID_ARG;
+  if (o_dtype == ZEBRA_F32 && (os.stride_token % 8 != 0 || os.stride_head % 8 != 0))
+    return ZEBRA_ERR_UNSUPPORTED;
+  const Range orng = seq_range(o, os, o_dtype == ZEBRA_F32 ? 4 : 2);
+  const uint64_t aff_n = (uint64_t)qs.n_heads * zebra::kHeadDim;
+  const Range inputs[] = {seq_range(q, qs, 2), seq_range(k, kvs, 2), seq_range(v, kvs, 2),
+                          flat_range(aff_scale, aff_n, 4), flat_range(aff_bias, aff_n, 4)};
+  for (const Range& r : inputs)
+    if (overlaps(orng, r)) return ZEBRA_ERR_INVALID_ARG;
+  void* scratch = nullptr;
+  if (zebra::noalloc_scratch(&scratch) != hipSuccess) return ZEBRA_ERR_HIP;
+  return hip_status(zebra::launch_linear(
+      (const uint16_t*)q, qs.n_tokens, qs.stride_token, qs.stride_head, (const uint16_t*)k,
+      (const uint16_t*)v, kvs.n_tokens, kvs.stride_token, kvs.stride_head, qs.n_heads,
+      aff_scale, aff_bias, o, os.stride_token, os.stride_head, o_dtype == ZEBRA_F32, scratch,
+      (hipStream_t)stream));
+}
+
 namespace {
 
 zebra_status fit_common(const float* x, const float* y, int32_t m, int32_t n_heads,
