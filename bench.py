@@ -49,6 +49,13 @@ def parse():
                    help="skip the per-workload stages timed after the stack")
     p.add_argument("--extra-launches", type=int, default=20,
                    help="timed launches per workload in the per-workload section")
+    p.add_argument("--single-stage", type=int, default=None, metavar="S",
+                   help="only time stage S of the workload on its own (pool+select and "
+                        "attention apart, --steps launches after --warmup) and exit; the "
+                        "command the committed kernel profiles are taken with")
+    p.add_argument("--fallback", action="store_true",
+                   help="with --single-stage: queries x8, so every item takes the "
+                        "running-maximum softmax path")
     p.add_argument("--cpu-rows", type=int, default=8,
                    help="sampled (head, query tile) rows for the oracle's attention step")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -284,69 +291,73 @@ def _timed_launches(torch, fn, warmup, launches, flush=None):
     return float(np.mean(ms)), float(np.median(ms))
 
 
+def time_stage(args, torch, zb, stage_mod, synth, name, stage, q_mul, launches, flush):
+    """One stage of a workload timed on its own (pool+select and attention apart
+    for a sparse stage), with its roofline. q_mul scales the queries (a power
+    of two: exact in bf16, the selection unchanged) to push every item past the
+    fixed-reference bound onto the running-maximum softmax path."""
+    dev = torch.device("cuda", 0)
+    w = synth.WORKLOADS[name]
+    n, heads = w.n_tokens, w.heads
+    q, k, v = synth.stage_inputs(w, stage, dev)
+    if w.stage_kind(stage) == "linear":
+        idx = torch.from_numpy(synth.fit_sample_indices(n, w.fit_samples,
+                                                        w.stage_seed(stage))).to(dev)
+        cal = stage_mod.calibrate_linear(q, k, v, idx, SCALE, w.k_tile)
+        o = torch.empty((heads, n, 64), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(zb.library().zebra_linear_attn_workspace(n, heads, 64),
+                         dtype=torch.uint8, device=dev)
+        mean, med = _timed_launches(
+            torch, lambda: stage_mod.linear_stage(q, k, v, cal.aff_scale, cal.aff_bias, out=o,
+                                                  workspace=ws),
+            2, launches, flush)
+        by = heads * 64 * 4 * n * 2
+        return {"views": w.n_views, "tokens": n, "stage_ms": mean, "stage_ms_median": med,
+                "launches": launches, "bound": "hbm", "bytes_per_launch": by,
+                "achieved": by / (mean * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": by / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    if q_mul != 1.0:
+        q = q * q_mul
+    bufs = stage_mod.SparseBuffers.allocate(heads, n, n, w.q_tile, w.k_tile, w.k, dev)
+    sel_ms, _ = _timed_launches(
+        torch, lambda: stage_mod.sparse_select(q, k, v, w.q_tile, w.k_tile, w.k, bufs),
+        min(2, args.warmup + 1), launches, flush)
+    att_ms, att_med = _timed_launches(
+        torch, lambda: stage_mod.sparse_attend(q, k, v, w.q_tile, w.k_tile, w.k, SCALE, bufs),
+        min(1, args.warmup), launches, flush)
+    sel_fl, lm_fl = sparse_flops(n, n, w.q_tile, w.k_tile, w.k, bufs.sel.cpu().numpy())
+    ach = sel_fl / (att_ms * 1e-3) / 1e12
+    out = {"views": w.n_views, "tokens": n, "q_tile": w.q_tile, "k_tile": w.k_tile,
+           "top_k": w.k, "t_k": w.t_k, "launches": launches,
+           "stage_ms": sel_ms + att_ms, "pool_select_ms": sel_ms,
+           "attn_ms": att_ms, "attn_ms_median": att_med, "bound": "mfma",
+           "selected_flops": sel_fl, "landmark_flops": lm_fl, "achieved": ach,
+           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+           "achieved_with_landmarks": (sel_fl + lm_fl) / (att_ms * 1e-3) / 1e12,
+           "pool_bytes": 3 * heads * n * 64 * 2}
+    if q_mul != 1.0:
+        out["softmax"] = (f"running maximum (queries x{q_mul:g}: every item's logit bound "
+                          "exceeds the fixed-reference limit)")
+    return out
+
+
 def per_workload(args, torch, zb, stage_mod, synth):
     """One stage of each single-stage workload (16 and 1,024 views sparse, 128
     views linear) and stage 9 of the 512-view stack on the running-maximum
     softmax path: pool+select and attention timed apart, with their rooflines.
     Outside the step and its value."""
-    dev = torch.device("cuda", 0)
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    flush = lambda: scratch.zero_()
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = lambda: scratch.zero_()  # evicts the inputs from the 256 MB Infinity Cache
     out = {}
     for name, stage, q_mul in (("sparse-16v", 0, 1.0), ("linear-128v", 0, 1.0),
                                ("sparse-1024v", 0, 1.0), ("stack24-512v", 9, 8.0)):
-        w = synth.WORKLOADS[name]
-        n, heads = w.n_tokens, w.heads
-        q, k, v = synth.stage_inputs(w, stage, dev)
         key = f"{name}:{stage}" + (":fallback" if q_mul != 1.0 else "")
         # the running-maximum leg is a comparison point: a few launches suffice
         launches = args.extra_launches if q_mul == 1.0 else max(3, args.extra_launches // 4)
-        if w.stage_kind(stage) == "linear":
-            idx = torch.from_numpy(synth.fit_sample_indices(n, w.fit_samples,
-                                                            w.stage_seed(stage))).to(dev)
-            cal = stage_mod.calibrate_linear(q, k, v, idx, SCALE, w.k_tile)
-            o = torch.empty((heads, n, 64), dtype=torch.bfloat16, device=dev)
-            ws = torch.empty(zb.library().zebra_linear_attn_workspace(n, heads, 64),
-                             dtype=torch.uint8, device=dev)
-            mean, med = _timed_launches(
-                torch, lambda: stage_mod.linear_stage(q, k, v, cal.aff_scale, cal.aff_bias,
-                                                      out=o, workspace=ws),
-                2, launches, flush)
-            by = heads * 64 * 4 * n * 2
-            out[key] = {"views": w.n_views, "tokens": n, "stage_ms": mean, "stage_ms_median": med,
-                        "launches": launches, "bound": "hbm", "bytes_per_launch": by,
-                        "achieved": by / (mean * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                        "unit": "GB/s", "frac": by / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS}
-            del o, ws, cal
-        else:
-            if q_mul != 1.0:
-                q = q * q_mul  # a power of two: exact in bf16, selection unchanged
-            bufs = stage_mod.SparseBuffers.allocate(heads, n, n, w.q_tile, w.k_tile, w.k, dev)
-            sel_ms, _ = _timed_launches(
-                torch, lambda: stage_mod.sparse_select(q, k, v, w.q_tile, w.k_tile, w.k, bufs),
-                2, launches, flush)
-            att_ms, att_med = _timed_launches(
-                torch, lambda: stage_mod.sparse_attend(q, k, v, w.q_tile, w.k_tile, w.k, SCALE,
-                                                       bufs),
-                1, launches, flush)
-            sel_fl, lm_fl = sparse_flops(n, n, w.q_tile, w.k_tile, w.k, bufs.sel.cpu().numpy())
-            ach = sel_fl / (att_ms * 1e-3) / 1e12
-            pool_bytes = 3 * heads * n * 64 * 2
-            out[key] = {"views": w.n_views, "tokens": n, "q_tile": w.q_tile, "k_tile": w.k_tile,
-                        "top_k": w.k, "t_k": w.t_k, "launches": launches,
-                        "stage_ms": sel_ms + att_ms, "pool_select_ms": sel_ms,
-                        "attn_ms": att_ms, "attn_ms_median": att_med, "bound": "mfma",
-                        "selected_flops": sel_fl, "landmark_flops": lm_fl, "achieved": ach,
-                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                        "frac": ach / PEAK_BF16_TFLOPS,
-                        "achieved_with_landmarks": (sel_fl + lm_fl) / (att_ms * 1e-3) / 1e12,
-                        "pool_bytes": pool_bytes}
-            if q_mul != 1.0:
-                out[key]["softmax"] = (f"running maximum (queries x{q_mul:g}: every item's "
-                                       "logit bound exceeds the fixed-reference limit)")
-            del bufs
-        del q, k, v
+        out[key] = time_stage(args, torch, zb, stage_mod, synth, name, stage, q_mul, launches,
+                              flush)
         torch.cuda.synchronize()
+        torch.cuda.empty_cache()
         print(f"[bench] {key}: {json.dumps(out[key])}", file=sys.stderr, flush=True)
     del scratch
     return out
@@ -551,6 +562,12 @@ def main():
         return
     if args.backward:
         backward(args, w, torch, zb, stage_mod, synth)
+        return
+    if args.single_stage is not None:
+        res = time_stage(args, torch, zb, stage_mod, synth, w.name, args.single_stage,
+                         8.0 if args.fallback else 1.0, max(1, args.steps), None)
+        print(json.dumps({"single_stage": {"workload": w.name, "stage": args.single_stage,
+                                           **res}}), flush=True)
         return
     res, inputs = run_gpu(args, w, torch, zb, stage_mod, synth)
     report_sel = res.pop("report_sel", None)
