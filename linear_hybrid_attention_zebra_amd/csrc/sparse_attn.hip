@@ -148,6 +148,14 @@ __device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t r,
                                               uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
 }
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), in order
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(static_cast<F&&>(f));
+  }
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -950,6 +958,11 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
   // the workgroup. Piece u covers rows 8 u + lane / 8, lane chunk
   // (lane % 8) ^ swz_f(row).
   constexpr bool kOwnHalf = W == 2;
+  // blocks in flight ahead of use: with own-half staging a wave refills the
+  // ring stage it has just read (its own rows only) with the blocks two steps
+  // ahead, once its reads of that stage have completed; with four waves the
+  // stages are shared and each is refilled one step ahead behind a barrier
+  constexpr int kAhead = kOwnHalf ? 2 : 1;
   const int lrow = lane >> 3;
   auto piece = [&](int v) { return kOwnHalf ? 4 * kh + v : wave + W * v; };
   // (key/value rows are 128 bytes apart here, like landmark rows)
@@ -1084,7 +1097,8 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
       }
       return block_rsrc(base, rows * 128);
     };
-    auto fire = [&](const Src& src, lds_blk* dst, int v) {
+    auto fire = [&](const Src& src, lds_blk* dst, auto v_c) {
+      constexpr int v = decltype(v_c)::value;
       buffer_to_lds(src, (__attribute__((address_space(3))) void*)&dst[piece(v)][0], off_v[v]);
     };
     auto block_mask = [&](int t) -> uint64_t {
@@ -1236,6 +1250,11 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         bf16x8(&pw)[2][2] = pbuf(par);
         bf16x8(&pr)[2][2] = pbuf(R{});
         read_v(R{}, va);  // V(t-1)
+        if constexpr (kAhead == 2) {
+          // K(t+1) too: stage R is refilled below once both reads are done
+#pragma unroll
+          for (int s = 0; s < 4; ++s) read_k1(R{}, ka, s);
+        }
         if constexpr (kMasked) {
           if (tail_col >= 0) add_col(sacc, tail_col, p.lm_tail_corr);
           apply_mask(sacc, cmask);
@@ -1254,26 +1273,42 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         job(0);
         job(1);
         if constexpr (kFast) __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {  // slots 1-8: PV(t-1)
-          const int qh = j >> 2, m = (j >> 1) & 1, db = j & 1;
+        static_for<8>([&](auto jc) {  // slots 1-8: PV(t-1)
+          constexpr int j = decltype(jc)::value;
+          constexpr int qh = j >> 2, m = (j >> 1) & 1, db = j & 1;
           oacc[qh][db] = mfma32(as_bf16x8(va[m][db]), pr[qh][m], oacc[qh][db]);
           job(2 + j);
-          if (j < 2) {
-            read_k1(R{}, ka, 2 * j);  // K(t+1); past the end a repeated block
-            read_k1(R{}, ka, 2 * j + 1);
-          }
-          constexpr int kPer = (2 * NU + 7) / 8;
-#pragma unroll
-          for (int k = 0; k < kPer; ++k) {
-            const int q = j * kPer + k;
-            if (q < NU)
-              fire(sk, kbuf(par), q);
-            else if (q < 2 * NU)
-              fire(sv, vbuf(par), q - NU);
+          if constexpr (kAhead == 2) {
+            // K(t+3) and V(t+1) into stage R, whose reads (V(t-1), K(t+1))
+            // must have completed first: an LDS write by a global load is not
+            // ordered after LDS reads still in flight
+            if constexpr (j == 2) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            static_assert(NU == 4, "own-half staging: 4 pieces per tensor");
+            constexpr int q0 = j < 2 ? 8 : (j < 4 ? 2 * (j - 2) : j);
+            constexpr int nq = j < 2 ? 0 : (j < 4 ? 2 : 1);
+            static_for<nq>([&](auto kc) {
+              constexpr int q = q0 + decltype(kc)::value;
+              if constexpr (q < NU)
+                fire(sk, kbuf(R{}), std::integral_constant<int, q>{});
+              else
+                fire(sv, vbuf(R{}), std::integral_constant<int, q - NU>{});
+            });
+          } else {
+            if constexpr (j < 2) {
+              read_k1(R{}, ka, 2 * j);  // K(t+1); past the end a repeated block
+              read_k1(R{}, ka, 2 * j + 1);
+            }
+            constexpr int kPer = (2 * NU + 7) / 8;
+            static_for<kPer>([&](auto kc) {
+              constexpr int q = j * kPer + decltype(kc)::value;
+              if constexpr (q < NU)
+                fire(sk, kbuf(par), std::integral_constant<int, q>{});
+              else if constexpr (q < 2 * NU)
+                fire(sv, vbuf(par), std::integral_constant<int, q - NU>{});
+            });
           }
           if constexpr (kFast) __builtin_amdgcn_sched_barrier(0);
-        }
+        });
         if constexpr (!kFast) {
           if (moved) {
 #pragma unroll
@@ -1307,17 +1342,29 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         keep_vgpr(l_run[1]);
       };
       auto step = [&](int t, auto par, auto masked_c) {
-        wait_vmcnt<0>();
+        // the blocks read in this step were issued kAhead steps ago; the
+        // kAhead - 1 newer steps' loads (2 NU each) may stay in flight
+        wait_vmcnt<2 * NU * (kAhead - 1)>();
         step_sync();
-        const int tkn = min(t + 2, n_total - 1);
-        const int tvn = max(min(t, n_total - 1), 0);
+        if constexpr (decltype(masked_c)::value == 2) {
+          // streaming step: 0 <= t < n_kept - 2 - kAhead, so K(t + 1 + kAhead)
+          // and V(t + kAhead - 1) are whole kept tiles (the short last tile is
+          // at most the last kept one) and the whole kept list is in the window
+          const int jk = dense ? t + 1 + kAhead
+                               : __builtin_amdgcn_readfirstlane(win[t + 1 + kAhead]);
+          const int jv = dense ? t + kAhead - 1
+                               : __builtin_amdgcn_readfirstlane(win[t + kAhead - 1]);
+          const Src sk = block_rsrc(khp + (int64_t)jk * (KT * 128), KT * 128);
+          const Src sv = block_rsrc(vhp + (int64_t)jv * (KT * 128), KT * 128);
+          body(par, std::false_type{}, 0ull, 0.f, -1, sk, sv);
+        } else {
+        const int tkn = min(t + 1 + kAhead, n_total - 1);
+        const int tvn = max(min(t + kAhead - 1, n_total - 1), 0);
         ensure_window(tvn, tkn);
         const Src sk = prep(tkn, khp, klm), sv = prep(tvn, vhp, vlm);
         if (t < 0) {
-#pragma unroll
-          for (int v = 0; v < NU; ++v) fire(sk, kbuf(par), v);
-#pragma unroll
-          for (int v = 0; v < NU; ++v) fire(sv, vbuf(par), v);
+          static_for<NU>([&](auto vc) { fire(sk, kbuf(par), vc); });
+          static_for<NU>([&](auto vc) { fire(sv, vbuf(par), vc); });
         }
         if (t == -1) {
           bf16x8 ka[4];
@@ -1327,7 +1374,7 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
           qk_q(ka, sacc[1], 1);
         }
         if (t < 0) return;
-        if constexpr (decltype(masked_c)::value) {
+        if constexpr (decltype(masked_c)::value == 1) {
           const bool lm = t >= n_kept;
           const int tcol = lm && log_count && lb0 + t - n_kept == n_lb_all - 1 && tail_rows < KT
                                ? last_lrows - 1
@@ -1335,6 +1382,7 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
           body(par, masked_c, block_mask(t), lm ? lm_shift : 0.f, tcol, sk, sv);
         } else {
           body(par, masked_c, 0ull, 0.f, -1, sk, sv);
+        }
         }
       };
       auto drain = [&](auto par) {  // PV of the last block
@@ -1354,9 +1402,42 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
       using Plain = std::false_type;
       using Masked = std::true_type;
       const int n_plain = last_rows < KT ? n_kept - 1 : n_kept;
-      step(-2, P0{}, Plain{});
-      step(-1, P1{}, Plain{});
+      using Stream = std::integral_constant<int, 2>;
+      // streaming steps need the whole kept list in the window (then it
+      // starts at entry 0 and never moves)
+      // (own-half staging only: with four waves the shared stages and their
+      // barriers set the pace, and the straight-line step measured slower)
+      const int n_stream =
+          kOwnHalf && (dense || n_kept <= kWin) ? max(n_kept - 2 - kAhead, 0) : 0;
+      if constexpr (kAhead == 2) {
+        // K(0) -> stage 0, K(1) -> stage 1, and V(0) -> V stage 1 as a finite
+        // stand-in for the absent V(-1) (its probabilities P(-1) are zero);
+        // QK(0) once K(0) has landed; then K(2) -> stage 0 and V(0) -> V stage 0
+        ensure_window(0, min(2, n_total - 1));
+        const Src k0 = prep(0, khp, klm), k1 = prep(min(1, n_total - 1), khp, klm);
+        const Src v0 = prep(0, vhp, vlm);
+        static_for<NU>([&](auto vc) { fire(k0, kbuf(P0{}), vc); });
+        static_for<NU>([&](auto vc) { fire(k1, kbuf(P1{}), vc); });
+        static_for<NU>([&](auto vc) { fire(v0, vbuf(P1{}), vc); });
+        wait_vmcnt<2 * NU>();
+        bf16x8 ka[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) read_k1(P0{}, ka, s);
+        qk_q(ka, sacc[0], 0);  // QK(0)
+        qk_q(ka, sacc[1], 1);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const Src k2 = prep(min(2, n_total - 1), khp, klm);
+        static_for<NU>([&](auto vc) { fire(k2, kbuf(P0{}), vc); });
+        static_for<NU>([&](auto vc) { fire(v0, vbuf(P0{}), vc); });
+      } else {
+        step(-2, P0{}, Plain{});
+        step(-1, P1{}, Plain{});
+      }
       int t = 0;
+      for (; t + 2 <= n_stream; t += 2) {
+        step(t, P0{}, Stream{});
+        step(t + 1, P1{}, Stream{});
+      }
       for (; t + 2 <= n_plain; t += 2) {
         step(t, P0{}, Plain{});
         step(t + 1, P1{}, Plain{});
