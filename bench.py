@@ -89,13 +89,16 @@ def copy_probe(mib: int):
 
 def peak_probe():
     """Achievable bf16 MFMA rate (an 8192^3 GEMM through the vendor library) and
-    achievable HBM rate (a 4 GiB copy reads and writes 8 GiB), median of 10."""
+    achievable HBM rates with the runtime's own kernels on 4 GiB buffers: a
+    copy (reads and writes 8 GiB), a read-only sum and a write-only fill,
+    median of 10."""
     import torch
     n = 8192
     a = torch.randn((n, n), device="cuda").bfloat16()
     b = torch.randn((n, n), device="cuda").bfloat16()
     src = torch.empty(4 << 30, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
+    src_f = src.view(torch.float32)
 
     def med_ms(fn):
         fn()
@@ -112,9 +115,15 @@ def peak_probe():
 
     gemm_ms = med_ms(lambda: torch.matmul(a, b))
     copy_ms = med_ms(lambda: dst.copy_(src))
+    read_ms = med_ms(lambda: torch.sum(src_f))
+    write_ms = med_ms(lambda: dst.fill_(3))
+    nb = src.numel()
     print(json.dumps({"gemm_bf16_tflops": 2.0 * n ** 3 / (gemm_ms * 1e-3) / 1e12,
-                      "copy_gbs": 2.0 * src.numel() / (copy_ms * 1e-3) / 1e9,
-                      "gemm_ms": gemm_ms, "copy_ms": copy_ms}), flush=True)
+                      "copy_gbs": 2.0 * nb / (copy_ms * 1e-3) / 1e9,
+                      "read_gbs": nb / (read_ms * 1e-3) / 1e9,
+                      "write_gbs": nb / (write_ms * 1e-3) / 1e9,
+                      "gemm_ms": gemm_ms, "copy_ms": copy_ms, "read_ms": read_ms,
+                      "write_ms": write_ms}), flush=True)
 
 
 # ----------------------------------------------------------------------------

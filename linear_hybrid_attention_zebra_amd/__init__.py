@@ -19,7 +19,10 @@ from typing import Optional
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzebra.so")
+# the in-tree build; ZEBRA_LIBRARY selects another build of the same library
+# (the host-AddressSanitizer copy that the host ABI tests run against)
+LIB_PATH = os.environ.get("ZEBRA_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libzebra.so")
 HEAD_DIM = 64
 
 ZEBRA_OK, ZEBRA_ERR_INVALID_ARG, ZEBRA_ERR_UNSUPPORTED, ZEBRA_ERR_WORKSPACE, ZEBRA_ERR_HIP = range(5)
@@ -29,7 +32,8 @@ ZEBRA_SPARSE_NO_LANDMARKS, ZEBRA_SPARSE_LANDMARK_LOG_COUNT = 1, 2
 ENTRY_POINTS = (
     "zebra_pool_landmarks", "zebra_select_tiles_workspace", "zebra_select_tiles",
     "zebra_tile_sparse_attn_workspace", "zebra_tile_sparse_attn", "zebra_tile_sparse_attn_ex",
-    "zebra_linear_attn_workspace", "zebra_linear_attn", "zebra_fit_affine", "zebra_fit_scale_only",
+    "zebra_linear_attn_workspace", "zebra_linear_attn", "zebra_linear_attn_noalloc_max_bytes",
+    "zebra_linear_attn_noalloc", "zebra_fit_affine", "zebra_fit_scale_only",
     "zebra_block_mass_workspace", "zebra_block_mass", "zebra_spatial_order",
     "zebra_permute_tokens", "zebra_linear_attn_backward_workspace", "zebra_linear_attn_backward",
     "zebra_tile_sparse_attn_backward_workspace", "zebra_tile_sparse_attn_backward",

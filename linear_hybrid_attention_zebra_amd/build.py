@@ -77,6 +77,46 @@ def device_asm(src: str, out: str) -> str:
     return out
 
 
+ASAN_DIR = os.path.join(BUILD_DIR, "asan")
+ASAN_LIB_PATH = os.path.join(ASAN_DIR, "libzebra_asan.so")
+
+
+def asan_runtime() -> str:
+    """Path of the host AddressSanitizer runtime of the ROCm compiler."""
+    res = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True)
+    return res.stdout.strip()
+
+
+def build_asan(jobs: int = 8) -> str:
+    """A copy of the library whose HOST code is built with AddressSanitizer
+    (the gfx950 device code is built as usual): for the host-side ABI tests,
+    which exercise argument validation and launch nothing. Needs the ASan
+    runtime preloaded into the process that loads it."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    flags = COMMON_FLAGS + ["-Xarch_host", "-fsanitize=address", "-Xarch_host",
+                            "-fno-omit-frame-pointer", "-g"]
+
+    def one(src):
+        obj = os.path.join(ASAN_DIR, os.path.basename(src) + ".o")
+        cmd = [hipcc()] + flags + (["-x", "hip"] if src.endswith(".cpp") else []) + \
+            ["-c", src, "-o", obj]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc (asan) failed on {src}:\n{res.stderr}")
+        return obj
+
+    srcs = sources()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
+        objs = list(ex.map(one, srcs))
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libasan",
+           "-Xarch_host", "-fsanitize=address", "-o", ASAN_LIB_PATH] + objs
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"asan link failed:\n{res.stderr}")
+    return ASAN_LIB_PATH
+
+
 def build(verbose: bool = False, jobs: int = 8) -> str:
     """Compile every kernel source for gfx950 and link libzebra.so; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
@@ -95,4 +135,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    if len(sys.argv) > 1 and sys.argv[1] == "--asan":
+        print(build_asan())
+    else:
+        build(verbose=True)
