@@ -153,10 +153,12 @@ def recorded_traffic(workload: str):
     """HBM bytes per sparse launch from the committed rocprofv3 counter summary
     (FETCH_SIZE + WRITE_SIZE, copy-scaled), or None when the summary does not
     cover this workload or the attention kernel source has changed since."""
-    if workload != "stack24-512v":
+    names = {"stack24-512v": "tile_sparse_kh_kernel_stack24-512v_hbm_bytes.md",
+             "sparse-1024v": "tile_sparse_kh_kernel_sparse-1024v_hbm_bytes.md"}
+    if workload not in names:
         return None
     root = os.path.dirname(os.path.abspath(__file__))
-    summary = os.path.join(root, "profiles", "tile_sparse_kh_kernel_stack24-512v_hbm_bytes.md")
+    summary = os.path.join(root, "profiles", names[workload])
     source = os.path.join(root, "linear_hybrid_attention_zebra_amd", "csrc", "sparse_attn.hip")
     try:
         text = open(summary).read()
@@ -347,6 +349,8 @@ def time_stage(args, torch, zb, stage_mod, synth, name, stage, q_mul, launches, 
     if q_mul != 1.0:
         out["softmax"] = (f"running maximum (queries x{q_mul:g}: every item's logit bound "
                           "exceeds the fixed-reference limit)")
+    elif w.kind != "stack":
+        out["traffic"] = recorded_traffic(w.name)
     return out
 
 
