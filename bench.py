@@ -56,7 +56,7 @@ def parse():
     p.add_argument("--fallback", action="store_true",
                    help="with --single-stage: queries x8, so every item takes the "
                         "running-maximum softmax path")
-    p.add_argument("--cpu-rows", type=int, default=8,
+    p.add_argument("--cpu-rows", type=int, default=64,
                    help="sampled (head, query tile) rows for the oracle's attention step")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB three times (the "
