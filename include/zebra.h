@@ -165,6 +165,24 @@ zebra_status zebra_tile_sparse_attn_ex(const void* q, zebra_seq qs, const void* 
                                        size_t workspace_bytes, void* stream);
 
 /*
+ * zebra_tile_sparse_attn_ex that also writes each query's softmax normaliser,
+ * for zebra_tile_sparse_attn_backward_lse (a training step keeps it from its
+ * forward, as the refinement of a converted model would; Zebra3D paper page,
+ * Tables 18-19). lse_out: float32 [H][Nq], contiguous, 4-byte aligned, caller
+ * owned; lse[h][n] = log2 of sum_c 2^(w_c) over the columns c of query n, with
+ * w_c = scale * log2(e) * q_n . key_c (+ log2 n_j for a landmark under
+ * ZEBRA_SPARSE_LANDMARK_LOG_COUNT), the column weights of the forward's own
+ * float32 sums. It must not overlap any other argument (ZEBRA_ERR_INVALID_ARG).
+ * Output and workspace as for zebra_tile_sparse_attn_ex.
+ */
+zebra_status zebra_tile_sparse_attn_lse(const void* q, zebra_seq qs, const void* k, const void* v,
+                                        zebra_seq kvs, const float* kbar, const float* vbar,
+                                        const int32_t* sel, int32_t q_tile, int32_t k_tile,
+                                        int32_t top_k, float scale, void* o, zebra_seq os,
+                                        zebra_dtype o_dtype, uint32_t flags, float* lse_out,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Linear attention plus affine map. Tolerant stages run linear(-centered)
  * attention (Zebra3D paper page, Abstract; Table 3(a) "Linear-centered +
  * fit"). With phi(x) = elu(x) + 1 per channel:
@@ -258,6 +276,22 @@ zebra_status zebra_tile_sparse_attn_backward(
     float scale, uint32_t flags, const void* dout, zebra_seq dos, zebra_dtype g_dtype, void* dq,
     zebra_seq dqs, void* dk, void* dv, zebra_seq dkvs, void* workspace, size_t workspace_bytes,
     void* stream);
+
+/*
+ * zebra_tile_sparse_attn_backward with the normaliser lse of an earlier
+ * zebra_tile_sparse_attn_lse call on the same q, k, v, landmarks, selection,
+ * tiles, scale and flags: the call then does not run the forward itself (it
+ * packs the landmarks and copies lse into its workspace; its first sweep
+ * renormalises that copy). The gradients are bitwise those of
+ * zebra_tile_sparse_attn_backward. lse: float32 [H][Nq], contiguous, 4-byte
+ * aligned, read only. Workspace: zebra_tile_sparse_attn_backward_workspace.
+ */
+zebra_status zebra_tile_sparse_attn_backward_lse(
+    const void* q, zebra_seq qs, const void* k, const void* v, zebra_seq kvs, const float* kbar,
+    const float* vbar, const int32_t* sel, int32_t q_tile, int32_t k_tile, int32_t top_k,
+    float scale, uint32_t flags, const float* lse, const void* dout, zebra_seq dos,
+    zebra_dtype g_dtype, void* dq, zebra_seq dqs, void* dk, void* dv, zebra_seq dkvs,
+    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Gradients of one linear stage (for the optional refinement of a converted

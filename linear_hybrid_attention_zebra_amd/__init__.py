@@ -32,6 +32,7 @@ ZEBRA_SPARSE_NO_LANDMARKS, ZEBRA_SPARSE_LANDMARK_LOG_COUNT = 1, 2
 ENTRY_POINTS = (
     "zebra_pool_landmarks", "zebra_select_tiles_workspace", "zebra_select_tiles",
     "zebra_tile_sparse_attn_workspace", "zebra_tile_sparse_attn", "zebra_tile_sparse_attn_ex",
+    "zebra_tile_sparse_attn_lse", "zebra_tile_sparse_attn_backward_lse",
     "zebra_linear_attn_workspace", "zebra_linear_attn", "zebra_linear_attn_noalloc_max_bytes",
     "zebra_linear_attn_noalloc", "zebra_fit_affine", "zebra_fit_scale_only",
     "zebra_block_mass_workspace", "zebra_block_mass", "zebra_spatial_order",
@@ -78,6 +79,14 @@ def _declare(lib):
         "zebra_tile_sparse_attn_ex": (c_i32, [c_p, ZebraSeq, c_p, c_p, ZebraSeq, c_p, c_p, c_p,
                                               c_i32, c_i32, c_i32, c_f, c_p, ZebraSeq, c_i32,
                                               ctypes.c_uint32, c_p, c_sz, c_p]),
+        "zebra_tile_sparse_attn_lse": (c_i32, [c_p, ZebraSeq, c_p, c_p, ZebraSeq, c_p, c_p, c_p,
+                                               c_i32, c_i32, c_i32, c_f, c_p, ZebraSeq, c_i32,
+                                               ctypes.c_uint32, c_p, c_p, c_sz, c_p]),
+        "zebra_tile_sparse_attn_backward_lse": (c_i32, [c_p, ZebraSeq, c_p, c_p, ZebraSeq, c_p,
+                                                        c_p, c_p, c_i32, c_i32, c_i32, c_f,
+                                                        ctypes.c_uint32, c_p, c_p, ZebraSeq, c_i32,
+                                                        c_p, ZebraSeq, c_p, c_p, ZebraSeq, c_p,
+                                                        c_sz, c_p]),
         "zebra_linear_attn_workspace": (c_sz, [c_i64, c_i32, c_i32]),
         "zebra_linear_attn": (c_i32, [c_p, ZebraSeq, c_p, c_p, ZebraSeq, c_p, c_p, c_p, ZebraSeq,
                                       c_i32, c_p, c_sz, c_p]),
@@ -231,9 +240,12 @@ def zebra_tile_sparse_attn_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                               sel: Optional[torch.Tensor], q_tile: int, k_tile: int, top_k: int,
                               scale: float, flags: int, out: Optional[torch.Tensor] = None,
                               out_dtype=torch.bfloat16,
-                              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                              workspace: Optional[torch.Tensor] = None,
+                              lse_out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Sparse-operator variants: flags ZEBRA_SPARSE_NO_LANDMARKS (kbar, vbar may be
-    None) or ZEBRA_SPARSE_LANDMARK_LOG_COUNT; 0 is zebra_tile_sparse_attn."""
+    None) or ZEBRA_SPARSE_LANDMARK_LOG_COUNT; 0 is zebra_tile_sparse_attn. With
+    lse_out (float32 [H][Nq]) it calls zebra_tile_sparse_attn_lse, which also
+    writes each query's softmax normaliser for zebra_tile_sparse_attn_backward."""
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, torch.bfloat16, name)
     if k.shape != v.shape or k.stride() != v.stride():
@@ -255,6 +267,16 @@ def zebra_tile_sparse_attn_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     nbytes = lib.zebra_tile_sparse_attn_workspace(q.shape[1], k.shape[1], k.shape[0], HEAD_DIM,
                                                   q_tile, k_tile, top_k)
     workspace = _workspace(nbytes, q.device, workspace)
+    if lse_out is not None:
+        _need(lse_out, torch.float32, "lse_out")
+        if not lse_out.is_contiguous() or lse_out.numel() != q.shape[0] * q.shape[1]:
+            raise ValueError("lse_out must be a contiguous [H][Nq] float32 tensor")
+        _check("zebra_tile_sparse_attn_lse", lib.zebra_tile_sparse_attn_lse(
+            _ptr(q), seq_of(q), _ptr(k), _ptr(v), seq_of(k), _ptr(kbar), _ptr(vbar), _ptr(sel),
+            q_tile, k_tile, top_k, scale, _ptr(out), seq_of(out),
+            ZEBRA_F32 if out.dtype == torch.float32 else ZEBRA_BF16, flags, _ptr(lse_out),
+            _ptr(workspace), nbytes, _stream(q.device)))
+        return out
     _check("zebra_tile_sparse_attn_ex", lib.zebra_tile_sparse_attn_ex(
         _ptr(q), seq_of(q), _ptr(k), _ptr(v), seq_of(k), _ptr(kbar), _ptr(vbar), _ptr(sel),
         q_tile, k_tile, top_k, scale, _ptr(out), seq_of(out),
@@ -433,9 +455,12 @@ def zebra_tile_sparse_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.T
                                     kbar: Optional[torch.Tensor], vbar: Optional[torch.Tensor],
                                     sel: torch.Tensor, q_tile: int, k_tile: int, top_k: int,
                                     scale: float, dout: torch.Tensor, flags: int = 0,
-                                    workspace: Optional[torch.Tensor] = None):
+                                    workspace: Optional[torch.Tensor] = None,
+                                    lse: Optional[torch.Tensor] = None):
     """Gradients (dq, dk, dv) of sum(dout * out) for one tile-sparse stage, sel fixed;
-    the gradients take dout's dtype (bfloat16 or float32)."""
+    the gradients take dout's dtype (bfloat16 or float32). With lse, the normaliser a
+    forward call wrote (zebra_tile_sparse_attn_ex with lse_out), the call does not
+    run the forward again (zebra_tile_sparse_attn_backward_lse)."""
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, torch.bfloat16, name)
     _need(sel, torch.int32, "sel")
@@ -453,9 +478,19 @@ def zebra_tile_sparse_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.T
     nbytes = lib.zebra_tile_sparse_attn_backward_workspace(q.shape[1], k.shape[1], q.shape[0],
                                                            HEAD_DIM, q_tile, k_tile, top_k)
     workspace = _workspace(nbytes, q.device, workspace)
+    g_dtype = ZEBRA_F32 if dout.dtype == torch.float32 else ZEBRA_BF16
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
+        if not lse.is_contiguous() or lse.numel() != q.shape[0] * q.shape[1]:
+            raise ValueError("lse must be a contiguous [H][Nq] float32 tensor")
+        _check("zebra_tile_sparse_attn_backward_lse", lib.zebra_tile_sparse_attn_backward_lse(
+            _ptr(q), seq_of(q), _ptr(k), _ptr(v), seq_of(k), _ptr(kbar), _ptr(vbar), _ptr(sel),
+            q_tile, k_tile, top_k, scale, flags, _ptr(lse), _ptr(dout), seq_of(dout), g_dtype,
+            _ptr(dq), seq_of(dq), _ptr(dk), _ptr(dv), seq_of(dk), _ptr(workspace), nbytes,
+            _stream(q.device)))
+        return dq, dk, dv
     _check("zebra_tile_sparse_attn_backward", lib.zebra_tile_sparse_attn_backward(
         _ptr(q), seq_of(q), _ptr(k), _ptr(v), seq_of(k), _ptr(kbar), _ptr(vbar), _ptr(sel),
-        q_tile, k_tile, top_k, scale, flags, _ptr(dout), seq_of(dout),
-        ZEBRA_F32 if dout.dtype == torch.float32 else ZEBRA_BF16, _ptr(dq), seq_of(dq), _ptr(dk),
-        _ptr(dv), seq_of(dk), _ptr(workspace), nbytes, _stream(q.device)))
+        q_tile, k_tile, top_k, scale, flags, _ptr(dout), seq_of(dout), g_dtype, _ptr(dq),
+        seq_of(dq), _ptr(dk), _ptr(dv), seq_of(dk), _ptr(workspace), nbytes, _stream(q.device)))
     return dq, dk, dv

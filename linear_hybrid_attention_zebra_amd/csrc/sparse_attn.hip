@@ -1728,6 +1728,16 @@ size_t sparse_workspace_bytes(int64_t n_q, int64_t n_kv, int32_t heads, int32_t 
   return 2 * lm + range + sp.coff + sp.part_o + sp.part_ml;
 }
 
+hipError_t launch_pack_landmarks(const float* kbar, const float* vbar, int32_t heads, int32_t tk,
+                                 uint16_t* kb, uint16_t* vb, hipStream_t s) {
+  const int64_t pairs = (int64_t)heads * tk * (kHeadDim / 2);
+  if (pairs == 0) return hipSuccess;
+  const int blocks = (int)std::min<int64_t>((pairs + 255) / 256, 8192);
+  hipLaunchKernelGGL(pack_landmarks_kernel, dim3(blocks), dim3(256), 0, s, kbar, vbar, pairs, kb,
+                     vb);
+  return hipGetLastError();
+}
+
 hipError_t launch_tile_sparse(const uint16_t* q, int64_t nq, int64_t qst, int64_t qsh,
                               const uint16_t* k, const uint16_t* v, int64_t nk, int64_t kst,
                               int64_t ksh, int32_t heads, const float* kbar, const float* vbar,
@@ -1781,11 +1791,7 @@ hipError_t launch_tile_sparse(const uint16_t* q, int64_t nq, int64_t qst, int64_
     const size_t lm = align256((size_t)heads * p.tk * kHeadDim * sizeof(uint16_t));
     uint16_t* kb = (uint16_t*)ws;
     uint16_t* vb = (uint16_t*)((uint8_t*)ws + lm);
-    const int64_t pairs = (int64_t)heads * p.tk * (kHeadDim / 2);
-    const int blocks = (int)std::min<int64_t>((pairs + 255) / 256, 8192);
-    hipLaunchKernelGGL(pack_landmarks_kernel, dim3(blocks), dim3(256), 0, s, kbar, vbar, pairs,
-                       kb, vb);
-    hipError_t err = hipGetLastError();
+    hipError_t err = launch_pack_landmarks(kbar, vbar, heads, p.tk, kb, vb, s);
     if (err != hipSuccess) return err;
     p.kbar_b = kb;
     p.vbar_b = vb;

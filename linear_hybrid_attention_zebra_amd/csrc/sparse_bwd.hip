@@ -1340,7 +1340,8 @@ hipError_t launch_tile_sparse_bwd(const uint16_t* q, int64_t nq, int64_t qst, in
                                   int32_t k_tile, int32_t top_k, float scale, uint32_t flags,
                                   const void* dout, int64_t dst, int64_t dsh, bool g_f32,
                                   void* dq, int64_t qgst, int64_t qgsh, void* dk, void* dv,
-                                  int64_t kgst, int64_t kgsh, void* ws, hipStream_t s) {
+                                  int64_t kgst, int64_t kgsh, void* ws, hipStream_t s,
+                                  const float* lse_in) {
   if (heads == 0 || (nq == 0 && nk == 0)) return hipSuccess;
   const BwdLayout L = bwd_layout(nq, nk, heads, q_tile, k_tile, top_k);
   uint8_t* w = (uint8_t*)ws;
@@ -1369,11 +1370,22 @@ hipError_t launch_tile_sparse_bwd(const uint16_t* q, int64_t nq, int64_t qst, in
   const int32_t bit_words = (tk + 31) / 32;
   const bool landmarks = (flags & kSparseNoLandmarks) == 0 && top_k < tk;
   hipError_t err;
-  // forward: float32 output and the log2 normaliser (also packs the bf16 landmarks)
-  if (nq > 0) {
+  // forward: float32 output and the log2 normaliser (also packs the bf16 landmarks), or,
+  // with the normaliser of an earlier forward call given, the landmarks alone and a copy of
+  // the normaliser (sweep 0 renormalises the copy in place)
+  if (nq > 0 && lse_in == nullptr) {
     err = launch_tile_sparse(q, nq, qst, qsh, k, v, nk, kst, ksh, heads, kbar, vbar, sel, q_tile,
                              k_tile, top_k, scale, dq_acc, kHeadDim, nq * kHeadDim, true, flags, w,
                              s, lse);
+    if (err != hipSuccess) return err;
+  } else if (nq > 0) {
+    if (landmarks) {
+      const size_t lmb = a256((size_t)heads * tk * kHeadDim * sizeof(uint16_t));
+      err = launch_pack_landmarks(kbar, vbar, heads, tk, (uint16_t*)w, (uint16_t*)(w + lmb), s);
+      if (err != hipSuccess) return err;
+    }
+    err = hipMemcpyAsync(lse, lse_in, (size_t)heads * nq * sizeof(float),
+                         hipMemcpyDeviceToDevice, s);
     if (err != hipSuccess) return err;
   }
   // dout packed as bf16 rows for the dk, dv kernels' direct-to-LDS staging

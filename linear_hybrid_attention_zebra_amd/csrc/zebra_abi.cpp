@@ -171,12 +171,13 @@ zebra_status zebra_tile_sparse_attn(const void* q, zebra_seq qs, const void* k, 
                                    scale, o, os, o_dtype, 0u, workspace, workspace_bytes, stream);
 }
 
-zebra_status zebra_tile_sparse_attn_ex(const void* q, zebra_seq qs, const void* k, const void* v,
-                                       zebra_seq kvs, const float* kbar, const float* vbar,
-                                       const int32_t* sel, int32_t q_tile, int32_t k_tile,
-                                       int32_t top_k, float scale, void* o, zebra_seq os,
-                                       zebra_dtype o_dtype, uint32_t flags, void* workspace,
-                                       size_t workspace_bytes, void* stream) {
+// zebra_tile_sparse_attn_ex and zebra_tile_sparse_attn_lse: lse_out (float32 [H][Nq]) or NULL
+static zebra_status sparse_fwd(const void* q, zebra_seq qs, const void* k, const void* v,
+                               zebra_seq kvs, const float* kbar, const float* vbar,
+                               const int32_t* sel, int32_t q_tile, int32_t k_tile, int32_t top_k,
+                               float scale, void* o, zebra_seq os, zebra_dtype o_dtype,
+                               uint32_t flags, float* lse_out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   zebra_status st;
   const uint32_t known = ZEBRA_SPARSE_NO_LANDMARKS | ZEBRA_SPARSE_LANDMARK_LOG_COUNT;
   if ((flags & ~known) != 0u || flags == known) return ZEBRA_ERR_INVALID_ARG;
@@ -227,12 +228,40 @@ zebra_status zebra_tile_sparse_attn_ex(const void* q, zebra_seq qs, const void* 
     if (overlaps(ws, r)) return ZEBRA_ERR_INVALID_ARG;
   for (const Range& r : inputs)
     if (overlaps(orng, r)) return ZEBRA_ERR_INVALID_ARG;
+  if (lse_out != nullptr) {
+    if (((uintptr_t)lse_out % 4) != 0) return ZEBRA_ERR_INVALID_ARG;
+    const Range lr = flat_range(lse_out, (uint64_t)qs.n_heads * qs.n_tokens, 4);
+    if (overlaps(lr, orng) || overlaps(lr, ws)) return ZEBRA_ERR_INVALID_ARG;
+    for (const Range& r : inputs)
+      if (overlaps(lr, r)) return ZEBRA_ERR_INVALID_ARG;
+  }
   return hip_status(zebra::launch_tile_sparse(
       (const uint16_t*)q, qs.n_tokens, qs.stride_token, qs.stride_head, (const uint16_t*)k,
       (const uint16_t*)v, kvs.n_tokens, kvs.stride_token, kvs.stride_head, qs.n_heads,
       use_lm ? kbar : nullptr, use_lm ? vbar : nullptr, dense ? nullptr : sel, q_tile, k_tile,
       top_k, scale, o, os.stride_token, os.stride_head, o_dtype == ZEBRA_F32,
-      dense ? 0u : flags, workspace, (hipStream_t)stream));
+      dense ? 0u : flags, workspace, (hipStream_t)stream, lse_out));
+}
+
+zebra_status zebra_tile_sparse_attn_ex(const void* q, zebra_seq qs, const void* k, const void* v,
+                                       zebra_seq kvs, const float* kbar, const float* vbar,
+                                       const int32_t* sel, int32_t q_tile, int32_t k_tile,
+                                       int32_t top_k, float scale, void* o, zebra_seq os,
+                                       zebra_dtype o_dtype, uint32_t flags, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  return sparse_fwd(q, qs, k, v, kvs, kbar, vbar, sel, q_tile, k_tile, top_k, scale, o, os,
+                    o_dtype, flags, nullptr, workspace, workspace_bytes, stream);
+}
+
+zebra_status zebra_tile_sparse_attn_lse(const void* q, zebra_seq qs, const void* k, const void* v,
+                                        zebra_seq kvs, const float* kbar, const float* vbar,
+                                        const int32_t* sel, int32_t q_tile, int32_t k_tile,
+                                        int32_t top_k, float scale, void* o, zebra_seq os,
+                                        zebra_dtype o_dtype, uint32_t flags, float* lse_out,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (lse_out == nullptr && !seq_empty(qs)) return ZEBRA_ERR_INVALID_ARG;
+  return sparse_fwd(q, qs, k, v, kvs, kbar, vbar, sel, q_tile, k_tile, top_k, scale, o, os,
+                    o_dtype, flags, lse_out, workspace, workspace_bytes, stream);
 }
 
 size_t zebra_block_mass_workspace(int64_t n_q, int32_t n_heads) {
@@ -401,12 +430,14 @@ size_t zebra_tile_sparse_attn_backward_workspace(int64_t n_q, int64_t n_kv, int3
   return zebra::sparse_bwd_workspace_bytes(n_q, n_kv, n_heads, q_tile, k_tile, top_k);
 }
 
-zebra_status zebra_tile_sparse_attn_backward(
+// zebra_tile_sparse_attn_backward and zebra_tile_sparse_attn_backward_lse: lse_in (float32
+// [H][Nq], from zebra_tile_sparse_attn_lse with the same arguments) or NULL
+static zebra_status sparse_bwd(
     const void* q, zebra_seq qs, const void* k, const void* v, zebra_seq kvs, const float* kbar,
     const float* vbar, const int32_t* sel, int32_t q_tile, int32_t k_tile, int32_t top_k,
-    float scale, uint32_t flags, const void* dout, zebra_seq dos, zebra_dtype g_dtype, void* dq,
-    zebra_seq dqs, void* dk, void* dv, zebra_seq dkvs, void* workspace, size_t workspace_bytes,
-    void* stream) {
+    float scale, uint32_t flags, const float* lse_in, const void* dout, zebra_seq dos,
+    zebra_dtype g_dtype, void* dq, zebra_seq dqs, void* dk, void* dv, zebra_seq dkvs,
+    void* workspace, size_t workspace_bytes, void* stream) {
   zebra_status st;
   const uint32_t known = ZEBRA_SPARSE_NO_LANDMARKS | ZEBRA_SPARSE_LANDMARK_LOG_COUNT;
   if ((flags & ~known) != 0u || flags == known) return ZEBRA_ERR_INVALID_ARG;
@@ -455,6 +486,10 @@ zebra_status zebra_tile_sparse_attn_backward(
     ins.push_back(flat_range(kbar, (uint64_t)h * tk * zebra::kHeadDim, 4));
     ins.push_back(flat_range(vbar, (uint64_t)h * tk * zebra::kHeadDim, 4));
   }
+  if (lse_in != nullptr) {
+    if (((uintptr_t)lse_in % 4) != 0) return ZEBRA_ERR_INVALID_ARG;
+    ins.push_back(flat_range(lse_in, (uint64_t)h * qs.n_tokens, 4));
+  }
   const Range outs[] = {seq_range(dq, dqs, gel), seq_range(dk, dkvs, gel),
                         seq_range(dv, dkvs, gel), flat_range(workspace, need, 1)};
   for (size_t i = 0; i < 4; ++i) {
@@ -469,7 +504,30 @@ zebra_status zebra_tile_sparse_attn_backward(
       use_lm ? kbar : nullptr, use_lm ? vbar : nullptr, sel, q_tile, k_tile, top_k, scale,
       top_k < tk ? flags : 0u, dout, dos.stride_token, dos.stride_head, g_dtype == ZEBRA_F32, dq,
       dqs.stride_token, dqs.stride_head, dk, dv, dkvs.stride_token, dkvs.stride_head, workspace,
-      (hipStream_t)stream));
+      (hipStream_t)stream, lse_in));
+}
+
+zebra_status zebra_tile_sparse_attn_backward(
+    const void* q, zebra_seq qs, const void* k, const void* v, zebra_seq kvs, const float* kbar,
+    const float* vbar, const int32_t* sel, int32_t q_tile, int32_t k_tile, int32_t top_k,
+    float scale, uint32_t flags, const void* dout, zebra_seq dos, zebra_dtype g_dtype, void* dq,
+    zebra_seq dqs, void* dk, void* dv, zebra_seq dkvs, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  return sparse_bwd(q, qs, k, v, kvs, kbar, vbar, sel, q_tile, k_tile, top_k, scale, flags,
+                    nullptr, dout, dos, g_dtype, dq, dqs, dk, dv, dkvs, workspace,
+                    workspace_bytes, stream);
+}
+
+zebra_status zebra_tile_sparse_attn_backward_lse(
+    const void* q, zebra_seq qs, const void* k, const void* v, zebra_seq kvs, const float* kbar,
+    const float* vbar, const int32_t* sel, int32_t q_tile, int32_t k_tile, int32_t top_k,
+    float scale, uint32_t flags, const float* lse, const void* dout, zebra_seq dos,
+    zebra_dtype g_dtype, void* dq, zebra_seq dqs, void* dk, void* dv, zebra_seq dkvs,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  if (lse == nullptr && !seq_empty(qs)) return ZEBRA_ERR_INVALID_ARG;
+  return sparse_bwd(q, qs, k, v, kvs, kbar, vbar, sel, q_tile, k_tile, top_k, scale, flags, lse,
+                    dout, dos, g_dtype, dq, dqs, dk, dv, dkvs, workspace, workspace_bytes,
+                    stream);
 }
 
 size_t zebra_linear_attn_backward_workspace(int64_t n_q, int64_t n_kv, int32_t n_heads,

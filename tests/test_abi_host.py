@@ -32,7 +32,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 24, names
     for name in names:
         assert hasattr(lib, name), f"{name} declared in zebra.h but not exported"
     assert set(names) == set(zb.ENTRY_POINTS)
@@ -133,6 +133,35 @@ def test_zero_stride_outputs_rejected_everywhere(lib):
             zb.ZEBRA_ERR_INVALID_ARG
         assert lib.zebra_permute_tokens(P(1 << 16), s, P(1 << 24), 0, 0, P(1 << 28), bad,
                                         None) == zb.ZEBRA_ERR_INVALID_ARG
+
+
+def test_lse_entry_points_validation(lib):
+    """The normaliser-carrying forward and backward need their lse pointer, refuse an
+    lse that overlaps an output, and otherwise validate as their plain forms."""
+    f = lib.zebra_tile_sparse_attn_lse
+    s = seq(256)
+    ws = lib.zebra_tile_sparse_attn_workspace(256, 256, 2, 64, 64, 64, 2)
+
+    def fwd(lse, ws_b=ws):
+        return f(P(1 << 16), s, P(1 << 18), P(1 << 20), s, P(1 << 22), P(1 << 23), P(1 << 24), 64,
+                 64, 2, 0.125, P(1 << 28), s, 0, 0, lse, P(1 << 30), ws_b, None)
+
+    assert fwd(None) == zb.ZEBRA_ERR_INVALID_ARG
+    assert fwd(P((1 << 28) + 64)) == zb.ZEBRA_ERR_INVALID_ARG  # inside the output
+    assert fwd(P((1 << 16) + 64)) == zb.ZEBRA_ERR_INVALID_ARG  # inside q
+    assert fwd(P((1 << 29) + 2)) == zb.ZEBRA_ERR_INVALID_ARG   # misaligned
+    assert fwd(P(1 << 29), ws_b=ws - 1) == zb.ZEBRA_ERR_WORKSPACE
+    b = lib.zebra_tile_sparse_attn_backward_lse
+    bws = lib.zebra_tile_sparse_attn_backward_workspace(256, 256, 2, 64, 64, 64, 2)
+
+    def bwd(lse, ws_b=bws):
+        return b(P(1 << 16), s, P(1 << 18), P(1 << 20), s, P(1 << 22), P(1 << 23), P(1 << 24), 64,
+                 64, 2, 0.125, 0, lse, P(1 << 25), s, 0, P(1 << 26), s, P(1 << 27), P(1 << 28), s,
+                 P(1 << 31), ws_b, None)
+
+    assert bwd(None) == zb.ZEBRA_ERR_INVALID_ARG
+    assert bwd(P((1 << 26) + 64)) == zb.ZEBRA_ERR_INVALID_ARG  # read from inside dq
+    assert bwd(P(1 << 30), ws_b=bws - 1) == zb.ZEBRA_ERR_WORKSPACE
 
 
 def test_sparse_variant_flags_validation(lib):

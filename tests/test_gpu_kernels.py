@@ -608,6 +608,58 @@ def test_sparse_backward_parity(case, g_dtype):
     assert_grad_close(dv, rv, f"sparse dv {case}")
 
 
+LSE_CASES = [
+    # (q_tile, k_tile, n_q, n_kv, top_k, n_hot, heads, variant)
+    (64, 64, 300, 300, 2, 2, 2, "default"),
+    (128, 32, 257, 300, 4, 2, 1, "log_count"),
+    (32, 64, 100, 450, 1, 1, 2, "no_landmarks"),
+    (64, 64, 300, 65536 + 333, 206, 3, 1, "default"),  # split keys: the combine writes lse
+]
+
+
+@pytest.mark.parametrize("case", LSE_CASES, ids=[str(c) for c in LSE_CASES])
+def test_forward_lse_and_backward_from_it(case):
+    """The forward's normaliser equals the oracle's log2-sum-exp of the column weights
+    (bf16-rounded probabilities are summed: 1e-2 in log2 units), the output is bitwise
+    the plain forward's, and the backward from the saved normaliser is bitwise the
+    backward that runs its own forward."""
+    q_tile, k_tile, n_q, n_kv, top_k, n_hot, heads, variant = case
+    flags, kw = BWD_FLAGS[variant]
+    print(f"[case] forward lse + backward from it {case}", flush=True)
+    q, k, v = _clustered(n_q + 5 * n_kv + top_k, heads, n_q, n_kv, q_tile, k_tile, n_hot)
+    qg, kg, vg = bf16_gpu(q), bf16_gpu(k), bf16_gpu(v)
+    bufs = stage.SparseBuffers.allocate(heads, n_q, n_kv, q_tile, k_tile, top_k, DEV)
+    stage.sparse_select(qg, kg, vg, q_tile, k_tile, top_k, bufs)
+    lse = torch.empty((heads, n_q), dtype=torch.float32, device=DEV)
+    out_l = zb.zebra_tile_sparse_attn_ex(qg, kg, vg, bufs.kbar, bufs.vbar, bufs.sel, q_tile,
+                                         k_tile, top_k, 0.125, flags, lse_out=lse)
+    out_p = zb.zebra_tile_sparse_attn_ex(qg, kg, vg, bufs.kbar, bufs.vbar, bufs.sel, q_tile,
+                                         k_tile, top_k, 0.125, flags)
+    rng = np.random.default_rng(n_q + top_k)
+    dout = torch.from_numpy(synth.bf16_round(
+        rng.standard_normal((heads, n_q, 64)).astype(np.float32))).to(DEV)
+    g_self = zb.zebra_tile_sparse_attn_backward(qg, kg, vg, bufs.kbar, bufs.vbar, bufs.sel,
+                                                q_tile, k_tile, top_k, 0.125, dout, flags)
+    g_lse = zb.zebra_tile_sparse_attn_backward(qg, kg, vg, bufs.kbar, bufs.vbar, bufs.sel,
+                                               q_tile, k_tile, top_k, 0.125, dout, flags, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out_l, out_p)
+    for a, b, name in zip(g_self, g_lse, ("dq", "dk", "dv")):
+        assert torch.equal(a, b), f"{name} from the saved normaliser differs"
+    sel = bufs.sel.cpu().numpy()
+    got = lse.cpu().numpy()
+    worst = 0.0
+    for h in range(heads):
+        for i, (s0, e0) in enumerate(zo.tile_bounds(n_q, q_tile)):
+            ck, _, bias = zo.attention_columns(k[h], v[h], k_tile, sel[h, i], **kw)
+            lg = 0.125 * (q[h, s0:e0].astype(np.float64) @ ck.T) + bias[None, :]
+            m = lg.max(axis=1)
+            ref = (m + np.log(np.exp(lg - m[:, None]).sum(axis=1))) / np.log(2.0)
+            worst = max(worst, float(np.abs(got[h, s0:e0] - ref).max()))
+    print(f"[parity] lse max abs error (log2 units) {worst:.3e}", flush=True)
+    assert worst <= 1e-2
+
+
 def test_sparse_backward_multirow_bits_partial_group():
     """dk and dv through the kept-tile bit matrix built several query tiles per
     workgroup: 16 heads x 283 query tiles of 32 (4,528 rows) give 2 rows per
