@@ -71,6 +71,10 @@ def parse():
     p.add_argument("--backward", action="store_true",
                    help="only time the gradients of the workload's first sparse stage (and, for "
                         "the stack and linear workloads, of its first linear stage) and exit")
+    p.add_argument("--save-affine", default=None, metavar="NPZ",
+                   help="write the fitted affine map of every linear stage to NPZ")
+    p.add_argument("--load-affine", default=None, metavar="NPZ",
+                   help="take the linear stages' affine maps from NPZ instead of fitting them")
     return p.parse_args()
 
 
@@ -224,18 +228,31 @@ def run_gpu(args, w, torch, zb, stage_mod, synth):
     # calibration, once per linear stage before timing (warm call, then a timed one)
     cal_timer = Timer(torch)
     cals = {}
+    if args.load_affine:
+        cals = stage_mod.load_calibrations(args.load_affine, dev)
+        missing = [s for s in stages if kinds[s] == "linear" and s not in cals]
+        if missing or any(c.aff_scale.shape[0] != heads for c in cals.values()):
+            raise SystemExit(f"{args.load_affine}: no {heads}-head affine map for stages "
+                             f"{missing or sorted(cals)}")
     for s in stages:
-        if kinds[s] == "linear":
+        if kinds[s] == "linear" and s not in cals:
             q, k, v = inputs[s]
             stage_mod.calibrate_linear(q, k, v, fit_idx[s], SCALE, w.k_tile)
             cal_timer.start("calibration")
             cals[s] = stage_mod.calibrate_linear(q, k, v, fit_idx[s], SCALE, w.k_tile)
             cal_timer.stop("calibration")
     torch.cuda.synchronize()
+    if args.save_affine:
+        stage_mod.save_calibrations(args.save_affine, cals)
+    # one roctx range per stage (torch's nvtx calls are roctx on ROCm), for
+    # rocprofv3 --marker-trace
+    mark_push, mark_pop = torch.cuda.nvtx.range_push, torch.cuda.nvtx.range_pop
+    labels = {s: f"stage {s} {kinds[s]}" for s in stages}
 
     def step():
         for s in stages:
             q, k, v = inputs[s]
+            mark_push(labels[s])
             if kinds[s] == "sparse":
                 timer.start("sparse_stage")
                 stage_mod.sparse_select(q, k, v, w.q_tile, w.k_tile, top_k, sparse_bufs)
@@ -249,6 +266,7 @@ def run_gpu(args, w, torch, zb, stage_mod, synth):
                 stage_mod.linear_stage(q, k, v, cal.aff_scale, cal.aff_bias, out=lin_out,
                                        workspace=lin_ws)
                 timer.stop("linear_stage")
+            mark_pop()
 
     for _ in range(args.warmup):
         step()

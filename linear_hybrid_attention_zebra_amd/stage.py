@@ -11,8 +11,9 @@ on the current stream.
 from __future__ import annotations
 
 import dataclasses
-from typing import Optional
+from typing import Dict, Optional
 
+import numpy as np
 import torch
 
 from . import (ceil_div, zebra_fit_affine, zebra_linear_attn, zebra_permute_tokens,
@@ -111,8 +112,8 @@ class Calibration:
     aff_bias: torch.Tensor   # [H][64]
     n_degenerate: int
     sample_index: torch.Tensor
-    x: torch.Tensor  # unfitted linear output at the samples, float32 [H][M][64]
-    y: torch.Tensor  # dense softmax output at the samples, float32 [H][M][64]
+    x: Optional[torch.Tensor] = None  # unfitted linear output at the samples, float32 [H][M][64]
+    y: Optional[torch.Tensor] = None  # dense softmax output at the samples, float32 [H][M][64]
 
 
 def calibrate_linear(q, k, v, sample_index: torch.Tensor, scale: float, k_tile: int = 64,
@@ -128,3 +129,37 @@ def calibrate_linear(q, k, v, sample_index: torch.Tensor, scale: float, k_tile: 
     x = zebra_linear_attn(qs, k, v, out_dtype=torch.float32)
     a, b, n_deg = zebra_fit_affine(x, y)
     return Calibration(a, b, int(n_deg.item()), sample_index, x, y)
+
+
+def save_calibrations(path, cals: Dict[int, Calibration]) -> None:
+    """Write the fitted affine map of every linear stage to one ``.npz``.
+
+    Per stage ``s`` the file holds ``s{s}_aff_scale`` and ``s{s}_aff_bias``
+    (float32 [H][64]), ``s{s}_sample_index`` (int64 [M]) and
+    ``s{s}_n_degenerate`` (int64 scalar). A converted stack is then usable
+    again without re-fitting. The samples x, y are not stored."""
+    arrays = {}
+    for s, c in sorted(cals.items()):
+        arrays[f"s{s}_aff_scale"] = c.aff_scale.detach().float().cpu().numpy()
+        arrays[f"s{s}_aff_bias"] = c.aff_bias.detach().float().cpu().numpy()
+        arrays[f"s{s}_sample_index"] = c.sample_index.detach().to(torch.int64).cpu().numpy()
+        arrays[f"s{s}_n_degenerate"] = np.int64(c.n_degenerate)
+    np.savez(path, **arrays)
+
+
+def load_calibrations(path, device) -> Dict[int, Calibration]:
+    """Read a file written by :func:`save_calibrations` (no pickled objects are
+    loaded) and place the maps on ``device``."""
+    cals: Dict[int, Calibration] = {}
+    with np.load(path, allow_pickle=False) as z:
+        stages = sorted({int(k[1:].split("_", 1)[0]) for k in z.files})
+        for s in stages:
+            a = torch.from_numpy(z[f"s{s}_aff_scale"]).to(device=device, dtype=torch.float32)
+            b = torch.from_numpy(z[f"s{s}_aff_bias"]).to(device=device, dtype=torch.float32)
+            if a.dim() != 2 or a.shape[1] != 64 or b.shape != a.shape:
+                raise ValueError(f"stage {s}: affine map of shape {tuple(a.shape)}, "
+                                 f"{tuple(b.shape)}; expected [H][64] twice")
+            idx = torch.from_numpy(z[f"s{s}_sample_index"]).to(device)
+            cals[s] = Calibration(a.contiguous(), b.contiguous(),
+                                  int(z[f"s{s}_n_degenerate"]), idx)
+    return cals
