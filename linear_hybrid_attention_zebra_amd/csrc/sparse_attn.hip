@@ -64,6 +64,7 @@
 // One barrier per step. 16-byte LDS chunks are XOR swizzled by row so both
 // operand reads are bank-conflict free.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -111,6 +112,9 @@ struct SparseParams {
   float* part_o;           // [H][nq][n_chunks][64] unnormalised outputs
   float2* part_ml;         // [H][nq][n_chunks] (reference, row sum), p = 2^(c s - reference)
   float* lse;              // [H][nq] log2 of the softmax normaliser (log2 units), or null
+  // kept-list walk phase (key-half kernel): 0, or the number of items the
+  // device runs at once (see the kernel)
+  int64_t phase_period;
 };
 
 // Byte offset of 16-byte chunk `chunk` of 128-byte row `row` in a tile. The
@@ -1005,6 +1009,41 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
     const int n_total = n_kept + n_lb;
     const int32_t* sel_row = dense ? nullptr : sel + row * p.top_k + kept0;
+    // Walk order of the kept list. Any order gives the same softmax up to
+    // rounding; with a phase period P (the items the device runs at once) the
+    // walk starts at the first kept tile at or after position (item mod P) / P
+    // of the item's key range and wraps around. Items are dispatched in index
+    // order at a steady rate, P at a time, so the items in flight walk the
+    // same part of the range together and share its blocks in L2. A short
+    // last key tile stays the last step, where its missing rows are masked.
+    // (Two-wave items only: split keys run them.)
+    int rot = 0, n_rot = 0;
+    if (kOwnHalf && !dense && p.phase_period > 0 && n_kept > 1) {
+      const int last = __builtin_amdgcn_readfirstlane(sel_row[n_kept - 1]);
+      n_rot = (last >= p.tk - 1 && tail_rows < KT) ? n_kept - 1 : n_kept;
+      const int span = n_ch > 1 ? p.chunk_tiles : p.tk;
+      const int target = (n_ch > 1 ? ch * p.chunk_tiles : 0) +
+                         (int)((item % p.phase_period) * span / p.phase_period);
+      int lo = 0, hi = n_rot;  // first entry >= target (the list ascends)
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (__builtin_amdgcn_readfirstlane(sel_row[mid]) < target)
+          lo = mid + 1;
+        else
+          hi = mid;
+      }
+      rot = lo < n_rot ? lo : 0;
+    }
+    auto kept_at = [&](int e) -> uint16_t {
+      int i = e;
+      if constexpr (kOwnHalf) {
+        if (e < n_rot) {
+          i = e + rot;
+          if (i >= n_rot) i -= n_rot;
+        }
+      }
+      return (uint16_t)min(max(sel_row[i], 0), p.tk - 1);
+    };
     const uint8_t* khp = (const uint8_t*)(p.k + (int64_t)h * p.ksh);
     const uint8_t* vhp = (const uint8_t*)(p.v + (int64_t)h * p.ksh);
     const bool has_lm = n_lb_all > 0;
@@ -1021,7 +1060,7 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
     if (!dense) {
       const int nw = min(kWin, n_kept);
-      for (int e = tid; e < nw; e += NT) win[e] = (uint16_t)min(max(sel_row[e], 0), p.tk - 1);
+      for (int e = tid; e < nw; e += NT) win[e] = kept_at(e);
     }
     // query operands of both query halves: Q[q][16s + 8hh .. +7]
     const int64_t qbase = (int64_t)qtile * QT + 64 * qg + qi;
@@ -1077,8 +1116,7 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
       __syncthreads();
       win_lo = t_v;
       const int nw = min(kWin, n_kept - t_v);
-      for (int e = tid; e < nw; e += NT)
-        win[e] = (uint16_t)min(max(sel_row[t_v + e], 0), p.tk - 1);
+      for (int e = tid; e < nw; e += NT) win[e] = kept_at(t_v + e);
       __syncthreads();  // no direct-to-LDS load is in flight here
     };
     // a block as a buffer resource whose records end at its last valid row
@@ -1687,6 +1725,29 @@ SplitPlan split_plan(int64_t nq, int64_t tk, int32_t heads, int32_t q_tile, int3
   return sp;
 }
 
+// Workgroups of the key-half kernel the current device runs at once (its
+// occupancy per CU times the CUs), or 0 if the runtime cannot say.
+template <int QT>
+int64_t kh_items_at_once() {
+  static std::atomic<int> per_cu{-1};
+  int nb = per_cu.load(std::memory_order_relaxed);
+  if (nb < 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, tile_sparse_kh_kernel<QT>, QT * 2, 0) !=
+        hipSuccess) {
+      (void)hipGetLastError();
+      nb = 0;
+    }
+    per_cu.store(nb, std::memory_order_relaxed);
+  }
+  int dev = 0, cus = 0;
+  if (nb == 0 || hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return (int64_t)nb * cus;
+}
+
 template <int QT, int KT>
 hipError_t launch_kernel(const SparseParams& p, const int32_t* sel, hipStream_t s) {
   // one workgroup per item (the item loop serves the rest when the grid is capped)
@@ -1694,8 +1755,13 @@ hipError_t launch_kernel(const SparseParams& p, const int32_t* sel, hipStream_t 
   // key-half kernel: 64-key tiles, 64 or 128 queries, 128-byte key rows
   if constexpr (KT == 64 && QT >= 64) {
     if (p.kst == kHeadDim) {
+      SparseParams pk = p;
+      // phase the kept-list walks of split-key launches (short walks over one
+      // chunk, many rounds of items); measured slower on whole key ranges
+      const int64_t period = p.n_chunks > 1 ? kh_items_at_once<QT>() : 0;
+      pk.phase_period = sel != nullptr && period > 0 && p.n_items >= 4 * period ? period : 0;
       hipLaunchKernelGGL((tile_sparse_kh_kernel<QT>), dim3((unsigned)grid), dim3(QT * 2), 0, s,
-                         p, sel);
+                         pk, sel);
       return hipGetLastError();
     }
   }
@@ -1767,6 +1833,7 @@ hipError_t launch_tile_sparse(const uint16_t* q, int64_t nq, int64_t qst, int64_
   p.part_o = nullptr;
   p.part_ml = nullptr;
   p.lse = lse;
+  p.phase_period = 0;
   p.top_k = top_k;
   p.scale_log2 = scale * kLog2e;
   p.o_f32 = o_f32 ? 1 : 0;

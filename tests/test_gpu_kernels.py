@@ -171,6 +171,42 @@ def test_split_keys_is_deterministic():
     assert torch.equal(outs[0], outs[1])
 
 
+def test_split_keys_phased_walks():
+    """Split keys with enough items (4 heads x 3 chunks x 500 query tiles, several
+    times what the device runs at once) that every item walks its kept tiles from
+    a phase-dependent start, wrapping around. The last chunk holds 501 tiles and
+    the short 36-token last key tile, which must stay the last step of the walks
+    that keep it. Every selection row against the oracle's pooled scores; every
+    output element of head 0 and 48 rows of the other heads that keep the short
+    tile against the oracle on the GPU's selection; two runs bitwise equal."""
+    heads, n_q, n_kv, top_k = 4, 32000, 2 * 32768 + 500 * 64 + 36, 100
+    print(f"[case] phased split keys H={heads} Nq={n_q} Nk={n_kv} top_k={top_k}", flush=True)
+    q, k, v = _clustered(31, heads, n_q, n_kv, 64, 64, 3)
+    outs = []
+    for _ in range(2):
+        bufs = stage.SparseBuffers.allocate(heads, n_q, n_kv, 64, 64, top_k, DEV)
+        stage.sparse_stage(bf16_gpu(q), bf16_gpu(k), bf16_gpu(v), 64, 64, top_k, 0.125, bufs)
+        outs.append(bufs.out.clone())
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]), "phased walks are not repeatable"
+    sel = bufs.sel.cpu().numpy()
+    scores = np.stack([zo.block_scores(zo.pool_tiles(q[h], 64), zo.pool_tiles(k[h], 64))
+                       for h in range(heads)])
+    swaps = check_selection(sel, scores, top_k)
+    ref, _ = zo.tile_sparse_attention(q[:1], k[:1], v[:1], 64, 64, top_k, 0.125, sel=sel[:1])
+    assert_close(outs[0][:1], ref, "phased split keys, head 0")
+    t_k = -(-n_kv // 64)
+    tail_rows = np.argwhere(np.any(sel[1:] == t_k - 1, axis=2))
+    print(f"[case] rows of heads 1-3 keeping the short last tile: {len(tail_rows)}", flush=True)
+    assert len(tail_rows) >= 48
+    for hh, i in tail_rows[np.random.default_rng(5).choice(len(tail_rows), 48, replace=False)]:
+        h = int(hh) + 1
+        s0, e0 = 64 * int(i), min(n_q, 64 * int(i) + 64)
+        r = zo.tile_sparse_attention_tile(q[h, s0:e0], k[h], v[h], 64, sel[h, i], 0.125)
+        assert_close(outs[0][h, s0:e0], r, f"phased split keys head {h} tile {i}")
+    print(f"[parity] near-tie swaps {swaps}", flush=True)
+
+
 @pytest.mark.parametrize("q_tile,k_tile,n_q,n_kv", [(64, 64, 300, 300), (128, 64, 130, 700),
                                                     (32, 32, 100, 65)])
 def test_dense_mode_parity(q_tile, k_tile, n_q, n_kv):
