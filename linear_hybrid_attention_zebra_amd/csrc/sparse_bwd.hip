@@ -32,6 +32,7 @@
 // (as in the forward). Sums run in a fixed order: no atomics in any
 // floating-point sum, so the gradients are bitwise reproducible.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -147,6 +148,12 @@ struct BwdParams {
   float* l_acc;            // [H][nq] sum of P', sum of P' dP (dq sweep 0)
   float* d_acc;
   float* dq_acc;           // [H][nq][64] float32 dq accumulator (dq sweep 1)
+  // phased walks (dq, and dk/dv of key tiles): 0, or the workgroups the
+  // device runs at once; an item then starts its walk of this launch's range
+  // at the first entry at or after position (item mod P) / P and wraps around,
+  // so the items in flight walk the same part of the range together (as in
+  // the forward's split keys). The walk order changes only summation order.
+  int64_t phase_period;
 };
 
 // The lanes of a 32x32 C-layout block whose row (key) is set in a uniform
@@ -429,8 +436,20 @@ __global__ __launch_bounds__(KT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     if (n_i == 0 && !p.first && !p.last) continue;  // nothing to add in this launch
     // query tile of list entry ii (a selection with repeated entries would
     // leave list slots unwritten)
+    int rot = 0;  // phased walk of the query tiles keeping this key tile
+    if constexpr (!LM) {
+      if (p.phase_period > 0 && n_i > 1) {
+        const int64_t idx = (int64_t)h * gridDim.x + cb;  // dispatch order: x, then y
+        const int target =
+            p.q_lo + (int)((idx % p.phase_period) * (p.q_hi - p.q_lo) / p.phase_period);
+        const int r = lower_bound_i32(p.list, i_base, i_base + n_i, target) - i_base;
+        rot = r < n_i ? r : 0;
+      }
+    }
     auto qtile_of = [&](int ii) -> int {
-      return LM ? i_base + ii : min(max(p.list[i_base + ii], 0), p.tq - 1);
+      if constexpr (LM) return i_base + ii;
+      const int jj = ii + rot < n_i ? ii + rot : ii + rot - n_i;
+      return min(max(p.list[i_base + jj], 0), p.tq - 1);
     };
     // stage query tile qt: rows past nq repeat the last row (masked below)
     auto issue = [&](int qt, auto stc) {
@@ -897,6 +916,13 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int n_kept = t1 - t0;
     const int n_total = n_kept + max(lb1 - lb0, 0);
     const uint32_t* brow = p.bits + row * p.bit_words;
+    int rot = 0;  // phased walk of the kept tiles
+    if (p.phase_period > 0 && n_kept > 1) {
+      const int target =
+          p.k_lo + (int)((item % p.phase_period) * (p.k_hi - p.k_lo) / p.phase_period);
+      const int r = lower_bound_i32(sel_row, t0, t1, target) - t0;
+      rot = r < n_kept ? r : 0;
+    }
     // block t of the list: kept key tile (ascending) or landmark block
     struct Blk {
       const uint16_t* kbase;
@@ -910,7 +936,8 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
       Blk r;
       r.lm = t >= n_kept;
       if (!r.lm) {
-        const int j = min(max(sel_row[t0 + t], 0), p.tk - 1);
+        const int tt = t + rot < n_kept ? t + rot : t + rot - n_kept;
+        const int j = min(max(sel_row[t0 + tt], 0), p.tk - 1);
         r.kbase = p.k + (int64_t)h * p.ksh + (int64_t)j * KT * p.kst;
         r.vbase = p.v + (int64_t)h * p.ksh + (int64_t)j * KT * p.kst;
         r.stride = p.kst;
@@ -1270,6 +1297,34 @@ BwdLayout bwd_layout(int64_t nq, int64_t nk, int32_t heads, int32_t q_tile, int3
 // and dout (dk, dv), which then stay in L2, as in the forward's split keys.
 constexpr int kChunkRows = 32768;
 
+// Workgroups of kernel K (with the given block size) the current device runs
+// at once, or 0 if the runtime cannot say.
+template <auto K, int Threads>
+int64_t wgs_at_once() {
+  static std::atomic<int> per_cu{-1};
+  int nb = per_cu.load(std::memory_order_relaxed);
+  if (nb < 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, K, Threads, 0) != hipSuccess) {
+      (void)hipGetLastError();
+      nb = 0;
+    }
+    per_cu.store(nb, std::memory_order_relaxed);
+  }
+  int dev = 0, cus = 0;
+  if (nb == 0 || hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return (int64_t)nb * cus;
+}
+
+// phase period for a launch of `items` workgroups: only when it runs many
+// rounds of them
+inline int64_t phase_for(int64_t items, int64_t at_once) {
+  return at_once > 0 && items >= 4 * at_once ? at_once : 0;
+}
+
 template <int QT, int KT>
 hipError_t launch_bwd_kernels(BwdParams p, int32_t heads, hipStream_t s) {
   hipError_t err;
@@ -1284,10 +1339,13 @@ hipError_t launch_bwd_kernels(BwdParams p, int32_t heads, hipStream_t s) {
       p.k_hi = std::min(p.tk, (c + 1) * ct);
       p.first = c == 0;
       p.last = c == nkc - 1;
-      if (sweep == 0)
+      if (sweep == 0) {
+        p.phase_period = phase_for(items, wgs_at_once<bwd_dq_kernel<QT, KT, false>, QT * 2>());
         hipLaunchKernelGGL((bwd_dq_kernel<QT, KT, false>), qgrid, dim3(QT * 2), 0, s, p);
-      else
+      } else {
+        p.phase_period = phase_for(items, wgs_at_once<bwd_dq_kernel<QT, KT, true>, QT * 2>());
         hipLaunchKernelGGL((bwd_dq_kernel<QT, KT, true>), qgrid, dim3(QT * 2), 0, s, p);
+      }
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (sweep == 0) {
@@ -1310,11 +1368,16 @@ hipError_t launch_bwd_kernels(BwdParams p, int32_t heads, hipStream_t s) {
       const dim3 grid((unsigned)nb, heads);
       // two-stage rings keep two waves per SIMD while QT <= KT (LDS)
       if constexpr (QT <= KT) {
-        if (pass == 0)
+        if (pass == 0) {
+          p.phase_period = 0;
           hipLaunchKernelGGL((bwd_dkdv_kernel<QT, KT, true>), grid, dim3(KT * 2), 0, s, p);
-        else
+        } else {
+          p.phase_period = phase_for((int64_t)nb * heads,
+                                     wgs_at_once<bwd_dkdv_kernel<QT, KT, false>, KT * 2>());
           hipLaunchKernelGGL((bwd_dkdv_kernel<QT, KT, false>), grid, dim3(KT * 2), 0, s, p);
+        }
       } else {
+        p.phase_period = 0;
         if (pass == 0)
           hipLaunchKernelGGL((bwd_dkdv_sync_kernel<QT, KT, true>), grid, dim3(KT * 2), 0, s, p);
         else
@@ -1478,6 +1541,7 @@ hipError_t launch_tile_sparse_bwd(const uint16_t* q, int64_t nq, int64_t qst, in
   p.d_acc = d_acc;
   p.dq_acc = dq_acc;
   p.q_lo = p.q_hi = p.k_lo = p.k_hi = p.first = p.last = 0;
+  p.phase_period = 0;
   if (k_tile == 64) {
     if (q_tile == 32) return launch_bwd_kernels<32, 64>(p, heads, s);
     if (q_tile == 64) return launch_bwd_kernels<64, 64>(p, heads, s);

@@ -723,6 +723,38 @@ def test_sparse_backward_multirow_bits_partial_group():
         assert_grad_close(dv[h], rv[0], f"multirow bits dv head {h}")
 
 
+def test_sparse_backward_phased_walks():
+    """dq and the key tiles' dk, dv with phased walks: 64 heads x 142 query and key
+    tiles (9,088 workgroups per launch, several times what the device runs at
+    once), so every item walks its kept tiles (dq) or the query tiles keeping
+    its key tile (dk, dv) from a phase-dependent start and wraps around; a
+    26-token last key tile is kept by some rows. Two whole heads against the
+    oracle, all three gradients, and two runs bitwise equal."""
+    heads, q_tile, k_tile, n, top_k = 64, 64, 64, 9050, 29
+    print(f"[case] sparse backward phased walks: H={heads} N={n} top_k={top_k}", flush=True)
+    q, k, v = _clustered(9052, heads, n, n, q_tile, k_tile, 3)
+    rng = np.random.default_rng(9053)
+    dout = synth.bf16_round(rng.standard_normal((heads, n, 64)).astype(np.float32))
+    qg, kg, vg = bf16_gpu(q), bf16_gpu(k), bf16_gpu(v)
+    bufs = stage.sparse_stage(qg, kg, vg, q_tile, k_tile, top_k, 0.125)
+    dg = torch.from_numpy(dout).to(DEV)
+    runs = [zb.zebra_tile_sparse_attn_backward(qg, kg, vg, bufs.kbar, bufs.vbar, bufs.sel, q_tile,
+                                               k_tile, top_k, 0.125, dg) for _ in range(2)]
+    torch.cuda.synchronize()
+    for a, b, name in zip(runs[0], runs[1], ("dq", "dk", "dv")):
+        assert torch.equal(a, b), f"phased backward {name} is not repeatable"
+    dq, dk, dv = runs[0]
+    sel = bufs.sel.cpu().numpy()
+    assert np.any(sel == -(-n // k_tile) - 1)
+    for h in (0, 63):
+        rq, rk, rv = zo.tile_sparse_attention_backward(q[h:h + 1], k[h:h + 1], v[h:h + 1],
+                                                       q_tile, k_tile, sel[h:h + 1], 0.125,
+                                                       dout[h:h + 1])
+        assert_grad_close(dq[h], rq[0], f"phased walks dq head {h}")
+        assert_grad_close(dk[h], rk[0], f"phased walks dk head {h}")
+        assert_grad_close(dv[h], rv[0], f"phased walks dv head {h}")
+
+
 def test_sparse_backward_running_max_path_and_determinism():
     """Query tiles with a loose logit bound (the forward's running-maximum path)
     and bitwise-equal gradients on a second call."""
