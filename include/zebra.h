@@ -124,11 +124,11 @@ zebra_status zebra_select_tiles(const float* qbar, const float* kbar, int32_t n_
  *          k_tile, top_k) bytes, 16-byte aligned: the landmarks as bf16 (when
  *          top_k < t_k) and per-head maxima of the key norms and value
  *          magnitudes. For long key ranges with q_tile <= 64 (at least
- *          2 x 32768 keys, top_k < t_k) the keys are processed in chunks and
- *          the workspace also holds float32 partial outputs,
- *          H x Nq x chunks x 264 bytes, at most 64 GiB (60 GiB for 16 heads
- *          of 703,488 tokens). Never 0; the contents on return are
- *          unspecified.
+ *          2 x 32768 keys, top_k < t_k) the keys are processed in chunks of
+ *          32768 keys (65536 from 4 x 65536 keys on) and the workspace also
+ *          holds float32 partial outputs, H x Nq x chunks x 264 bytes, at
+ *          most 64 GiB (30.4 GiB for 16 heads of 703,488 tokens). Never 0;
+ *          the contents on return are unspecified.
  * The key/value token stride must be at most 2^24 elements
  * (ZEBRA_ERR_UNSUPPORTED otherwise).
  */

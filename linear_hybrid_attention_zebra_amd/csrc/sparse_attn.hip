@@ -1688,8 +1688,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Keys per chunk of the split-key decomposition: K and V of one chunk of one
-// head take kChunkKeys * 256 bytes.
+// head take kChunkKeys * 256 bytes. Ranges of at least four long chunks use
+// the long ones: with phased walks the items in flight share a window of the
+// chunk, not the whole chunk, so fewer chunks save partials and per-item work
+// (measured at 512 views: 65,536 keys 3% faster than 32,768 or 98,304).
 constexpr int64_t kChunkKeys = 32768;
+constexpr int64_t kChunkKeysLong = 65536;
 // Partial outputs take at most this much workspace; longer ranges use fewer,
 // larger chunks.
 constexpr double kMaxPartialBytes = 64.0 * (1ull << 30);
@@ -1706,7 +1710,7 @@ SplitPlan split_plan(int64_t nq, int64_t tk, int32_t heads, int32_t q_tile, int3
                      int32_t top_k) {
   SplitPlan sp;
   if (top_k >= tk || q_tile > 64) return sp;
-  int64_t ct = kChunkKeys / k_tile;
+  int64_t ct = (tk * k_tile >= 4 * kChunkKeysLong ? kChunkKeysLong : kChunkKeys) / k_tile;
   const double per_chunk = (double)heads * nq * (kHeadDim + 2) * sizeof(float);
   const int64_t max_chunks = (int64_t)(kMaxPartialBytes / per_chunk);
   if (max_chunks < 2 || tk < 2 * ct) return sp;
