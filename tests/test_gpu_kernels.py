@@ -207,6 +207,41 @@ def test_split_keys_phased_walks():
     print(f"[parity] near-tie swaps {swaps}", flush=True)
 
 
+def test_split_keys_long_chunks_phased_walks():
+    """Key ranges of at least 4 x 65,536 keys split into 65,536-key chunks (here 4 of
+    1,024 tiles and one of 301 ending in a 36-token tile), with phased walks (2
+    heads x 5 chunks x 410 query tiles). Every selection row against the oracle's
+    pooled scores; 24 rows that keep the short last tile and 24 other rows against
+    the oracle on the GPU's selection; two runs bitwise equal."""
+    heads, n_q, n_kv, top_k = 2, 410 * 64, 4 * 65536 + 300 * 64 + 36, 220
+    print(f"[case] long-chunk split keys H={heads} Nq={n_q} Nk={n_kv} top_k={top_k}", flush=True)
+    q, k, v = _clustered(37, heads, n_q, n_kv, 64, 64, 3)
+    outs = []
+    for _ in range(2):
+        bufs = stage.SparseBuffers.allocate(heads, n_q, n_kv, 64, 64, top_k, DEV)
+        stage.sparse_stage(bf16_gpu(q), bf16_gpu(k), bf16_gpu(v), 64, 64, top_k, 0.125, bufs)
+        outs.append(bufs.out.clone())
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]), "long-chunk phased walks are not repeatable"
+    sel = bufs.sel.cpu().numpy()
+    scores = np.stack([zo.block_scores(zo.pool_tiles(q[h], 64), zo.pool_tiles(k[h], 64))
+                       for h in range(heads)])
+    swaps = check_selection(sel, scores, top_k)
+    t_k = -(-n_kv // 64)
+    keeps = np.any(sel == t_k - 1, axis=2)
+    rng = np.random.default_rng(38)
+    tail_rows, other_rows = np.argwhere(keeps), np.argwhere(~keeps)
+    print(f"[case] rows keeping the short last tile: {len(tail_rows)}", flush=True)
+    assert len(tail_rows) >= 24
+    rows = np.concatenate([tail_rows[rng.choice(len(tail_rows), 24, replace=False)],
+                           other_rows[rng.choice(len(other_rows), 24, replace=False)]])
+    for h, i in rows:
+        s0 = 64 * int(i)
+        r = zo.tile_sparse_attention_tile(q[h, s0:s0 + 64], k[h], v[h], 64, sel[h, i], 0.125)
+        assert_close(outs[0][h, s0:s0 + 64], r, f"long-chunk split keys head {h} tile {i}")
+    print(f"[parity] near-tie swaps {swaps}", flush=True)
+
+
 @pytest.mark.parametrize("q_tile,k_tile,n_q,n_kv", [(64, 64, 300, 300), (128, 64, 130, 700),
                                                     (32, 32, 100, 65)])
 def test_dense_mode_parity(q_tile, k_tile, n_q, n_kv):
