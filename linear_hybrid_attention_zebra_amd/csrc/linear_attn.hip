@@ -35,7 +35,11 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlockTok = 64;
 constexpr int kStateFloats = kHeadDim * kHeadDim + kHeadDim;  // S then z
-constexpr int kTargetStateBlocks = 2048;
+// State workgroups per launch (all heads): one round of the 4 workgroups per
+// CU the kernel's registers allow on 256 CUs. Measured at 512 views: 1,024
+// ran 2.6% faster than 2,048 and faster than 768, 1,280 or 1,536 (a partial
+// second round); the fp64 reduce sums the partials in chunk order either way.
+constexpr int kTargetStateBlocks = 1024;
 
 // Byte offset of 16-byte chunk `chunk` of 128-byte row `row`: chunks are
 // XORed with a function of the row that keeps the transposed operand reads
@@ -403,9 +407,12 @@ hipError_t launch_linear(const uint16_t* q, int64_t nq, int64_t qst, int64_t qsh
   float* state = nullptr;
   hipError_t err = launch_linear_state(k, v, nk, kst, ksh, heads, ws, &state, s);
   if (err != hipSuccess) return err;
-  // about 2 workgroups of 4 waves per CU per head group; each wave loops over
-  // 32-query steps with the next step's loads in flight
-  const int64_t per_block = std::max<int64_t>(512, ((nq * heads + 4095) / 4096 + 127) / 128 * 128);
+  // about 32,768 workgroups of 4 waves over all heads (8 rounds of the 4 per CU
+  // the registers allow); each wave loops over 32-query steps with the next
+  // step's loads in flight. Measured at 512 views against 4,096 workgroups:
+  // 8,192 -2.3%, 16,384 -5%, 32,768 -6.4%, one 128-query step each (88k) +2.5%.
+  const int64_t per_block =
+      std::max<int64_t>(128, ((nq * heads + 32767) / 32768 + 127) / 128 * 128);
   const int64_t nblocks = (nq + per_block - 1) / per_block;
   hipLaunchKernelGGL(linear_apply_kernel, dim3((unsigned)nblocks, heads), dim3(256), 0, s, q, nq,
                      qst, qsh, state, aff_scale, aff_bias, per_block, o, ost, osh, o_f32 ? 1 : 0);
