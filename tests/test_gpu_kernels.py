@@ -171,15 +171,17 @@ def test_split_keys_is_deterministic():
     assert torch.equal(outs[0], outs[1])
 
 
-def test_split_keys_phased_walks():
+@pytest.mark.parametrize("top_k", [100, 2])
+def test_split_keys_phased_walks(top_k):
     """Split keys with enough items (4 heads x 3 chunks x 500 query tiles, several
     times what the device runs at once) that every item walks its kept tiles from
-    a phase-dependent start, wrapping around. The last chunk holds 501 tiles and
-    the short 36-token last key tile, which must stay the last step of the walks
-    that keep it. Every selection row against the oracle's pooled scores; every
-    output element of head 0 and 48 rows of the other heads that keep the short
+    a phase-dependent start, wrapping around (top_k 2: most chunks keep at most
+    one tile and do not rotate). The last chunk holds 501 tiles and the short
+    36-token last key tile, which must stay the last step of the walks that keep
+    it. Every selection row against the oracle's pooled scores; every output
+    element of head 0 and up to 48 rows of the other heads that keep the short
     tile against the oracle on the GPU's selection; two runs bitwise equal."""
-    heads, n_q, n_kv, top_k = 4, 32000, 2 * 32768 + 500 * 64 + 36, 100
+    heads, n_q, n_kv = 4, 32000, 2 * 32768 + 500 * 64 + 36
     print(f"[case] phased split keys H={heads} Nq={n_q} Nk={n_kv} top_k={top_k}", flush=True)
     q, k, v = _clustered(31, heads, n_q, n_kv, 64, 64, 3)
     outs = []
@@ -198,8 +200,9 @@ def test_split_keys_phased_walks():
     t_k = -(-n_kv // 64)
     tail_rows = np.argwhere(np.any(sel[1:] == t_k - 1, axis=2))
     print(f"[case] rows of heads 1-3 keeping the short last tile: {len(tail_rows)}", flush=True)
-    assert len(tail_rows) >= 48
-    for hh, i in tail_rows[np.random.default_rng(5).choice(len(tail_rows), 48, replace=False)]:
+    assert len(tail_rows) >= (48 if top_k > 50 else 1)
+    n_pick = min(48, len(tail_rows))
+    for hh, i in tail_rows[np.random.default_rng(5).choice(len(tail_rows), n_pick, replace=False)]:
         h = int(hh) + 1
         s0, e0 = 64 * int(i), min(n_q, 64 * int(i) + 64)
         r = zo.tile_sparse_attention_tile(q[h, s0:e0], k[h], v[h], 64, sel[h, i], 0.125)
