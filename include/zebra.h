@@ -212,7 +212,7 @@ zebra_status zebra_linear_attn(const void* q, zebra_seq qs, const void* k, const
  * The call allocates nothing and frees nothing.
  *
  * Limit: zebra_linear_attn_workspace(Nk, H, 64) must not exceed that size
- * (true for up to 64 heads at any length); otherwise ZEBRA_ERR_WORKSPACE,
+ * (true for up to 840 heads at any length); otherwise ZEBRA_ERR_WORKSPACE,
  * before any HIP call. Every call on one GPU shares that GPU's array and the
  * kernels overwrite it entirely (nothing must start at zero); calls that
  * overlap in time on one GPU (two streams, two threads) race on it and must

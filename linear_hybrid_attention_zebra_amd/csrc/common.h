@@ -130,7 +130,7 @@ hipError_t launch_permute(const void* src, int64_t s_tok, int64_t s_head, void* 
 hipError_t launch_fit(const float* x, const float* y, int32_t m, int32_t heads, float* a,
                       float* b, int32_t* n_deg, bool centred, hipStream_t s);
 // Size of the fixed device scratch of the allocation-free linear-attention
-// entry point (40 MiB: the linear workspace of up to 64 heads at any length).
+// entry point (40 MiB: the linear workspace of up to 840 heads at any length).
 constexpr size_t kNoAllocScratchBytes = size_t(40) << 20;
 // The current device's scratch array (device address, taken once per device).
 hipError_t noalloc_scratch(void** out);
