@@ -171,8 +171,9 @@ def test_split_keys_is_deterministic():
     assert torch.equal(outs[0], outs[1])
 
 
-@pytest.mark.parametrize("top_k", [100, 2])
-def test_split_keys_phased_walks(top_k):
+@pytest.mark.parametrize("top_k,q_mul", [(100, 1.0), (2, 1.0), (100, 8.0)],
+                         ids=["k100", "k2", "k100-running-max"])
+def test_split_keys_phased_walks(top_k, q_mul):
     """Split keys with enough items (4 heads x 3 chunks x 500 query tiles, several
     times what the device runs at once) that every item walks its kept tiles from
     a phase-dependent start, wrapping around (top_k 2: most chunks keep at most
@@ -180,10 +181,14 @@ def test_split_keys_phased_walks(top_k):
     36-token last key tile, which must stay the last step of the walks that keep
     it. Every selection row against the oracle's pooled scores; every output
     element of head 0 and up to 48 rows of the other heads that keep the short
-    tile against the oracle on the GPU's selection; two runs bitwise equal."""
+    tile against the oracle on the GPU's selection; two runs bitwise equal. With the
+    queries times 8 (exact in bf16) every item's logit bound exceeds the fixed-
+    reference limit and the walks run on the running-maximum path."""
     heads, n_q, n_kv = 4, 32000, 2 * 32768 + 500 * 64 + 36
-    print(f"[case] phased split keys H={heads} Nq={n_q} Nk={n_kv} top_k={top_k}", flush=True)
+    print(f"[case] phased split keys H={heads} Nq={n_q} Nk={n_kv} top_k={top_k} "
+          f"q x{q_mul:g}", flush=True)
     q, k, v = _clustered(31, heads, n_q, n_kv, 64, 64, 3)
+    q = synth.bf16_round(q * np.float32(q_mul))
     outs = []
     for _ in range(2):
         bufs = stage.SparseBuffers.allocate(heads, n_q, n_kv, 64, 64, top_k, DEV)
