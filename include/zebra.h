@@ -126,8 +126,10 @@ zebra_status zebra_select_tiles(const float* qbar, const float* kbar, int32_t n_
  *          magnitudes. For long key ranges with q_tile <= 64 (at least
  *          2 x 32768 keys, top_k < t_k) the keys are processed in chunks of
  *          32768 keys (65536 from 4 x 65536 keys on) and the workspace also
- *          holds float32 partial outputs, H x Nq x chunks x 264 bytes, at
- *          most 64 GiB (30.4 GiB for 16 heads of 703,488 tokens). Never 0;
+ *          holds float32 partial outputs, H x Nq x slots x 264 bytes, one
+ *          slot per chunk plus, for 64-query and 64-key tiles with
+ *          landmarks, one for the landmark columns; at most 64 GiB
+ *          (33.2 GiB for 16 heads of 703,488 tokens). Never 0;
  *          the contents on return are unspecified.
  * The key/value token stride must be at most 2^24 elements
  * (ZEBRA_ERR_UNSUPPORTED otherwise).

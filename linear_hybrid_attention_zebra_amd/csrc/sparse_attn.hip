@@ -115,6 +115,11 @@ struct SparseParams {
   // kept-list walk phase (key-half kernel): 0, or the number of items the
   // device runs at once (see the kernel)
   int64_t phase_period;
+  // split keys: partial slots per query (n_chunks, plus one for the landmark
+  // columns when a separate landmark pass computes them: lm_separate, and the
+  // key-chunk items then skip their landmark blocks)
+  int32_t part_slots, lm_separate;
+  int32_t tq_sel;          // landmark-only pass: 64-query tiles (selection rows) per head
 };
 
 // Byte offset of 16-byte chunk `chunk` of 128-byte row `row` in a tile. The
@@ -829,7 +834,7 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
     const float l_sum = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
     if (n_ch > 1) {  // split keys: unnormalised partial and (reference, row sum)
       if (qvalid) {
-        const int64_t prow = ((int64_t)h * p.nq + qrow) * n_ch + ch;
+        const int64_t prow = ((int64_t)h * p.nq + qrow) * p.part_slots + ch;
         float* op = p.part_o + prow * kHeadDim + 4 * hh;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
@@ -882,7 +887,18 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(QT >= 64
 // partial output, row sum and reference to its partner. With the fixed
 // reference both partials share it and simply add; on the fallback path each
 // is first scaled to the larger of the two running maxima.
-template <int QT>
+// The second query group's kept-tile bitmap of the landmark-only pass
+// (function-local, so only that instantiation holds it in LDS).
+__device__ __forceinline__ uint32_t* lm_bits_second() {
+  __shared__ uint32_t bits[kBitWords];
+  return bits;
+}
+
+// kLmOnly (128-query tiles, split keys): an item is one (head, pair of 64-query
+// tiles) over every landmark block of the head, query group qg masked by the
+// kept tiles of 64-query tile 2 g + qg; it writes the landmark columns'
+// unnormalised output and (reference, row sum) into the last partial slot.
+template <int QT, bool kLmOnly>
 __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) void tile_sparse_kh_kernel(
     SparseParams p, const int32_t* __restrict__ sel) {
   constexpr int KT = 64;
@@ -891,6 +907,7 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
   constexpr int KB_PER_TILE = KT * 128 / 1024;
   constexpr int NU = KB_PER_TILE / W;    // 1 KB direct-to-LDS pieces per wave per tensor
   static_assert(KB_PER_TILE % W == 0 && W >= 2, "load split");
+  static_assert(!kLmOnly || QT == 128, "landmark-only items are 128-query pairs");
 
   __shared__ u32x4 ks0[KB_PER_TILE][64], ks1[KB_PER_TILE][64];
   __shared__ u32x4 vs0[KB_PER_TILE][64], vs1[KB_PER_TILE][64];
@@ -994,19 +1011,28 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     void* o_arg = p.o;
     float* part_o_arg = p.part_o;
     asm volatile("" : "+s"(q_arg), "+s"(range_arg), "+s"(o_arg), "+s"(part_o_arg));
-    const int h = (int)(item / items_per_head);
-    const int64_t rem = item - (int64_t)h * items_per_head;
-    const int ch = (int)(rem / p.tq);
-    const int qtile = (int)(rem - (int64_t)ch * p.tq);
+    const int h = (int)(item / (kLmOnly ? (int64_t)p.tq : items_per_head));
+    const int64_t rem = item - (int64_t)h * (kLmOnly ? (int64_t)p.tq : items_per_head);
+    const int ch = kLmOnly ? p.part_slots - 1 : (int)(rem / p.tq);
+    const int qtile = kLmOnly ? (int)rem : (int)(rem - (int64_t)ch * p.tq);
     const int64_t row = (int64_t)h * p.tq + qtile;
     int kept0 = 0, n_kept = dense ? p.tk : p.top_k, lb0 = 0, n_lb = n_lb_all;
-    if (n_ch > 1) {
+    if constexpr (kLmOnly) {
+      n_kept = 0;  // every landmark block, masked per query group below
+    } else if (n_ch > 1) {
       const int32_t* co = p.coff + row * (n_ch + 1) + ch;
       kept0 = __builtin_amdgcn_readfirstlane(co[0]);
       n_kept = max(__builtin_amdgcn_readfirstlane(co[1]) - kept0, 0);
       lb0 = ch * lb_per_chunk;
-      n_lb = n_lb_all > 0 ? min(lb_per_chunk, n_lb_all - lb0) : 0;
+      // (only two-wave items hand their landmark blocks to the separate pass)
+      n_lb = n_lb_all > 0 && !(kOwnHalf && p.lm_separate) ? min(lb_per_chunk, n_lb_all - lb0) : 0;
     }
+    // the selection rows of the pair's two 64-query tiles (landmark-only pass)
+    const int64_t lm_row0 = (int64_t)h * p.tq_sel + min(2 * qtile, p.tq_sel - 1);
+    const int64_t lm_row1 = (int64_t)h * p.tq_sel + min(2 * qtile + 1, p.tq_sel - 1);
+    // this wave's kept-tile bitmap (its query group's, in the landmark-only pass)
+    uint32_t* my_bits = kept_bits;
+    if constexpr (kLmOnly) my_bits = qg == 0 ? kept_bits : lm_bits_second();
     const int n_total = n_kept + n_lb;
     const int32_t* sel_row = dense ? nullptr : sel + row * p.top_k + kept0;
     // Walk order of the kept list. Any order gives the same softmax up to
@@ -1057,6 +1083,8 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     if (n_lb > 0) {
       const int words = 2 * n_lb;
       for (int e = tid; e < words; e += NT) kept_bits[2 * lb0 + e] = 0u;
+      if constexpr (kLmOnly)
+        for (int e = tid; e < words; e += NT) lm_bits_second()[e] = 0u;
     }
     if (!dense) {
       const int nw = min(kWin, n_kept);
@@ -1083,11 +1111,19 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int last_kept =
         dense ? p.tk - 1 : (n_kept > 0 ? min(max(sel_row[n_kept - 1], 0), p.tk - 1) : -1);
     __syncthreads();
-    if (n_lb > 0)
+    if constexpr (kLmOnly) {
+      for (int e = tid; e < 2 * p.top_k; e += NT) {
+        const int g = e >= p.top_k;
+        const int j = min(max(sel[(g ? lm_row1 : lm_row0) * p.top_k + e - g * p.top_k], 0),
+                          p.tk - 1);
+        atomicOr(&(g ? lm_bits_second() : kept_bits)[j >> 5], 1u << (j & 31));
+      }
+    } else if (n_lb > 0) {
       for (int e = tid; e < n_kept; e += NT) {
         const int j = min(max(sel_row[e], 0), p.tk - 1);
         atomicOr(&kept_bits[j >> 5], 1u << (j & 31));
       }
+    }
     k2 = wave_max(k2);
     vmax = wave_max(vmax);
     float m_q[2], nm_fast[2];
@@ -1142,8 +1178,8 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     auto block_mask = [&](int t) -> uint64_t {
       if (t < n_kept) return t == n_kept - 1 && last_rows < KT ? ~0ull << last_rows : 0ull;
       const int b = lb0 + t - n_kept;
-      const uint32_t lo = __builtin_amdgcn_readfirstlane(kept_bits[2 * b]);
-      const uint32_t hi = __builtin_amdgcn_readfirstlane(kept_bits[2 * b + 1]);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane(my_bits[2 * b]);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane(my_bits[2 * b + 1]);
       uint64_t m = ((uint64_t)hi << 32) | lo;
       if (b == n_lb_all - 1 && last_lrows < KT) m |= ~0ull << last_lrows;
       return m;
@@ -1550,8 +1586,10 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
       if (l_sum == 0.f) ref = r_mine;  // no columns at all (split keys, no landmarks)
       const int64_t qrow = qbase + 32 * kh;
       if (qrow >= p.nq) return;
-      if (n_ch > 1) {  // split keys: unnormalised partial and (reference, row sum)
-        const int64_t prow = ((int64_t)h * p.nq + qrow) * n_ch + ch;
+      if (kLmOnly || n_ch > 1) {  // split keys: unnormalised partial, (reference, row sum)
+        // (four-wave key-chunk items are never split: their stride stays n_ch)
+        const int slots = kOwnHalf || kLmOnly ? p.part_slots : n_ch;
+        const int64_t prow = ((int64_t)h * p.nq + qrow) * slots + ch;
         float* op = part_o_arg + prow * kHeadDim + 4 * hh;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
@@ -1712,7 +1750,8 @@ SplitPlan split_plan(int64_t nq, int64_t tk, int32_t heads, int32_t q_tile, int3
   if (top_k >= tk || q_tile > 64) return sp;
   int64_t ct = (tk * k_tile >= 4 * kChunkKeysLong ? kChunkKeysLong : kChunkKeys) / k_tile;
   const double per_chunk = (double)heads * nq * (kHeadDim + 2) * sizeof(float);
-  const int64_t max_chunks = (int64_t)(kMaxPartialBytes / per_chunk);
+  // one partial slot per chunk, plus one for the landmark columns
+  const int64_t max_chunks = (int64_t)(kMaxPartialBytes / per_chunk) - 1;
   if (max_chunks < 2 || tk < 2 * ct) return sp;
   int64_t nc = (tk + ct - 1) / ct;
   if (nc > max_chunks) {  // widen the chunks to a multiple of k_tile landmark rows
@@ -1724,8 +1763,8 @@ SplitPlan split_plan(int64_t nq, int64_t tk, int32_t heads, int32_t q_tile, int3
   sp.n_chunks = (int32_t)nc;
   sp.chunk_tiles = (int32_t)ct;
   sp.coff = align256((size_t)heads * tq * (nc + 1) * sizeof(int32_t));
-  sp.part_o = align256((size_t)heads * nq * nc * kHeadDim * sizeof(float));
-  sp.part_ml = align256((size_t)heads * nq * nc * sizeof(float2));
+  sp.part_o = align256((size_t)heads * nq * (nc + 1) * kHeadDim * sizeof(float));
+  sp.part_ml = align256((size_t)heads * nq * (nc + 1) * sizeof(float2));
   return sp;
 }
 
@@ -1736,7 +1775,8 @@ int64_t kh_items_at_once() {
   static std::atomic<int> per_cu{-1};
   int nb = per_cu.load(std::memory_order_relaxed);
   if (nb < 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, tile_sparse_kh_kernel<QT>, QT * 2, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, tile_sparse_kh_kernel<QT, false>, QT * 2,
+                                                     0) !=
         hipSuccess) {
       (void)hipGetLastError();
       nb = 0;
@@ -1764,7 +1804,7 @@ hipError_t launch_kernel(const SparseParams& p, const int32_t* sel, hipStream_t 
       // chunk, many rounds of items); measured slower on whole key ranges
       const int64_t period = p.n_chunks > 1 ? kh_items_at_once<QT>() : 0;
       pk.phase_period = sel != nullptr && period > 0 && p.n_items >= 4 * period ? period : 0;
-      hipLaunchKernelGGL((tile_sparse_kh_kernel<QT>), dim3((unsigned)grid), dim3(QT * 2), 0, s,
+      hipLaunchKernelGGL((tile_sparse_kh_kernel<QT, false>), dim3((unsigned)grid), dim3(QT * 2), 0, s,
                          pk, sel);
       return hipGetLastError();
     }
@@ -1838,6 +1878,9 @@ hipError_t launch_tile_sparse(const uint16_t* q, int64_t nq, int64_t qst, int64_
   p.part_ml = nullptr;
   p.lse = lse;
   p.phase_period = 0;
+  p.part_slots = 1;
+  p.lm_separate = 0;
+  p.tq_sel = p.tq;
   p.top_k = top_k;
   p.scale_log2 = scale * kLog2e;
   p.o_f32 = o_f32 ? 1 : 0;
@@ -1884,16 +1927,33 @@ hipError_t launch_tile_sparse(const uint16_t* q, int64_t nq, int64_t qst, int64_
   p.part_o = (float*)(w + sp.coff);
   p.part_ml = (float2*)(w + sp.coff + sp.part_o);
   p.n_items = (int64_t)heads * sp.n_chunks * p.tq;
+  // the key-half kernel's 64-query items leave their landmark blocks to one
+  // pass of 128-query items (pairs of query tiles) over all landmark rows, which
+  // halves the landmark blocks' gathers; its partial takes the last slot
+  const bool lm_pass = p.landmarks && q_tile == 64 && k_tile == 64 && kst == kHeadDim;
+  p.lm_separate = lm_pass ? 1 : 0;
+  p.part_slots = sp.n_chunks + (lm_pass ? 1 : 0);
   const int64_t rows = (int64_t)heads * p.tq;
   const int64_t n_off = rows * (sp.n_chunks + 1);
   hipLaunchKernelGGL(chunk_offsets_kernel, dim3((unsigned)((n_off + 255) / 256)), dim3(256), 0, s,
                      sel, rows, top_k, sp.n_chunks, sp.chunk_tiles, (int32_t*)w);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if ((err = launch_tiles(p, sel, q_tile, k_tile, s)) != hipSuccess) return err;
+  if (lm_pass) {
+    SparseParams pl = p;
+    pl.tq_sel = p.tq;
+    pl.tq = (p.tq + 1) / 2;  // pairs of 64-query tiles
+    pl.n_items = (int64_t)heads * pl.tq;
+    pl.phase_period = 0;
+    hipLaunchKernelGGL((tile_sparse_kh_kernel<128, true>),
+                       dim3((unsigned)std::min<int64_t>(pl.n_items, (int64_t)1 << 24)), dim3(256),
+                       0, s, pl, sel);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   const int64_t qrows = (int64_t)heads * nq;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((qrows + 15) / 16)), dim3(256), 0, s,
-                     (const float*)p.part_o, (const float2*)p.part_ml, sp.n_chunks, nq, qrows, o,
-                     ost, osh, p.o_f32, lse);
+                     (const float*)p.part_o, (const float2*)p.part_ml, p.part_slots, nq, qrows,
+                     o, ost, osh, p.o_f32, lse);
   return hipGetLastError();
 }
 
