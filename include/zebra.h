@@ -256,7 +256,9 @@ zebra_status zebra_fit_affine(const float* x, const float* y, int32_t m, int32_t
  *   dq = scale sum_c dS_c k_c,  dk_c = scale dS_c q,  dv_c = P_c dout,
  * and every token of tile j receives 1/n_j of its landmark column's dk and
  * dv (the landmark is the tile mean). The call runs the forward itself (its
- * float32 output and normaliser go to the workspace); dout enters the bf16
+ * float32 output and normaliser go to the workspace) and takes D from that
+ * float32 output and the bf16-rounded dout; P comes from the normaliser as
+ * the forward summed it (bf16-rounded probabilities). dout enters the bf16
  * MFMA products rounded to bf16, sums are float32 in a fixed order
  * (deterministic). sel is required (also when top_k == t_k).
  *
@@ -282,11 +284,14 @@ zebra_status zebra_tile_sparse_attn_backward(
 /*
  * zebra_tile_sparse_attn_backward with the normaliser lse of an earlier
  * zebra_tile_sparse_attn_lse call on the same q, k, v, landmarks, selection,
- * tiles, scale and flags: the call then does not run the forward itself (it
- * packs the landmarks and copies lse into its workspace; its first sweep
- * renormalises that copy). The gradients are bitwise those of
- * zebra_tile_sparse_attn_backward. lse: float32 [H][Nq], contiguous, 4-byte
- * aligned, read only. Workspace: zebra_tile_sparse_attn_backward_workspace.
+ * tiles, scale and flags, for a forward whose output was bf16: the call
+ * then does not run the forward itself (it packs the landmarks and copies lse
+ * into its workspace). Without a float32 output at hand, a first pass over
+ * every query's columns forms D = sum_c P_c dP_c and renormalises the copy of
+ * lse so that the float32 P_c sum to one. The gradients agree with
+ * zebra_tile_sparse_attn_backward to rounding (not bitwise). lse: float32
+ * [H][Nq], contiguous, 4-byte aligned, read only. Workspace:
+ * zebra_tile_sparse_attn_backward_workspace.
  */
 zebra_status zebra_tile_sparse_attn_backward_lse(
     const void* q, zebra_seq qs, const void* k, const void* v, zebra_seq kvs, const float* kbar,
@@ -294,6 +299,28 @@ zebra_status zebra_tile_sparse_attn_backward_lse(
     float scale, uint32_t flags, const float* lse, const void* dout, zebra_seq dos,
     zebra_dtype g_dtype, void* dq, zebra_seq dqs, void* dk, void* dv, zebra_seq dkvs,
     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * zebra_tile_sparse_attn_backward from both saved results of an earlier
+ * zebra_tile_sparse_attn_lse call with o_dtype ZEBRA_F32 on the same q, k, v,
+ * landmarks, selection, tiles, scale and flags: its normaliser lse and its
+ * float32 output out (os). The call does not run the forward; D comes from
+ * out as in zebra_tile_sparse_attn_backward, so the gradients are bitwise
+ * those of zebra_tile_sparse_attn_backward, with one pass over each query's
+ * columns instead of the two of zebra_tile_sparse_attn_backward_lse (for a
+ * training step that keeps the forward's output in float32; Zebra3D paper
+ * page, Tables 18-19). lse: float32 [H][Nq], contiguous, 4-byte aligned.
+ * out: float32 [H][Nq][64] with 16-byte aligned rows (ZEBRA_ERR_UNSUPPORTED
+ * otherwise). Both are read only and must not overlap an output
+ * (ZEBRA_ERR_INVALID_ARG); both are required unless Nq or H is 0. Workspace:
+ * zebra_tile_sparse_attn_backward_workspace.
+ */
+zebra_status zebra_tile_sparse_attn_backward_saved(
+    const void* q, zebra_seq qs, const void* k, const void* v, zebra_seq kvs, const float* kbar,
+    const float* vbar, const int32_t* sel, int32_t q_tile, int32_t k_tile, int32_t top_k,
+    float scale, uint32_t flags, const float* lse, const float* out, zebra_seq os,
+    const void* dout, zebra_seq dos, zebra_dtype g_dtype, void* dq, zebra_seq dqs, void* dk,
+    void* dv, zebra_seq dkvs, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Gradients of one linear stage (for the optional refinement of a converted

@@ -33,6 +33,7 @@ ENTRY_POINTS = (
     "zebra_pool_landmarks", "zebra_select_tiles_workspace", "zebra_select_tiles",
     "zebra_tile_sparse_attn_workspace", "zebra_tile_sparse_attn", "zebra_tile_sparse_attn_ex",
     "zebra_tile_sparse_attn_lse", "zebra_tile_sparse_attn_backward_lse",
+    "zebra_tile_sparse_attn_backward_saved",
     "zebra_linear_attn_workspace", "zebra_linear_attn", "zebra_linear_attn_noalloc_max_bytes",
     "zebra_linear_attn_noalloc", "zebra_fit_affine", "zebra_fit_scale_only",
     "zebra_block_mass_workspace", "zebra_block_mass", "zebra_spatial_order",
@@ -87,6 +88,11 @@ def _declare(lib):
                                                         ctypes.c_uint32, c_p, c_p, ZebraSeq, c_i32,
                                                         c_p, ZebraSeq, c_p, c_p, ZebraSeq, c_p,
                                                         c_sz, c_p]),
+        "zebra_tile_sparse_attn_backward_saved": (c_i32, [c_p, ZebraSeq, c_p, c_p, ZebraSeq,
+                                                          c_p, c_p, c_p, c_i32, c_i32, c_i32, c_f,
+                                                          ctypes.c_uint32, c_p, c_p, ZebraSeq,
+                                                          c_p, ZebraSeq, c_i32, c_p, ZebraSeq,
+                                                          c_p, c_p, ZebraSeq, c_p, c_sz, c_p]),
         "zebra_linear_attn_workspace": (c_sz, [c_i64, c_i32, c_i32]),
         "zebra_linear_attn": (c_i32, [c_p, ZebraSeq, c_p, c_p, ZebraSeq, c_p, c_p, c_p, ZebraSeq,
                                       c_i32, c_p, c_sz, c_p]),
@@ -456,11 +462,14 @@ def zebra_tile_sparse_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.T
                                     sel: torch.Tensor, q_tile: int, k_tile: int, top_k: int,
                                     scale: float, dout: torch.Tensor, flags: int = 0,
                                     workspace: Optional[torch.Tensor] = None,
-                                    lse: Optional[torch.Tensor] = None):
+                                    lse: Optional[torch.Tensor] = None,
+                                    out: Optional[torch.Tensor] = None):
     """Gradients (dq, dk, dv) of sum(dout * out) for one tile-sparse stage, sel fixed;
     the gradients take dout's dtype (bfloat16 or float32). With lse, the normaliser a
     forward call wrote (zebra_tile_sparse_attn_ex with lse_out), the call does not
-    run the forward again (zebra_tile_sparse_attn_backward_lse)."""
+    run the forward again: with that call's float32 output as out too, through
+    zebra_tile_sparse_attn_backward_saved (bitwise the plain backward), else through
+    zebra_tile_sparse_attn_backward_lse."""
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, torch.bfloat16, name)
     _need(sel, torch.int32, "sel")
@@ -479,10 +488,21 @@ def zebra_tile_sparse_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.T
                                                            HEAD_DIM, q_tile, k_tile, top_k)
     workspace = _workspace(nbytes, q.device, workspace)
     g_dtype = ZEBRA_F32 if dout.dtype == torch.float32 else ZEBRA_BF16
+    if out is not None and lse is None:
+        raise ValueError("out is read only together with lse")
     if lse is not None:
         _need(lse, torch.float32, "lse")
         if not lse.is_contiguous() or lse.numel() != q.shape[0] * q.shape[1]:
             raise ValueError("lse must be a contiguous [H][Nq] float32 tensor")
+    if out is not None:
+        _need(out, torch.float32, "out")
+        _check("zebra_tile_sparse_attn_backward_saved", lib.zebra_tile_sparse_attn_backward_saved(
+            _ptr(q), seq_of(q), _ptr(k), _ptr(v), seq_of(k), _ptr(kbar), _ptr(vbar), _ptr(sel),
+            q_tile, k_tile, top_k, scale, flags, _ptr(lse), _ptr(out), seq_of(out), _ptr(dout),
+            seq_of(dout), g_dtype, _ptr(dq), seq_of(dq), _ptr(dk), _ptr(dv), seq_of(dk),
+            _ptr(workspace), nbytes, _stream(q.device)))
+        return dq, dk, dv
+    if lse is not None:
         _check("zebra_tile_sparse_attn_backward_lse", lib.zebra_tile_sparse_attn_backward_lse(
             _ptr(q), seq_of(q), _ptr(k), _ptr(v), seq_of(k), _ptr(kbar), _ptr(vbar), _ptr(sel),
             q_tile, k_tile, top_k, scale, flags, _ptr(lse), _ptr(dout), seq_of(dout), g_dtype,

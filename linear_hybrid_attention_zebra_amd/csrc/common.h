@@ -98,7 +98,8 @@ hipError_t launch_tile_sparse_bwd(const uint16_t* q, int64_t nq, int64_t qst, in
                                   const void* dout, int64_t dst, int64_t dsh, bool g_f32,
                                   void* dq, int64_t qgst, int64_t qgsh, void* dk, void* dv,
                                   int64_t kgst, int64_t kgsh, void* ws, hipStream_t s,
-                                  const float* lse_in = nullptr);
+                                  const float* lse_in = nullptr, const float* out_in = nullptr,
+                                  int64_t ost_in = 0, int64_t osh_in = 0);
 size_t linear_workspace_bytes(int64_t n_kv, int32_t heads);
 // forward state S, z of every head into the linear workspace ([H][S | z] float32)
 hipError_t launch_linear_state(const uint16_t* k, const uint16_t* v, int64_t nk, int64_t kst,

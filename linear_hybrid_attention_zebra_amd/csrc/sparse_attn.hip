@@ -1112,11 +1112,24 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         dense ? p.tk - 1 : (n_kept > 0 ? min(max(sel_row[n_kept - 1], 0), p.tk - 1) : -1);
     __syncthreads();
     if constexpr (kLmOnly) {
-      for (int e = tid; e < 2 * p.top_k; e += NT) {
-        const int g = e >= p.top_k;
-        const int j = min(max(sel[(g ? lm_row1 : lm_row0) * p.top_k + e - g * p.top_k], 0),
-                          p.tk - 1);
-        atomicOr(&(g ? lm_bits_second() : kept_bits)[j >> 5], 1u << (j & 31));
+      // eight loads in flight per lane before the first bit is set
+      const int n2 = 2 * p.top_k;
+      for (int e0 = tid; e0 < n2; e0 += 8 * NT) {
+        int jv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = min(e0 + u * NT, n2 - 1);
+          const int g = e >= p.top_k;
+          jv[u] = sel[(g ? lm_row1 : lm_row0) * p.top_k + e - g * p.top_k];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = e0 + u * NT;
+          if (e < n2) {
+            const int j = min(max(jv[u], 0), p.tk - 1);
+            atomicOr(&(e >= p.top_k ? lm_bits_second() : kept_bits)[j >> 5], 1u << (j & 31));
+          }
+        }
       }
     } else if (n_lb > 0) {
       for (int e = tid; e < n_kept; e += NT) {

@@ -14,9 +14,13 @@
 // in bf16):
 //  1. the kept-tile bit matrix [H][Tq][Tk/32] and, by a stable counting sort
 //     over it, for every key tile the ascending list of query tiles keeping it;
-//  2. dq: one workgroup per (head, query tile), two sweeps over its kept
-//     tiles and landmark blocks: D = sum_c P_c dP_c (equal to dout . out, but
-//     from the same float32 P and dP as the gradient), then dS and dq;
+//  2. dq: one workgroup per (head, query tile), over its kept tiles and
+//     landmark blocks: dS and dq, with D = dout . out from the forward's
+//     float32 output (formed while dout is packed). With only the normaliser
+//     of an earlier forward at hand, a first sweep forms D = sum_c P_c dP_c
+//     from the same float32 P and dP and renormalises lse by sum_c P_c. D
+//     from a bf16-rounded output would be off by about 2^-9 |dout| |out|,
+//     which dP - D amplifies where the attention is concentrated;
 //  3. dk, dv of the landmark rows: one workgroup per (head, block of KT
 //     landmark rows), over every query tile, the kept tiles masked;
 //  4. dk, dv of the key tiles: one workgroup per (head, key tile), over the
@@ -133,8 +137,8 @@ struct BwdParams {
   float scale;
   int32_t g_f32, landmarks, log_count;
   float lm_log2_kt, lm_tail_corr;  // log-count biases (log2 units; tail in score units)
-  float* lse;              // [H][nq]; the dq kernel renormalises it in place
-  float* dsum;             // D [H][nq], written by the dq kernel
+  float* lse;              // [H][nq]; dq sweep 0 (when run) renormalises it in place
+  float* dsum;             // D [H][nq]: from the float32 output, or by dq sweep 0
   const uint32_t* bits;    // [H][tq][bit_words] kept tiles
   const int32_t* list_off; // [H][tk + 1]
   const int32_t* list;     // [H][tq * top_k] query tiles keeping each key tile
@@ -196,15 +200,40 @@ __global__ __launch_bounds__(256) void bwd_fill_u32_kernel(uint32_t* __restrict_
 
 // dout (bf16 or float32, any token/head strides) -> packed bf16 [H][nq][64],
 // 8 channels per thread; the dk, dv kernels stage it global -> LDS directly
+// With the forward's float32 output o given, the same pass also forms
+// D = dout . o per query (dout rounded to bf16, as the dP products see it):
+// the eight lanes of a row each take 8 channels, then add in a fixed tree.
 __global__ __launch_bounds__(256) void bwd_pack_dout_kernel(const void* __restrict__ dout,
                                                             int64_t dst, int64_t dsh, int32_t f32,
                                                             int64_t nq, int64_t n_pieces,
-                                                            uint16_t* __restrict__ out) {
+                                                            uint16_t* __restrict__ out,
+                                                            const float* __restrict__ o,
+                                                            int64_t ost, int64_t osh,
+                                                            float* __restrict__ dsum) {
+  // n_pieces is 8 per row and the stride a multiple of 256, so the eight
+  // lanes of a row are in one wave and take the loop together
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n_pieces;
        e += (int64_t)gridDim.x * 256) {
     const int64_t rowi = e >> 3, c8 = e & 7;
     const int64_t h = rowi / nq, q = rowi - h * nq;
-    *(u32x4*)(out + rowi * kHeadDim + 8 * c8) = load8_bf16(dout, h * dsh + q * dst + 8 * c8, f32 != 0);
+    const u32x4 w = load8_bf16(dout, h * dsh + q * dst + 8 * c8, f32 != 0);
+    *(u32x4*)(out + rowi * kHeadDim + 8 * c8) = w;
+    if (o != nullptr) {
+      const float* orow = o + h * osh + q * ost + 8 * c8;
+      const f32x4 a = *(const f32x4*)orow, b = *(const f32x4*)(orow + 4);
+      float d = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4& x = i < 2 ? a : b;
+        const int j = 2 * (i & 1);
+        d = __builtin_fmaf(__uint_as_float(w[i] << 16), x[j], d);
+        d = __builtin_fmaf(__uint_as_float(w[i] & 0xffff0000u), x[j + 1], d);
+      }
+      d += __shfl_xor(d, 1);
+      d += __shfl_xor(d, 2);
+      d += __shfl_xor(d, 4);
+      if (c8 == 0) dsum[rowi] = d;
+    }
   }
 }
 
@@ -1326,14 +1355,15 @@ inline int64_t phase_for(int64_t items, int64_t at_once) {
 }
 
 template <int QT, int KT>
-hipError_t launch_bwd_kernels(BwdParams p, int32_t heads, hipStream_t s) {
+hipError_t launch_bwd_kernels(BwdParams p, int32_t heads, bool have_d, hipStream_t s) {
   hipError_t err;
-  // dq: sweep 0 over key chunks (sums of P' and P' dP), finalize, sweep 1
+  // dq: sweep 0 over key chunks (sums of P' and P' dP), finalize, sweep 1;
+  // with D formed from the forward's float32 output (have_d), sweep 1 alone
   const int ct = kChunkRows / KT;  // key tiles per chunk, a multiple of KT
   const int nkc = (p.tk + ct - 1) / ct;
   const int64_t items = (int64_t)heads * p.tq;
   const dim3 qgrid((unsigned)std::min<int64_t>(items, 1 << 24));
-  for (int sweep = 0; sweep < 2; ++sweep) {
+  for (int sweep = have_d ? 1 : 0; sweep < 2; ++sweep) {
     for (int c = 0; c < nkc; ++c) {
       p.k_lo = c * ct;
       p.k_hi = std::min(p.tk, (c + 1) * ct);
@@ -1404,7 +1434,8 @@ hipError_t launch_tile_sparse_bwd(const uint16_t* q, int64_t nq, int64_t qst, in
                                   const void* dout, int64_t dst, int64_t dsh, bool g_f32,
                                   void* dq, int64_t qgst, int64_t qgsh, void* dk, void* dv,
                                   int64_t kgst, int64_t kgsh, void* ws, hipStream_t s,
-                                  const float* lse_in) {
+                                  const float* lse_in, const float* out_in, int64_t ost_in,
+                                  int64_t osh_in) {
   if (heads == 0 || (nq == 0 && nk == 0)) return hipSuccess;
   const BwdLayout L = bwd_layout(nq, nk, heads, q_tile, k_tile, top_k);
   uint8_t* w = (uint8_t*)ws;
@@ -1435,7 +1466,13 @@ hipError_t launch_tile_sparse_bwd(const uint16_t* q, int64_t nq, int64_t qst, in
   hipError_t err;
   // forward: float32 output and the log2 normaliser (also packs the bf16 landmarks), or,
   // with the normaliser of an earlier forward call given, the landmarks alone and a copy of
-  // the normaliser (sweep 0 renormalises the copy in place)
+  // the normaliser. D = dout . out then comes from the float32 output (the call's own, or
+  // the earlier call's when given) and dq needs one sweep; with the normaliser alone the
+  // first dq sweep forms D from the probabilities and renormalises the copy in place.
+  const bool have_d = lse_in == nullptr || out_in != nullptr;
+  const float* o_d = lse_in == nullptr ? dq_acc : out_in;
+  const int64_t ost_d = lse_in == nullptr ? kHeadDim : ost_in;
+  const int64_t osh_d = lse_in == nullptr ? nq * kHeadDim : osh_in;
   if (nq > 0 && lse_in == nullptr) {
     err = launch_tile_sparse(q, nq, qst, qsh, k, v, nk, kst, ksh, heads, kbar, vbar, sel, q_tile,
                              k_tile, top_k, scale, dq_acc, kHeadDim, nq * kHeadDim, true, flags, w,
@@ -1451,12 +1488,13 @@ hipError_t launch_tile_sparse_bwd(const uint16_t* q, int64_t nq, int64_t qst, in
                          hipMemcpyDeviceToDevice, s);
     if (err != hipSuccess) return err;
   }
-  // dout packed as bf16 rows for the dk, dv kernels' direct-to-LDS staging
+  // dout packed as bf16 rows for the dk, dv kernels' direct-to-LDS staging (and D)
   if (nq > 0) {
     const int64_t pieces = (int64_t)heads * nq * 8;
     hipLaunchKernelGGL(bwd_pack_dout_kernel,
                        dim3((unsigned)std::min<int64_t>((pieces + 255) / 256, 1 << 20)), dim3(256),
-                       0, s, dout, dst, dsh, g_f32 ? 1 : 0, nq, pieces, dout_b);
+                       0, s, dout, dst, dsh, g_f32 ? 1 : 0, nq, pieces, dout_b,
+                       have_d ? o_d : nullptr, ost_d, osh_d, dsum);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   // kept bits, counts, offsets, lists
@@ -1543,13 +1581,13 @@ hipError_t launch_tile_sparse_bwd(const uint16_t* q, int64_t nq, int64_t qst, in
   p.q_lo = p.q_hi = p.k_lo = p.k_hi = p.first = p.last = 0;
   p.phase_period = 0;
   if (k_tile == 64) {
-    if (q_tile == 32) return launch_bwd_kernels<32, 64>(p, heads, s);
-    if (q_tile == 64) return launch_bwd_kernels<64, 64>(p, heads, s);
-    return launch_bwd_kernels<128, 64>(p, heads, s);
+    if (q_tile == 32) return launch_bwd_kernels<32, 64>(p, heads, have_d, s);
+    if (q_tile == 64) return launch_bwd_kernels<64, 64>(p, heads, have_d, s);
+    return launch_bwd_kernels<128, 64>(p, heads, have_d, s);
   }
-  if (q_tile == 32) return launch_bwd_kernels<32, 32>(p, heads, s);
-  if (q_tile == 64) return launch_bwd_kernels<64, 32>(p, heads, s);
-  return launch_bwd_kernels<128, 32>(p, heads, s);
+  if (q_tile == 32) return launch_bwd_kernels<32, 32>(p, heads, have_d, s);
+  if (q_tile == 64) return launch_bwd_kernels<64, 32>(p, heads, have_d, s);
+  return launch_bwd_kernels<128, 32>(p, heads, have_d, s);
 }
 
 }  // namespace zebra

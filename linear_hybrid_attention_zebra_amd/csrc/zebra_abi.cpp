@@ -430,14 +430,15 @@ size_t zebra_tile_sparse_attn_backward_workspace(int64_t n_q, int64_t n_kv, int3
   return zebra::sparse_bwd_workspace_bytes(n_q, n_kv, n_heads, q_tile, k_tile, top_k);
 }
 
-// zebra_tile_sparse_attn_backward and zebra_tile_sparse_attn_backward_lse: lse_in (float32
-// [H][Nq], from zebra_tile_sparse_attn_lse with the same arguments) or NULL
+// zebra_tile_sparse_attn_backward, _backward_lse and _backward_saved: lse_in (float32
+// [H][Nq], from zebra_tile_sparse_attn_lse with the same arguments) or NULL; out_in (that
+// call's float32 output, layout os) or NULL
 static zebra_status sparse_bwd(
     const void* q, zebra_seq qs, const void* k, const void* v, zebra_seq kvs, const float* kbar,
     const float* vbar, const int32_t* sel, int32_t q_tile, int32_t k_tile, int32_t top_k,
-    float scale, uint32_t flags, const float* lse_in, const void* dout, zebra_seq dos,
-    zebra_dtype g_dtype, void* dq, zebra_seq dqs, void* dk, void* dv, zebra_seq dkvs,
-    void* workspace, size_t workspace_bytes, void* stream) {
+    float scale, uint32_t flags, const float* lse_in, const float* out_in, zebra_seq os,
+    const void* dout, zebra_seq dos, zebra_dtype g_dtype, void* dq, zebra_seq dqs, void* dk,
+    void* dv, zebra_seq dkvs, void* workspace, size_t workspace_bytes, void* stream) {
   zebra_status st;
   const uint32_t known = ZEBRA_SPARSE_NO_LANDMARKS | ZEBRA_SPARSE_LANDMARK_LOG_COUNT;
   if ((flags & ~known) != 0u || flags == known) return ZEBRA_ERR_INVALID_ARG;
@@ -490,6 +491,11 @@ static zebra_status sparse_bwd(
     if (((uintptr_t)lse_in % 4) != 0) return ZEBRA_ERR_INVALID_ARG;
     ins.push_back(flat_range(lse_in, (uint64_t)h * qs.n_tokens, 4));
   }
+  if (out_in != nullptr) {  // float32, read as 16-byte vectors
+    if ((st = check_seq(out_in, os, false)) != ZEBRA_OK) return st;
+    if (os.n_heads != h || os.n_tokens != qs.n_tokens) return ZEBRA_ERR_INVALID_ARG;
+    ins.push_back(seq_range(out_in, os, 4));
+  }
   const Range outs[] = {seq_range(dq, dqs, gel), seq_range(dk, dkvs, gel),
                         seq_range(dv, dkvs, gel), flat_range(workspace, need, 1)};
   for (size_t i = 0; i < 4; ++i) {
@@ -504,7 +510,7 @@ static zebra_status sparse_bwd(
       use_lm ? kbar : nullptr, use_lm ? vbar : nullptr, sel, q_tile, k_tile, top_k, scale,
       top_k < tk ? flags : 0u, dout, dos.stride_token, dos.stride_head, g_dtype == ZEBRA_F32, dq,
       dqs.stride_token, dqs.stride_head, dk, dv, dkvs.stride_token, dkvs.stride_head, workspace,
-      (hipStream_t)stream, lse_in));
+      (hipStream_t)stream, lse_in, out_in, os.stride_token, os.stride_head));
 }
 
 zebra_status zebra_tile_sparse_attn_backward(
@@ -514,8 +520,8 @@ zebra_status zebra_tile_sparse_attn_backward(
     zebra_seq dqs, void* dk, void* dv, zebra_seq dkvs, void* workspace, size_t workspace_bytes,
     void* stream) {
   return sparse_bwd(q, qs, k, v, kvs, kbar, vbar, sel, q_tile, k_tile, top_k, scale, flags,
-                    nullptr, dout, dos, g_dtype, dq, dqs, dk, dv, dkvs, workspace,
-                    workspace_bytes, stream);
+                    nullptr, nullptr, zebra_seq{}, dout, dos, g_dtype, dq, dqs, dk, dv, dkvs,
+                    workspace, workspace_bytes, stream);
 }
 
 zebra_status zebra_tile_sparse_attn_backward_lse(
@@ -526,8 +532,21 @@ zebra_status zebra_tile_sparse_attn_backward_lse(
     void* workspace, size_t workspace_bytes, void* stream) {
   if (lse == nullptr && !seq_empty(qs)) return ZEBRA_ERR_INVALID_ARG;
   return sparse_bwd(q, qs, k, v, kvs, kbar, vbar, sel, q_tile, k_tile, top_k, scale, flags, lse,
-                    dout, dos, g_dtype, dq, dqs, dk, dv, dkvs, workspace, workspace_bytes,
-                    stream);
+                    nullptr, zebra_seq{}, dout, dos, g_dtype, dq, dqs, dk, dv, dkvs, workspace,
+                    workspace_bytes, stream);
+}
+
+zebra_status zebra_tile_sparse_attn_backward_saved(
+    const void* q, zebra_seq qs, const void* k, const void* v, zebra_seq kvs, const float* kbar,
+    const float* vbar, const int32_t* sel, int32_t q_tile, int32_t k_tile, int32_t top_k,
+    float scale, uint32_t flags, const float* lse, const float* out, zebra_seq os,
+    const void* dout, zebra_seq dos, zebra_dtype g_dtype, void* dq, zebra_seq dqs, void* dk,
+    void* dv, zebra_seq dkvs, void* workspace, size_t workspace_bytes, void* stream) {
+  if ((lse == nullptr || out == nullptr) && !seq_empty(qs)) return ZEBRA_ERR_INVALID_ARG;
+  if (seq_empty(qs)) out = nullptr;
+  return sparse_bwd(q, qs, k, v, kvs, kbar, vbar, sel, q_tile, k_tile, top_k, scale, flags, lse,
+                    out, os, dout, dos, g_dtype, dq, dqs, dk, dv, dkvs, workspace,
+                    workspace_bytes, stream);
 }
 
 size_t zebra_linear_attn_backward_workspace(int64_t n_q, int64_t n_kv, int32_t n_heads,

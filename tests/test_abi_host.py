@@ -32,7 +32,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 24, names
+    assert len(names) == 25, names
     for name in names:
         assert hasattr(lib, name), f"{name} declared in zebra.h but not exported"
     assert set(names) == set(zb.ENTRY_POINTS)
@@ -162,6 +162,20 @@ def test_lse_entry_points_validation(lib):
     assert bwd(None) == zb.ZEBRA_ERR_INVALID_ARG
     assert bwd(P((1 << 26) + 64)) == zb.ZEBRA_ERR_INVALID_ARG  # read from inside dq
     assert bwd(P(1 << 30), ws_b=bws - 1) == zb.ZEBRA_ERR_WORKSPACE
+    # ... and from the saved float32 output too
+    sv = lib.zebra_tile_sparse_attn_backward_saved
+
+    def saved(lse, out, os=s, ws_b=bws):
+        return sv(P(1 << 16), s, P(1 << 18), P(1 << 20), s, P(1 << 22), P(1 << 23), P(1 << 24),
+                  64, 64, 2, 0.125, 0, lse, out, os, P(1 << 25), s, 0, P(1 << 26), s, P(1 << 27),
+                  P(1 << 28), s, P(1 << 31), ws_b, None)
+
+    assert saved(P(1 << 30), None) == zb.ZEBRA_ERR_INVALID_ARG
+    assert saved(None, P(1 << 29)) == zb.ZEBRA_ERR_INVALID_ARG
+    assert saved(P(1 << 30), P((1 << 27) + 256)) == zb.ZEBRA_ERR_INVALID_ARG  # inside dk
+    assert saved(P(1 << 30), P((1 << 29) + 4)) == zb.ZEBRA_ERR_UNSUPPORTED    # misaligned rows
+    assert saved(P(1 << 30), P(1 << 29), os=seq(255)) == zb.ZEBRA_ERR_INVALID_ARG  # wrong Nq
+    assert saved(P(1 << 30), P(1 << 29), ws_b=bws - 1) == zb.ZEBRA_ERR_WORKSPACE
 
 
 def test_sparse_variant_flags_validation(lib):

@@ -699,9 +699,10 @@ LSE_CASES = [
 @pytest.mark.parametrize("case", LSE_CASES, ids=[str(c) for c in LSE_CASES])
 def test_forward_lse_and_backward_from_it(case):
     """The forward's normaliser equals the oracle's log2-sum-exp of the column weights
-    (bf16-rounded probabilities are summed: 1e-2 in log2 units), the output is bitwise
-    the plain forward's, and the backward from the saved normaliser is bitwise the
-    backward that runs its own forward."""
+    (bf16-rounded probabilities are summed: 1e-2 in log2 units) and the output is bitwise
+    the plain forward's. The backward from the saved normaliser and float32 output is
+    bitwise the backward that runs its own forward; the backward from the normaliser
+    alone (its first sweep forms D and renormalises) matches the oracle."""
     q_tile, k_tile, n_q, n_kv, top_k, n_hot, heads, variant = case
     flags, kw = BWD_FLAGS[variant]
     print(f"[case] forward lse + backward from it {case}", flush=True)
@@ -714,18 +715,31 @@ def test_forward_lse_and_backward_from_it(case):
                                          k_tile, top_k, 0.125, flags, lse_out=lse)
     out_p = zb.zebra_tile_sparse_attn_ex(qg, kg, vg, bufs.kbar, bufs.vbar, bufs.sel, q_tile,
                                          k_tile, top_k, 0.125, flags)
+    lse32 = torch.empty((heads, n_q), dtype=torch.float32, device=DEV)
+    out32 = zb.zebra_tile_sparse_attn_ex(qg, kg, vg, bufs.kbar, bufs.vbar, bufs.sel, q_tile,
+                                         k_tile, top_k, 0.125, flags, out_dtype=torch.float32,
+                                         lse_out=lse32)
     rng = np.random.default_rng(n_q + top_k)
-    dout = torch.from_numpy(synth.bf16_round(
-        rng.standard_normal((heads, n_q, 64)).astype(np.float32))).to(DEV)
+    dout_np = synth.bf16_round(rng.standard_normal((heads, n_q, 64)).astype(np.float32))
+    dout = torch.from_numpy(dout_np).to(DEV)
     g_self = zb.zebra_tile_sparse_attn_backward(qg, kg, vg, bufs.kbar, bufs.vbar, bufs.sel,
                                                 q_tile, k_tile, top_k, 0.125, dout, flags)
+    g_saved = zb.zebra_tile_sparse_attn_backward(qg, kg, vg, bufs.kbar, bufs.vbar, bufs.sel,
+                                                 q_tile, k_tile, top_k, 0.125, dout, flags,
+                                                 lse=lse32, out=out32)
     g_lse = zb.zebra_tile_sparse_attn_backward(qg, kg, vg, bufs.kbar, bufs.vbar, bufs.sel,
                                                q_tile, k_tile, top_k, 0.125, dout, flags, lse=lse)
     torch.cuda.synchronize()
     assert torch.equal(out_l, out_p)
-    for a, b, name in zip(g_self, g_lse, ("dq", "dk", "dv")):
-        assert torch.equal(a, b), f"{name} from the saved normaliser differs"
+    assert torch.equal(lse, lse32)
+    for a, b, name in zip(g_self, g_saved, ("dq", "dk", "dv")):
+        assert torch.equal(a, b), f"{name} from the saved normaliser and output differs"
     sel = bufs.sel.cpu().numpy()
+    rq, rk, rv = zo.tile_sparse_attention_backward(q, k, v, q_tile, k_tile, sel, 0.125, dout_np,
+                                                    **kw)
+    assert_grad_close(g_lse[0], rq, f"dq from the normaliser alone {case}")
+    assert_grad_close(g_lse[1], rk, f"dk from the normaliser alone {case}")
+    assert_grad_close(g_lse[2], rv, f"dv from the normaliser alone {case}")
     got = lse.cpu().numpy()
     worst = 0.0
     for h in range(heads):
