@@ -753,6 +753,38 @@ def test_forward_lse_and_backward_from_it(case):
     assert worst <= 1e-2
 
 
+def test_backward_from_saved_output_strided():
+    """The saved float32 output may be token-major (head stride 64, token stride H x 64)
+    and the gradients float32: the saved-output backward is still bitwise the backward
+    that runs its own forward. Split keys (three chunks and the landmark pass) write the
+    normaliser and the output through the combine."""
+    heads, n, top_k = 2, 65536 + 333, 206
+    print(f"[case] saved-output backward, token-major output: H={heads} N={n}", flush=True)
+    q, k, v = _clustered(77, heads, 300, n, 64, 64, 3)
+    qg, kg, vg = bf16_gpu(q), bf16_gpu(k), bf16_gpu(v)
+    bufs = stage.SparseBuffers.allocate(heads, 300, n, 64, 64, top_k, DEV)
+    stage.sparse_select(qg, kg, vg, 64, 64, top_k, bufs)
+    out = torch.empty((300, heads, 64), dtype=torch.float32, device=DEV).permute(1, 0, 2)
+    lse = torch.empty((heads, 300), dtype=torch.float32, device=DEV)
+    zb.zebra_tile_sparse_attn_ex(qg, kg, vg, bufs.kbar, bufs.vbar, bufs.sel, 64, 64, top_k,
+                                 0.125, 0, out=out, lse_out=lse)
+    rng = np.random.default_rng(78)
+    dout = torch.from_numpy(rng.standard_normal((heads, 300, 64)).astype(np.float32)).to(DEV)
+    g_self = zb.zebra_tile_sparse_attn_backward(qg, kg, vg, bufs.kbar, bufs.vbar, bufs.sel, 64,
+                                                64, top_k, 0.125, dout)
+    g_saved = zb.zebra_tile_sparse_attn_backward(qg, kg, vg, bufs.kbar, bufs.vbar, bufs.sel, 64,
+                                                 64, top_k, 0.125, dout, lse=lse, out=out)
+    torch.cuda.synchronize()
+    for a, b, name in zip(g_self, g_saved, ("dq", "dk", "dv")):
+        assert a.dtype == torch.float32
+        assert torch.equal(a, b), f"{name} from the token-major saved output differs"
+    rq, rk, rv = zo.tile_sparse_attention_backward(q, k, v, 64, 64, bufs.sel.cpu().numpy(), 0.125,
+                                                    dout.cpu().numpy())
+    assert_grad_close(g_saved[0], rq, "saved-output dq")
+    assert_grad_close(g_saved[1], rk, "saved-output dk")
+    assert_grad_close(g_saved[2], rv, "saved-output dv")
+
+
 def test_sparse_backward_multirow_bits_partial_group():
     """dk and dv through the kept-tile bit matrix built several query tiles per
     workgroup: 16 heads x 283 query tiles of 32 (4,528 rows) give 2 rows per
