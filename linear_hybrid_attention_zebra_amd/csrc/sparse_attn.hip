@@ -1251,6 +1251,20 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
       }
     };
+    // Fixed-reference path: the excluded columns of S(t) take one more MFMA step
+    // per query half, the rank-one product of a key-side operand holding -2^100
+    // (exact in bf16) in the excluded key rows and 0 elsewhere with a query-side
+    // operand of ones. Kept scores gain exactly 0; excluded ones fall to about
+    // -2^100, whose probability 2^(c s - m_q + 60) is 0, as -inf gives. Four VALU
+    // instructions per block instead of a select per score register.
+    const bf16x8 ones_k0 = as_bf16x8(u32x4{lane < 32 ? 0x3f80u : 0u, 0u, 0u, 0u});
+    auto mask_by_mfma = [&](f32x16 (&sacc)[2], uint64_t colmask) {
+      const uint32_t w = (uint32_t)(colmask >> (32 * kh));
+      const uint32_t ex = lane < 32 ? (w >> qi) & 1u : 0u;
+      const bf16x8 big = as_bf16x8(u32x4{ex != 0u ? 0xf180u : 0u, 0u, 0u, 0u});
+      sacc[0] = mfma32(big, ones_k0, sacc[0]);
+      sacc[1] = mfma32(big, ones_k0, sacc[1]);
+    };
     auto add_col = [&](f32x16 (&sacc)[2], int col, float corr) {
       const int lc = col - 32 * kh;
       if (lc < 0 || lc >= 32) return;  // uniform
@@ -1344,7 +1358,10 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
         if constexpr (kMasked) {
           if (tail_col >= 0) add_col(sacc, tail_col, p.lm_tail_corr);
-          apply_mask(sacc, cmask);
+          if constexpr (kFast && !kOwnHalf)
+            mask_by_mfma(sacc, cmask);
+          else
+            apply_mask(sacc, cmask);
         }
         float nm[2] = {nm_fast[0], nm_fast[1]}, alpha[2] = {1.f, 1.f};
         bool moved = false;
