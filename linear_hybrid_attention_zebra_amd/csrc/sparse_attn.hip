@@ -1509,10 +1509,7 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
       using Stream = std::integral_constant<int, 2>;
       // streaming steps need the whole kept list in the window (then it
       // starts at entry 0 and never moves)
-      // (own-half staging only: with four waves the shared stages and their
-      // barriers set the pace, and the straight-line step measured slower)
-      const int n_stream =
-          kOwnHalf && (dense || n_kept <= kWin) ? max(n_kept - 2 - kAhead, 0) : 0;
+      const int n_stream = (dense || n_kept <= kWin) ? max(n_kept - 2 - kAhead, 0) : 0;
       if constexpr (kAhead == 2) {
         // K(0) -> stage 0, K(1) -> stage 1, and V(0) -> V stage 1 as a finite
         // stand-in for the absent V(-1) (its probabilities P(-1) are zero);
