@@ -171,6 +171,16 @@ __device__ __forceinline__ uint64_t half_lanes(uint32_t w, int off) {
 
 // 16 bytes per lane global -> LDS directly (the lane's bytes land at
 // dst + 16 lane)
+// 16 bytes per lane from a buffer resource straight into LDS (the lane's
+// bytes land at dst + 16 lane); reads past the resource's records return zeros
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ void b2l16(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                           voff, 0, 0, 0);
+}
 __device__ __forceinline__ void g2l16(const void* src, void* dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 }
@@ -372,6 +382,16 @@ __global__ __launch_bounds__(KT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
   const int h = blockIdx.y;
   const int lrow = lane >> 3;
   const bool gf = p.g_f32 != 0;
+  // byte offsets of the lane's 16 bytes of piece v within a staged query tile:
+  // Q rows p.qst elements apart, packed dout rows 64
+  uint32_t off_q[NU], off_d[NU];
+#pragma unroll
+  for (int v = 0; v < NU; ++v) {
+    const int r = 8 * (wave + W * v) + lrow;
+    const uint32_t c16 = 16u * (uint32_t)((lane & 7) ^ swz_f(r));
+    off_q[v] = (uint32_t)r * (uint32_t)p.qst * 2u + c16;
+    off_d[v] = (uint32_t)r * (uint32_t)kHeadDim * 2u + c16;
+  }
   // per-lane operand read offsets within a staged tile (see the dq kernel):
   // row operands of row kl (+ 32 per query chunk), transposed operands at
   // rows r0 and r0 + 8 (+ 16 per 16-query step) of channel block db
@@ -480,20 +500,25 @@ __global__ __launch_bounds__(KT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
       const int jj = ii + rot < n_i ? ii + rot : ii + rot - n_i;
       return min(max(p.list[i_base + jj], 0), p.tq - 1);
     };
-    // stage query tile qt: rows past nq repeat the last row (masked below)
+    // stage query tile qt through buffer resources whose records end at the
+    // tile's last valid row (rows past nq read as zeros; they are masked below)
     auto issue = [&](int qt, auto stc) {
       constexpr bool kS1 = decltype(stc)::value == 1;
       u32x4* qd = kS1 ? qs1 : qs0;
       u32x4* dd = kS1 ? ds1 : ds0;
       const int64_t last = p.nq - 1;
+      const int64_t q0 = (int64_t)qt * QT;
+      const int rows = (int)min<int64_t>(QT, p.nq - q0);
+      const __amdgpu_buffer_rsrc_t rq = rows_rsrc(
+          p.q + (int64_t)h * p.qsh + q0 * p.qst,
+          (uint32_t)(((int64_t)(rows - 1) * p.qst + kHeadDim) * 2));
+      const __amdgpu_buffer_rsrc_t rd = rows_rsrc(
+          p.dout_b + ((int64_t)h * p.nq + q0) * kHeadDim, (uint32_t)rows * kHeadDim * 2u);
 #pragma unroll
       for (int v = 0; v < NU; ++v) {
         const int u = wave + W * v;
-        const int r = 8 * u + lrow;
-        const int64_t qr = min((int64_t)qt * QT + r, last);
-        const int c = (lane & 7) ^ swz_f(r);
-        g2l16(p.q + (int64_t)h * p.qsh + qr * p.qst + 8 * c, &qd[64 * u]);
-        g2l16(p.dout_b + ((int64_t)h * p.nq + qr) * kHeadDim + 8 * c, &dd[64 * u]);
+        b2l16(rq, &qd[64 * u], off_q[v]);
+        b2l16(rd, &dd[64 * u], off_d[v]);
       }
       // lse and D of the tile's rows, 4 bytes per lane in pieces of 64 rows:
       // piece j holds rows 64 (j / 2).. of lse (j even) or D (j odd)
@@ -879,6 +904,16 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
   // physical chunk lane % 8, i.e. logical chunk (lane % 8) ^ swz_f(row) of
   // the row (the swizzled layout the operand reads expect)
   const int lrow = lane >> 3;
+  // byte offsets of the lane's 16 bytes of piece v within a staged block: key
+  // rows p.kst elements apart, landmark rows 64
+  uint32_t off_kv[NU], off_lm[NU];
+#pragma unroll
+  for (int v = 0; v < NU; ++v) {
+    const int r = 8 * (wave + W * v) + lrow;
+    const uint32_t c16 = 16u * (uint32_t)((lane & 7) ^ swz_f(r));
+    off_kv[v] = (uint32_t)r * (uint32_t)p.kst * 2u + c16;
+    off_lm[v] = (uint32_t)r * (uint32_t)kHeadDim * 2u + c16;
+  }
   // per-lane byte offsets of the operand reads within a staged block (the
   // swizzle depends on row bits 1-3 only, so 16- and 32-row steps are plain
   // offsets): row operands of key row qi, chunk 2 s + hh; transposed
@@ -981,19 +1016,21 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
       }
       return r;
     };
-    // stage block t (rows past the end repeat the last one; they are masked)
+    // stage block t through buffer resources whose records end at the block's
+    // last valid row (rows past a short tile read as zeros; they are masked)
     auto issue = [&](int t, auto stc) {
       const Blk bk = blk(t);
       u32x4* kd = decltype(stc)::value == 0 ? ks0 : ks1;
       u32x4* vd = decltype(stc)::value == 0 ? vs0 : vs1;
+      const uint32_t bytes = (uint32_t)(((int64_t)(bk.rows - 1) * bk.stride + kHeadDim) * 2);
+      const __amdgpu_buffer_rsrc_t rk = rows_rsrc(bk.kbase, bytes);
+      const __amdgpu_buffer_rsrc_t rv = rows_rsrc(bk.vbase, bytes);
 #pragma unroll
       for (int v = 0; v < NU; ++v) {
         const int u = wave + W * v;
-        const int r = 8 * u + lrow;
-        const int rr = min(r, bk.rows - 1);
-        const int64_t e = (int64_t)rr * bk.stride + 8 * ((lane & 7) ^ swz_f(r));
-        g2l16(bk.kbase + e, &kd[64 * u]);
-        g2l16(bk.vbase + e, &vd[64 * u]);
+        const uint32_t off = bk.lm ? off_lm[v] : off_kv[v];
+        b2l16(rk, &kd[64 * u], off);
+        b2l16(rv, &vd[64 * u], off);
       }
     };
     // sweep 0: sum_c P'_c and sum_c P'_c dP_c with P' = 2^(x - lse) in
