@@ -1461,6 +1461,17 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
           const Src sk = block_rsrc(khp + (int64_t)jk * (KT * 128), KT * 128);
           const Src sv = block_rsrc(vhp + (int64_t)jv * (KT * 128), KT * 128);
           body(par, std::false_type{}, 0ull, 0.f, -1, sk, sv);
+        } else if constexpr (decltype(masked_c)::value == 3) {
+          // landmark streaming step: n_kept <= t < n_total - 2 - kAhead, so
+          // block t and the loaded blocks K(t + 1 + kAhead), V(t + kAhead - 1)
+          // are whole landmark blocks (the head's last one, which may be short
+          // or carry the log-count correction, is the item's last block)
+          const int b = lb0 + t - n_kept;
+          const Src sk = block_rsrc(klm + (int64_t)(b + 1 + kAhead) * (KT * 128), KT * 128);
+          const Src sv = block_rsrc(vlm + (int64_t)(b + kAhead - 1) * (KT * 128), KT * 128);
+          const uint32_t lo = __builtin_amdgcn_readfirstlane(my_bits[2 * b]);
+          const uint32_t hi = __builtin_amdgcn_readfirstlane(my_bits[2 * b + 1]);
+          body(par, std::true_type{}, ((uint64_t)hi << 32) | lo, lm_shift, -1, sk, sv);
         } else {
         const int tkn = min(t + 1 + kAhead, n_total - 1);
         const int tvn = max(min(t + kAhead - 1, n_total - 1), 0);
@@ -1545,6 +1556,16 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
       }
       if (t < n_plain) step(t++, P0{}, Plain{});
       if ((t & 1) && t < n_total) step(t++, P1{}, Masked{});
+      // (the landmark-only pass: in the other items the extra step form costs
+      // the register allocation more than it saves)
+      if constexpr (kLmOnly) {
+        using LmStream = std::integral_constant<int, 3>;
+        const int n_lms = n_lb > 0 ? n_total - 2 - kAhead : 0;
+        for (; t + 2 <= n_lms; t += 2) {  // (no kept tiles: t >= n_kept = 0)
+          step(t, P0{}, LmStream{});
+          step(t + 1, P1{}, LmStream{});
+        }
+      }
       for (; t + 2 <= n_total; t += 2) {
         step(t, P0{}, Masked{});
         step(t + 1, P1{}, Masked{});
