@@ -896,8 +896,10 @@ __device__ __forceinline__ uint32_t* lm_bits_second() {
 
 // kLmOnly (128-query tiles, split keys): an item is one (head, pair of 64-query
 // tiles) over every landmark block of the head, query group qg masked by the
-// kept tiles of 64-query tile 2 g + qg; it writes the landmark columns'
-// unnormalised output and (reference, row sum) into the last partial slot.
+// kept tiles of 64-query tile 2 g + qg. It runs after the key-chunk launch and
+// merges its landmark columns' unnormalised output and (reference, row sum)
+// with the chunks' partials of its queries, in slot order with its own last,
+// into the normalised output (and the normaliser when asked for).
 template <int QT, bool kLmOnly>
 __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) void tile_sparse_kh_kernel(
     SparseParams p, const int32_t* __restrict__ sel) {
@@ -1634,9 +1636,83 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
       if (l_sum == 0.f) ref = r_mine;  // no columns at all (split keys, no landmarks)
       const int64_t qrow = qbase + 32 * kh;
       if (qrow >= p.nq) return;
-      if (kLmOnly || n_ch > 1) {  // split keys: unnormalised partial, (reference, row sum)
+      if constexpr (kLmOnly) {
+        // The key chunks' partials of this query are complete (the pass runs
+        // after the chunk launch, on the same stream): merge them with this
+        // one, which is the last slot, exactly as the combine does: reference
+        // R = the largest over the partials with columns, then in slot order
+        // l = sum l_c 2^(r_c - R) and O = sum O_c 2^(r_c - R), then O / l.
+        const int64_t prow0 = ((int64_t)h * p.nq + qrow) * p.part_slots;
+        const float2* ml = p.part_ml + prow0;
+        const float* po = part_o_arg + prow0 * kHeadDim + 4 * hh;
+        float big = l_sum > 0.f ? ref : -INFINITY;
+        for (int c = 0; c < n_ch; ++c) {
+          const float2 m = ml[c];
+          if (m.y > 0.f) big = __builtin_elementwise_maximum(big, m.x);
+        }
+        float l_tot = 0.f;
+        f32x4 acc[2][4];
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) acc[db][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto add = [&](float2 m, const f32x4 (&x)[2][4]) {
+          const float wgt = m.y > 0.f ? __builtin_amdgcn_exp2f(m.x - big) : 0.f;
+          l_tot = __builtin_fmaf(m.y, wgt, l_tot);
+#pragma unroll
+          for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                acc[db][g][r] = __builtin_fmaf(x[db][g][r], wgt, acc[db][g][r]);
+        };
+        for (int c = 0; c < n_ch; ++c) {
+          f32x4 x[2][4];
+#pragma unroll
+          for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              x[db][g] = *(const f32x4*)(po + (int64_t)c * kHeadDim + 32 * db + 8 * g);
+          add(ml[c], x);
+        }
+        {
+          f32x4 x[2][4];
+#pragma unroll
+          for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              x[db][g] = f32x4{om[db][4 * g], om[db][4 * g + 1], om[db][4 * g + 2],
+                               om[db][4 * g + 3]};
+          add(float2{ref, l_sum}, x);
+        }
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;  // 0 only without any column
+        if (p.lse != nullptr && hh == 0)
+          p.lse[(int64_t)h * p.nq + qrow] = big + __builtin_log2f(l_tot);
+        if (p.o_f32) {
+          float* op = (float*)o_arg + (int64_t)h * p.osh + qrow * p.ost + 4 * hh;
+#pragma unroll
+          for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              *(f32x4*)(op + 32 * db + 8 * g) =
+                  f32x4{acc[db][g][0] * inv, acc[db][g][1] * inv, acc[db][g][2] * inv,
+                        acc[db][g][3] * inv};
+        } else {
+          uint16_t* op = (uint16_t*)o_arg + (int64_t)h * p.osh + qrow * p.ost + 4 * hh;
+#pragma unroll
+          for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              *(u32x2*)(op + 32 * db + 8 * g) =
+                  u32x2{pack_bf16x2(acc[db][g][0] * inv, acc[db][g][1] * inv),
+                        pack_bf16x2(acc[db][g][2] * inv, acc[db][g][3] * inv)};
+        }
+        return;
+      }
+      if (n_ch > 1) {  // split keys: unnormalised partial, (reference, row sum)
         // (four-wave key-chunk items are never split: their stride stays n_ch)
-        const int slots = kOwnHalf || kLmOnly ? p.part_slots : n_ch;
+        const int slots = kOwnHalf ? p.part_slots : n_ch;
         const int64_t prow = ((int64_t)h * p.nq + qrow) * slots + ch;
         float* op = part_o_arg + prow * kHeadDim + 4 * hh;
 #pragma unroll
@@ -1977,7 +2053,8 @@ hipError_t launch_tile_sparse(const uint16_t* q, int64_t nq, int64_t qst, int64_
   p.n_items = (int64_t)heads * sp.n_chunks * p.tq;
   // the key-half kernel's 64-query items leave their landmark blocks to one
   // pass of 128-query items (pairs of query tiles) over all landmark rows, which
-  // halves the landmark blocks' gathers; its partial takes the last slot
+  // halves the landmark blocks' gathers; that pass, run last, also merges the
+  // chunks' partials (its own partial is the last slot, kept in registers)
   const bool lm_pass = p.landmarks && q_tile == 64 && k_tile == 64 && kst == kHeadDim;
   p.lm_separate = lm_pass ? 1 : 0;
   p.part_slots = sp.n_chunks + (lm_pass ? 1 : 0);
@@ -1998,6 +2075,7 @@ hipError_t launch_tile_sparse(const uint16_t* q, int64_t nq, int64_t qst, int64_
                        0, s, pl, sel);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
+  if (lm_pass) return hipSuccess;  // the landmark pass merged the partials
   const int64_t qrows = (int64_t)heads * nq;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((qrows + 15) / 16)), dim3(256), 0, s,
                      (const float*)p.part_o, (const float2*)p.part_ml, p.part_slots, nq, qrows,
