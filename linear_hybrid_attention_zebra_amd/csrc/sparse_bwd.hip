@@ -1315,6 +1315,316 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
   }
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// dq (sweep 1) for 64-query and 64-key tiles in the key-half layout: wave kh
+// takes all 64 queries of the tile over keys 32 kh .. 32 kh + 31 of every
+// block (S^T = K Q^T, dP^T = V dout^T, dq^T += K^T dS^T), so each K or V
+// operand read from LDS feeds both query halves. A wave stages only its own
+// rows of a block, global -> LDS directly, into two-stage rings: at the end
+// of step t, once its reads of the stage have completed, it refills that
+// stage with block t + 2, and step t + 1 waits only for the wave's own loads
+// of block t + 1. The steps need no workgroup barrier. The two key halves'
+// dq meet in LDS at the end of the item, where wave kh keeps query half kh.
+// Per block and wave the products and their summation order are those of
+// bwd_dq_kernel's half kh of the block.
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kh_kernel(
+    BwdParams p) {
+  constexpr int KT = 64, QT = 64;
+  __shared__ u32x4 ks0[KT * 8], vs0[KT * 8], ks1[KT * 8], vs1[KT * 8];
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int kh = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int qi = lane & 31, hh = lane >> 5;
+  const bool gf = p.g_f32 != 0;
+  const int n_lb_all = p.landmarks ? (p.tk + KT - 1) / KT : 0;
+  const int tail_rows = (int)(p.nk - (int64_t)(p.tk - 1) * KT);
+  const int last_lrows = p.tk - (n_lb_all - 1) * KT;
+  // this wave's pieces 4 kh + v (v = 0..3) of a block: rows 8 (4 kh + v) +
+  // lane / 8, logical chunk (lane % 8) ^ swz_f(row) landing at physical chunk
+  // lane % 8 (the swizzled layout the operand reads expect)
+  const int lrow = lane >> 3;
+  uint32_t off_kv[4], off_lm[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int r = 8 * (4 * kh + v) + lrow;
+    const uint32_t c16 = 16u * (uint32_t)((lane & 7) ^ swz_f(r));
+    off_kv[v] = (uint32_t)r * (uint32_t)p.kst * 2u + c16;
+    off_lm[v] = (uint32_t)r * (uint32_t)kHeadDim * 2u + c16;
+  }
+  // operand reads: row operands of key row 32 kh + qi, chunk 2 s + hh;
+  // transposed operands at rows r0 and r0 + 8 of 16-key chunk m = 2 kh + mm
+  uint32_t koff[4], toff[2][2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) koff[s] = swz(qi, 2 * s + hh) + 4096u * (uint32_t)kh;
+  {
+    const int G = lane >> 4, S = lane & 15;
+    const int r0 = 4 * (G >> 1) + (S >> 2);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int col = 32 * db + 16 * (G & 1) + 4 * (S & 3);
+      const int chunk = col >> 3, half = (col & 7) ? 8 : 0;
+      toff[db][0] = swz(r0, chunk) + half + 4096u * (uint32_t)kh;
+      toff[db][1] = swz(r0 + 8, chunk) + half + 4096u * (uint32_t)kh;
+    }
+  }
+  auto row_op = [&](const lds_u8* tile, int s) -> bf16x8 {
+    return as_bf16x8(*(const __attribute__((address_space(3))) u32x4*)(tile + koff[s]));
+  };
+  auto tr_op = [&](const lds_u8* tile, int mm, int db) -> bf16x8 {
+    const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(tile + toff[db][0] + 2048 * mm));
+    const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(tile + toff[db][1] + 2048 * mm));
+    const u32x2 w0 = __builtin_bit_cast(u32x2, t0), w1 = __builtin_bit_cast(u32x2, t1);
+    return as_bf16x8(u32x4{w0.x, w0.y, w1.x, w1.y});
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  for (int64_t item = blockIdx.x; item < (int64_t)p.heads * p.tq; item += gridDim.x) {
+    const int h = (int)(item / p.tq);
+    const int qt = (int)(item - (int64_t)h * p.tq);
+    const int64_t row = (int64_t)h * p.tq + qt;
+    const int32_t* sel_row = p.sel + row * p.top_k;
+    bf16x8 qop[2][4], dop[2][4];
+    float lse[2], dsum[2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      const int64_t qrow = (int64_t)qt * QT + 32 * qh + qi;
+      const bool qvalid = qrow < p.nq;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+        if (qvalid) {
+          a = *(const u32x4*)(p.q + (int64_t)h * p.qsh + qrow * p.qst + 16 * s + 8 * hh);
+          b = load8_bf16(p.dout, (int64_t)h * p.dsh + qrow * p.dst + 16 * s + 8 * hh, gf);
+        }
+        qop[qh][s] = as_bf16x8(a);
+        dop[qh][s] = as_bf16x8(b);
+      }
+      lse[qh] = qvalid ? p.lse[(int64_t)h * p.nq + qrow] : INFINITY;
+      dsum[qh] = qvalid ? p.dsum[(int64_t)h * p.nq + qrow] : 0.f;
+    }
+    f32x16 dqacc[2][2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dqacc[0][0][i] = 0.f;
+      dqacc[0][1][i] = 0.f;
+      dqacc[1][0][i] = 0.f;
+      dqacc[1][1][i] = 0.f;
+    }
+    // this launch's key tiles [k_lo, k_hi): kept entries [t0, t1) of the
+    // ascending row, landmark blocks [lb0, lb1)
+    const int t0 = lower_bound_i32(sel_row, 0, p.top_k, p.k_lo);
+    const int t1 = lower_bound_i32(sel_row, t0, p.top_k, p.k_hi);
+    const int lb0 = p.k_lo / KT, lb1 = min(n_lb_all, (p.k_hi + KT - 1) / KT);
+    const int n_kept = t1 - t0;
+    const int n_total = n_kept + max(lb1 - lb0, 0);
+    // the kept list and bits as constant memory (nothing writes them during
+    // the kernel): the per-block reads become scalar loads, counted apart
+    // from the staging loads that the steps wait on
+    typedef const __attribute__((address_space(4))) int32_t* cint_p;
+    typedef const __attribute__((address_space(4))) uint32_t* cuint_p;
+    const cint_p sel_c = (cint_p)sel_row;
+    const cuint_p brow = (cuint_p)(p.bits + row * p.bit_words);
+    int rot = 0;  // phased walk of the kept tiles
+    if (p.phase_period > 0 && n_kept > 1) {
+      const int target =
+          p.k_lo + (int)((item % p.phase_period) * (p.k_hi - p.k_lo) / p.phase_period);
+      const int r = lower_bound_i32(sel_row, t0, t1, target) - t0;
+      rot = r < n_kept ? r : 0;
+    }
+    // block t of the list: kept key tile (walk order) or landmark block
+    struct Blk {
+      const uint16_t* kbase;
+      const uint16_t* vbase;
+      int64_t stride;
+      int rows;
+      bool lm;
+      int b;  // landmark block index
+    };
+    auto blk = [&](int t) -> Blk {
+      Blk r;
+      r.lm = t >= n_kept;
+      if (!r.lm) {
+        const int tt = t + rot < n_kept ? t + rot : t + rot - n_kept;
+        const int j = min(max(sel_c[t0 + tt], 0), p.tk - 1);
+        r.kbase = p.k + (int64_t)h * p.ksh + (int64_t)j * KT * p.kst;
+        r.vbase = p.v + (int64_t)h * p.ksh + (int64_t)j * KT * p.kst;
+        r.stride = p.kst;
+        r.rows = j == p.tk - 1 ? tail_rows : KT;
+        r.b = 0;
+      } else {
+        r.b = lb0 + t - n_kept;
+        r.kbase = p.kbar_b + ((int64_t)h * p.tk + (int64_t)r.b * KT) * kHeadDim;
+        r.vbase = p.vbar_b + ((int64_t)h * p.tk + (int64_t)r.b * KT) * kHeadDim;
+        r.stride = kHeadDim;
+        r.rows = r.b == n_lb_all - 1 ? last_lrows : KT;
+      }
+      return r;
+    };
+    // this wave's rows of block t, through buffer resources whose records end
+    // at the block's last valid row (rows past a short tile read as zeros;
+    // their columns are masked)
+    auto issue = [&](int t, auto stc) {
+      const Blk bk = blk(t);
+      u32x4* kd = decltype(stc)::value == 0 ? ks0 : ks1;
+      u32x4* vd = decltype(stc)::value == 0 ? vs0 : vs1;
+      const uint32_t bytes = (uint32_t)(((int64_t)(bk.rows - 1) * bk.stride + kHeadDim) * 2);
+      const __amdgpu_buffer_rsrc_t rk = rows_rsrc(bk.kbase, bytes);
+      const __amdgpu_buffer_rsrc_t rv = rows_rsrc(bk.vbase, bytes);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int u = 4 * kh + v;
+        const uint32_t off = bk.lm ? off_lm[v] : off_kv[v];
+        b2l16(rk, &kd[64 * u], off);
+        b2l16(rv, &vd[64 * u], off);
+      }
+    };
+    auto step = [&](int t, auto stc) {
+      // this wave's loads of block t have landed; block t + 1's may be in
+      // flight (every step issues one block: past the end, the last again)
+      wait_vm<8>();
+      const lds_u8* ktile = (const lds_u8*)(decltype(stc)::value == 0 ? ks0 : ks1);
+      const lds_u8* vtile = (const lds_u8*)(decltype(stc)::value == 0 ? vs0 : vs1);
+      const Blk bk = blk(t);
+      uint64_t cmask = 0ull;  // excluded columns (bit set)
+      float bias = 0.f;       // log2 units
+      int tail_col = -1;
+      if (bk.lm) {
+        const uint32_t lo = brow[2 * bk.b];
+        const uint32_t hi = 2 * bk.b + 1 < p.bit_words ? brow[2 * bk.b + 1] : 0u;
+        cmask = ((uint64_t)hi << 32) | lo;
+        if (p.log_count) {
+          bias = p.lm_log2_kt;
+          if (bk.b == n_lb_all - 1 && tail_rows < KT) tail_col = last_lrows - 1;
+        }
+      }
+      if (bk.rows < KT) cmask |= ~0ull << bk.rows;
+      const uint32_t wm = (uint32_t)(cmask >> (32 * kh));
+      const uint32_t tw = tail_col >= 32 * kh && tail_col < 32 * kh + 32
+                              ? 1u << (tail_col - 32 * kh) : 0u;
+      bf16x8 kr[4], vr[4], kt[2][2];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        kr[s] = row_op(ktile, s);
+        vr[s] = row_op(vtile, s);
+      }
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) kt[mm][db] = tr_op(ktile, mm, db);
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh) {
+        // S^T = K Q^T, dP^T = V dout^T: lane = query, register v = key
+        // 32 kh + 8 (v / 4) + 4 hh + v % 4
+        f32x16 sacc, pacc;
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[0], qop[qh][0], f32x16{}, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[0], dop[qh][0], f32x16{}, 0, 0, 0);
+#pragma unroll
+        for (int s = 1; s < 4; ++s) {
+          sacc = mfma32(kr[s], qop[qh][s], sacc);
+          pacc = mfma32(vr[s], dop[qh][s], pacc);
+        }
+        if (wm != 0u || tw != 0u) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int off = 8 * (v >> 2) + (v & 3);
+            if (__builtin_amdgcn_inverse_ballot_w64(half_lanes(tw, off)))
+              sacc[v] += p.lm_tail_corr;
+            if (__builtin_amdgcn_inverse_ballot_w64(half_lanes(wm, off))) sacc[v] = -INFINITY;
+          }
+        }
+        const float nb = bias - lse[qh];
+        float dsr[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], p.c, nb));
+          dsr[v] = pv * (pacc[v] - dsum[qh]);
+        }
+        bf16x8 slo, shi, slo2, shi2;
+        pack16_split(dsr, slo, shi, slo2, shi2);
+        // dq^T += K^T dS^T over this wave's 16-key chunks
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          dqacc[qh][db] = mfma32(kt[0][db], slo, dqacc[qh][db]);
+          dqacc[qh][db] = mfma32(kt[1][db], shi, dqacc[qh][db]);
+          dqacc[qh][db] = mfma32(kt[0][db], slo2, dqacc[qh][db]);
+          dqacc[qh][db] = mfma32(kt[1][db], shi2, dqacc[qh][db]);
+        }
+      }
+      // refill this stage with block t + 2 once the reads above have
+      // completed: an LDS write by a global load is not ordered after LDS
+      // reads still in flight
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(min(t + 2, n_total - 1), stc);
+    };
+    __syncthreads();  // both waves are done with the previous item's LDS
+    if (n_total > 0) {
+      issue(0, S0{});
+      issue(min(1, n_total - 1), S1{});
+      int t = 0;
+      for (; t + 2 <= n_total; t += 2) {
+        step(t, S0{});
+        step(t + 1, S1{});
+      }
+      if (t < n_total) step(t, S0{});
+      wait_vm<0>();  // the repeated last blocks have landed
+    }
+    // the key halves meet: wave kh hands query half 1 - kh to its partner
+    // through the idle rings
+    __syncthreads();
+    // (kh is uniform: both branches index the register arrays statically)
+    auto put = [&](const f32x16 (&a)[2], f32x4* xo) {
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          xo[(db * 4 + g) * 64 + lane] =
+              f32x4{a[db][4 * g], a[db][4 * g + 1], a[db][4 * g + 2], a[db][4 * g + 3]};
+    };
+    if (kh == 0)
+      put(dqacc[1], (f32x4*)ks0);
+    else
+      put(dqacc[0], (f32x4*)vs0);
+    __syncthreads();
+    auto finish = [&](const f32x16 (&a)[2], const f32x4* xi) {
+      const int64_t qrow = (int64_t)qt * QT + 32 * kh + qi;
+      if (qrow >= p.nq) return;
+      // lane (qi, hh) holds channels 32 db + 8 g + 4 hh + r
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          // the two key halves' sums (float addition is commutative, so
+          // both waves form the same value)
+          f32x4 x = f32x4{a[db][4 * g], a[db][4 * g + 1], a[db][4 * g + 2], a[db][4 * g + 3]} +
+                    xi[(db * 4 + g) * 64 + lane];
+          const int64_t ai = ((int64_t)h * p.nq + qrow) * kHeadDim + 32 * db + 8 * g + 4 * hh;
+          if (!p.first) x += *(const f32x4*)(p.dq_acc + ai);
+          if (!p.last) {
+            *(f32x4*)(p.dq_acc + ai) = x;
+            continue;
+          }
+          x *= p.scale;
+          const int64_t base = (int64_t)h * p.qgsh + qrow * p.qgst + 32 * db + 8 * g + 4 * hh;
+          if (gf)
+            *(f32x4*)((float*)p.dq + base) = x;
+          else
+            *(u32x2*)((uint16_t*)p.dq + base) = u32x2{pack_bf16x2(x[0], x[1]),
+                                                      pack_bf16x2(x[2], x[3])};
+        }
+    };
+    if (kh == 0)
+      finish(dqacc[0], (const f32x4*)vs0);
+    else
+      finish(dqacc[1], (const f32x4*)ks0);
+  }
+}
+
 // after the sweep-0 launches: renormalise lse by the sum of P' and form D
 __global__ __launch_bounds__(256) void bwd_finalize_kernel(float* __restrict__ lse,
                                                            float* __restrict__ dsum,
@@ -1409,6 +1719,9 @@ hipError_t launch_bwd_kernels(BwdParams p, int32_t heads, bool have_d, hipStream
       if (sweep == 0) {
         p.phase_period = phase_for(items, wgs_at_once<bwd_dq_kernel<QT, KT, false>, QT * 2>());
         hipLaunchKernelGGL((bwd_dq_kernel<QT, KT, false>), qgrid, dim3(QT * 2), 0, s, p);
+      } else if constexpr (QT == 64 && KT == 64) {
+        p.phase_period = phase_for(items, wgs_at_once<bwd_dq_kh_kernel, 128>());
+        hipLaunchKernelGGL(bwd_dq_kh_kernel, qgrid, dim3(128), 0, s, p);
       } else {
         p.phase_period = phase_for(items, wgs_at_once<bwd_dq_kernel<QT, KT, true>, QT * 2>());
         hipLaunchKernelGGL((bwd_dq_kernel<QT, KT, true>), qgrid, dim3(QT * 2), 0, s, p);
