@@ -190,10 +190,11 @@ __device__ __forceinline__ void g2l4(const void* src, void* dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
 }
 
-// Read-only index data (kept lists, bits) read as constant memory: nothing
-// writes it while a gradient kernel runs, so uniform reads become scalar loads,
-// which the vector-memory counter that the staging steps wait on does not
-// count (a vector load there would make the step wait for its own prefetch).
+// Read-only index data (kept lists, bits) read as constant memory by the
+// key-half dq kernel: nothing writes it while the kernel runs, so uniform reads
+// become scalar loads, which the vector-memory counter that its steps wait on
+// does not count (a vector load there would make a step wait for its own
+// prefetch).
 typedef const __attribute__((address_space(4))) int32_t* cint_p;
 typedef const __attribute__((address_space(4))) uint32_t* cuint_p;
 
@@ -505,7 +506,7 @@ __global__ __launch_bounds__(KT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     auto qtile_of = [&](int ii) -> int {
       if constexpr (LM) return i_base + ii;
       const int jj = ii + rot < n_i ? ii + rot : ii + rot - n_i;
-      return min(max(((cint_p)p.list)[i_base + jj], 0), p.tq - 1);
+      return min(max(p.list[i_base + jj], 0), p.tq - 1);
     };
     // stage query tile qt through buffer resources whose records end at the
     // tile's last valid row (rows past nq read as zeros; they are masked below)
@@ -563,8 +564,7 @@ __global__ __launch_bounds__(KT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
       if constexpr (LM) {
         const int wi = (KT * cb + 32 * wave) / 32;  // the word of this wave's 32 columns
         const uint32_t word =
-            wi < p.bit_words ? ((cuint_p)p.bits)[((int64_t)h * p.tq + qt) * p.bit_words + wi]
-                             : 0u;
+            wi < p.bit_words ? p.bits[((int64_t)h * p.tq + qt) * p.bit_words + wi] : 0u;
         masked = masked || ((word >> kl) & 1u);
       }
       // an excluded landmark column enters with logit bias -inf (probability
@@ -766,14 +766,13 @@ __global__ __launch_bounds__(KT * 2) void bwd_dkdv_sync_kernel(BwdParams p) {
     if (n_i == 0 && !p.first && !p.last) continue;  // nothing to add in this launch
     for (int ii = 0; ii < n_i; ++ii) {
       // (a selection with repeated entries would leave list slots unwritten)
-      const int qt = LM ? i_base + ii : min(max(((cint_p)p.list)[i_base + ii], 0), p.tq - 1);
+      const int qt = LM ? i_base + ii : min(max(p.list[i_base + ii], 0), p.tq - 1);
       // kept mask of this lane's landmark column for query tile qt
       bool masked = !cvalid;
       if constexpr (LM) {
         const int wi = (KT * cb + 32 * wave) / 32;  // the word of this wave's 32 columns
         const uint32_t word =
-            wi < p.bit_words ? ((cuint_p)p.bits)[((int64_t)h * p.tq + qt) * p.bit_words + wi]
-                             : 0u;
+            wi < p.bit_words ? p.bits[((int64_t)h * p.tq + qt) * p.bit_words + wi] : 0u;
         masked = masked || ((word >> kl) & 1u);
       }
       __syncthreads();  // previous tiles consumed
@@ -988,7 +987,7 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int lb0 = p.k_lo / KT, lb1 = min(n_lb_all, (p.k_hi + KT - 1) / KT);
     const int n_kept = t1 - t0;
     const int n_total = n_kept + max(lb1 - lb0, 0);
-    const cuint_p brow = (cuint_p)(p.bits + row * p.bit_words);
+    const uint32_t* brow = p.bits + row * p.bit_words;
     int rot = 0;  // phased walk of the kept tiles
     if (p.phase_period > 0 && n_kept > 1) {
       const int target =
@@ -1010,7 +1009,7 @@ __global__ __launch_bounds__(QT * 2) __attribute__((amdgpu_waves_per_eu(2))) voi
       r.lm = t >= n_kept;
       if (!r.lm) {
         const int tt = t + rot < n_kept ? t + rot : t + rot - n_kept;
-        const int j = min(max(((cint_p)sel_row)[t0 + tt], 0), p.tk - 1);
+        const int j = min(max(sel_row[t0 + tt], 0), p.tk - 1);
         r.kbase = p.k + (int64_t)h * p.ksh + (int64_t)j * KT * p.kst;
         r.vbase = p.v + (int64_t)h * p.ksh + (int64_t)j * KT * p.kst;
         r.stride = p.kst;

@@ -659,6 +659,7 @@ SPARSE_BWD_CASES = [
     (32, 32, 2000, 2000, 7, 3, 1, "default"),        # many query tiles per key tile
     (64, 64, 1000, 1000, 16, 3, 1, "default"),       # every tile kept
     (64, 64, 300, 65536 + 333, 206, 3, 1, "default"),  # forward in split keys
+    (64, 64, 333, 700, 3, 2, 2, "log_count"),  # short last landmark block under the log count
 ]
 BWD_FLAGS = {"default": (0, {}), "no_landmarks": (1, dict(landmarks=False)),
              "log_count": (2, dict(landmark_log_count=True))}
@@ -783,6 +784,29 @@ def test_backward_from_saved_output_strided():
     assert_grad_close(g_saved[0], rq, "saved-output dq")
     assert_grad_close(g_saved[1], rk, "saved-output dk")
     assert_grad_close(g_saved[2], rv, "saved-output dv")
+
+
+def test_sparse_backward_token_major_inputs():
+    """Token-major [N][H][64] q, k and v (rows H x 64 elements apart) with 64-query and
+    64-key tiles: the key-half dq kernel and the dK/dV kernels stage strided rows."""
+    heads, nq, n, top_k = 3, 250, 900, 3
+    print(f"[case] sparse backward, token-major inputs: H={heads} Nq={nq} N={n}", flush=True)
+    q, k, v = _clustered(19, heads, nq, n, 64, 64, 2)
+    tm = lambda x: bf16_gpu(x).permute(1, 0, 2).contiguous().permute(1, 0, 2)
+    qg, kg, vg = tm(q), tm(k), tm(v)
+    bufs = stage.SparseBuffers.allocate(heads, nq, n, 64, 64, top_k, DEV)
+    stage.sparse_select(qg, kg, vg, 64, 64, top_k, bufs)
+    rng = np.random.default_rng(20)
+    dout = synth.bf16_round(rng.standard_normal((heads, nq, 64)).astype(np.float32))
+    dq, dk, dv = zb.zebra_tile_sparse_attn_backward(
+        qg, kg, vg, bufs.kbar, bufs.vbar, bufs.sel, 64, 64, top_k, 0.125,
+        torch.from_numpy(dout).to(DEV))
+    torch.cuda.synchronize()
+    rq, rk, rv = zo.tile_sparse_attention_backward(q, k, v, 64, 64, bufs.sel.cpu().numpy(),
+                                                    0.125, dout)
+    assert_grad_close(dq, rq, "token-major dq")
+    assert_grad_close(dk, rk, "token-major dk")
+    assert_grad_close(dv, rv, "token-major dv")
 
 
 def test_sparse_backward_multirow_bits_partial_group():
