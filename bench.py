@@ -658,8 +658,9 @@ def main():
         sec = res["sparse_attn_ms"] * 1e-3
         achieved = res["selected_flops"] / sec / 1e12
         out["roofline"] = {"kernel": "tile_sparse_kh_kernel (timed as its whole zebra_tile_sparse_attn "
-                                     "call: landmark packing, key ranges, chunk offsets, the kernel, "
-                                     "its landmark pass and the split-key combine)", "bound": "mfma",
+                                     "call: landmark packing, key ranges, chunk offsets, the key-chunk "
+                                     "kernel and its landmark pass, which merges the chunks' "
+                                     "partials)", "bound": "mfma",
                            "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": achieved / PEAK_BF16_TFLOPS,
                            "traffic": recorded_traffic(w.name),
