@@ -1329,7 +1329,8 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
 }
 
-// dq (sweep 1) for 64-query and 64-key tiles in the key-half layout: wave kh
+// dq for 64-query and 64-key tiles in the key-half layout (kGrad: sweep 1,
+// dS and dq; otherwise sweep 0, the sums of P' and P' dP): wave kh
 // takes all 64 queries of the tile over keys 32 kh .. 32 kh + 31 of every
 // block (S^T = K Q^T, dP^T = V dout^T, dq^T += K^T dS^T), so each K or V
 // operand read from LDS feeds both query halves. A wave stages only its own
@@ -1337,9 +1338,10 @@ __device__ __forceinline__ void wait_vm() {
 // of step t, once its reads of the stage have completed, it refills that
 // stage with block t + 2, and step t + 1 waits only for the wave's own loads
 // of block t + 1. The steps need no workgroup barrier. The two key halves'
-// dq meet in LDS at the end of the item, where wave kh keeps query half kh.
-// Per block and wave the products and their summation order are those of
-// bwd_dq_kernel's half kh of the block.
+// dq (or sums) meet in LDS at the end of the item, where wave kh keeps query
+// half kh. Per block and wave the products and their summation order are
+// those of bwd_dq_kernel's half kh of the block.
+template <bool kGrad>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kh_kernel(
     BwdParams p) {
   constexpr int KT = 64, QT = 64;
@@ -1414,8 +1416,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
         dop[qh][s] = as_bf16x8(b);
       }
       lse[qh] = qvalid ? p.lse[(int64_t)h * p.nq + qrow] : INFINITY;
-      dsum[qh] = qvalid ? p.dsum[(int64_t)h * p.nq + qrow] : 0.f;
+      dsum[qh] = kGrad && qvalid ? p.dsum[(int64_t)h * p.nq + qrow] : 0.f;
     }
+    // sweep 0: per query half, sum_c P'_c dP_c and sum_c P'_c over this wave's keys
+    float dpart[2] = {0.f, 0.f}, lpart[2] = {0.f, 0.f};
     f32x16 dqacc[2][2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -1517,10 +1521,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
         kr[s] = row_op(ktile, s);
         vr[s] = row_op(vtile, s);
       }
+      if constexpr (kGrad) {
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm)
+        for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-        for (int db = 0; db < 2; ++db) kt[mm][db] = tr_op(ktile, mm, db);
+          for (int db = 0; db < 2; ++db) kt[mm][db] = tr_op(ktile, mm, db);
+      }
 #pragma unroll
       for (int qh = 0; qh < 2; ++qh) {
         // S^T = K Q^T, dP^T = V dout^T: lane = query, register v = key
@@ -1543,6 +1549,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
           }
         }
         const float nb = bias - lse[qh];
+        if constexpr (!kGrad) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[v], p.c, nb));
+            dpart[qh] = __builtin_fmaf(pv, pacc[v], dpart[qh]);
+            lpart[qh] += pv;
+          }
+          continue;
+        }
         float dsr[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -1581,6 +1596,37 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
     // the key halves meet: wave kh hands query half 1 - kh to its partner
     // through the idle rings
     __syncthreads();
+    if constexpr (!kGrad) {
+      // sums over the lane halves (they hold different keys of a query), then
+      // over the two key halves; wave kh writes query half kh
+      float dq2[2], lq2[2];
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh) {
+        const auto sd = __builtin_amdgcn_permlane32_swap(__float_as_uint(dpart[qh]),
+                                                         __float_as_uint(dpart[qh]), false, false);
+        const auto sl = __builtin_amdgcn_permlane32_swap(__float_as_uint(lpart[qh]),
+                                                         __float_as_uint(lpart[qh]), false, false);
+        dq2[qh] = __uint_as_float(sd[0]) + __uint_as_float(sd[1]);
+        lq2[qh] = __uint_as_float(sl[0]) + __uint_as_float(sl[1]);
+      }
+      float2* xo = (float2*)(kh == 0 ? ks0 : vs0);
+      if (hh == 0) xo[qi] = kh == 0 ? float2{dq2[1], lq2[1]} : float2{dq2[0], lq2[0]};
+      __syncthreads();
+      const float2 o = ((const float2*)(kh == 0 ? vs0 : ks0))[qi];
+      float dtot = (kh == 0 ? dq2[0] : dq2[1]) + o.x;
+      float ltot = (kh == 0 ? lq2[0] : lq2[1]) + o.y;
+      const int64_t qrow = (int64_t)qt * QT + 32 * kh + qi;
+      if (qrow < p.nq && hh == 0) {
+        const int64_t qi2 = (int64_t)h * p.nq + qrow;
+        if (!p.first) {
+          dtot += p.d_acc[qi2];
+          ltot += p.l_acc[qi2];
+        }
+        p.d_acc[qi2] = dtot;
+        p.l_acc[qi2] = ltot;
+      }
+      continue;
+    }
     // (kh is uniform: both branches index the register arrays statically)
     auto put = [&](const f32x16 (&a)[2], f32x4* xo) {
 #pragma unroll
@@ -1720,12 +1766,17 @@ hipError_t launch_bwd_kernels(BwdParams p, int32_t heads, bool have_d, hipStream
       p.k_hi = std::min(p.tk, (c + 1) * ct);
       p.first = c == 0;
       p.last = c == nkc - 1;
-      if (sweep == 0) {
+      if constexpr (QT == 64 && KT == 64) {
+        if (sweep == 0) {
+          p.phase_period = phase_for(items, wgs_at_once<bwd_dq_kh_kernel<false>, 128>());
+          hipLaunchKernelGGL((bwd_dq_kh_kernel<false>), qgrid, dim3(128), 0, s, p);
+        } else {
+          p.phase_period = phase_for(items, wgs_at_once<bwd_dq_kh_kernel<true>, 128>());
+          hipLaunchKernelGGL((bwd_dq_kh_kernel<true>), qgrid, dim3(128), 0, s, p);
+        }
+      } else if (sweep == 0) {
         p.phase_period = phase_for(items, wgs_at_once<bwd_dq_kernel<QT, KT, false>, QT * 2>());
         hipLaunchKernelGGL((bwd_dq_kernel<QT, KT, false>), qgrid, dim3(QT * 2), 0, s, p);
-      } else if constexpr (QT == 64 && KT == 64) {
-        p.phase_period = phase_for(items, wgs_at_once<bwd_dq_kh_kernel, 128>());
-        hipLaunchKernelGGL(bwd_dq_kh_kernel, qgrid, dim3(128), 0, s, p);
       } else {
         p.phase_period = phase_for(items, wgs_at_once<bwd_dq_kernel<QT, KT, true>, QT * 2>());
         hipLaunchKernelGGL((bwd_dq_kernel<QT, KT, true>), qgrid, dim3(QT * 2), 0, s, p);
