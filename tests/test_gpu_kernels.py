@@ -128,7 +128,8 @@ def test_sparse_stage_parity(case, out_dtype):
 
 # With query tiles of at most 64, key ranges of at least 1,024 tiles of 64
 # (2,048 of 32) run as split keys: items per (head, key chunk of 512 tiles of
-# 64 / 1,024 of 32, query tile), merged by a combine kernel.
+# 64 / 1,024 of 32, query tile). With 64-query and 64-key tiles the landmark
+# pass merges the chunks' partials; other tiles merge them in a combine kernel.
 SPLIT_CASES = [
     # (q_tile, k_tile, n_q, n_kv, top_k, n_hot, heads)
     (64, 64, 300, 65536 + 333, 1, 1, 2),     # 3 chunks, ragged tail; most chunks keep nothing
@@ -693,7 +694,7 @@ LSE_CASES = [
     (64, 64, 300, 300, 2, 2, 2, "default"),
     (128, 32, 257, 300, 4, 2, 1, "log_count"),
     (32, 64, 100, 450, 1, 1, 2, "no_landmarks"),
-    (64, 64, 300, 65536 + 333, 206, 3, 1, "default"),  # split keys: the combine writes lse
+    (64, 64, 300, 65536 + 333, 206, 3, 1, "default"),  # split keys: the landmark pass merges and writes lse
 ]
 
 
@@ -757,8 +758,8 @@ def test_forward_lse_and_backward_from_it(case):
 def test_backward_from_saved_output_strided():
     """The saved float32 output may be token-major (head stride 64, token stride H x 64)
     and the gradients float32: the saved-output backward is still bitwise the backward
-    that runs its own forward. Split keys (three chunks and the landmark pass) write the
-    normaliser and the output through the combine."""
+    that runs its own forward. Split keys (three chunks and the landmark pass): the
+    landmark pass merges the chunks' partials and writes the normaliser and the output."""
     heads, n, top_k = 2, 65536 + 333, 206
     print(f"[case] saved-output backward, token-major output: H={heads} N={n}", flush=True)
     q, k, v = _clustered(77, heads, 300, n, 64, 64, 3)
