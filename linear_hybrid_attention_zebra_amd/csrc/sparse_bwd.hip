@@ -29,8 +29,11 @@
 // query tiles for dk and dv) so that the workgroups running together share
 // one chunk's operands in L2; each launch adds into float32 accumulators,
 // in launch order.
-// Steps 2 and 4 stage their blocks global -> LDS directly, one block ahead,
-// in two-stage rings (step 4 only while the rings leave two waves per SIMD).
+// Steps 2 and 4 stage their blocks global -> LDS directly into two-stage
+// rings (step 4 only while the rings leave two waves per SIMD): one block
+// ahead behind a barrier per step, or, for dq with 64-query and 64-key tiles
+// (the key-half layout, where each wave stages only its own rows), two blocks
+// ahead with no barrier.
 // Steps 2-4 recompute S and dP with bf16 MFMA 32x32x16 and accumulate in
 // float32; dS enters its products as a bf16 pair (float32-grade), P as bf16
 // (as in the forward). Sums run in a fixed order: no atomics in any
